@@ -1,0 +1,209 @@
+"""Benchmark: WaterSIC layer quantization on one MI355X.
+
+One step = the whole hot path on one layer whose inputs already sit in HBM:
+    Sigma = X^T X / N  ->  Sigma = U^T U  ->  waterfilled SIC at the target rate (every pass of
+    the rate controller)  ->  entropy of the codes  ->  distortion tr(E Sigma E^T).
+Default workload: the attention-projection layer (W 4096 x 4096 bf16, X 8192 x 4096 bf16,
+2 bits per weight). Metric: quantized weights per second (Gparams/s).
+
+Prints one JSON line. `roofline` is taken for the kernel family with the largest share of the
+timed region, from HIP events around its launches on the library's stream; `cpu_baseline` times
+the fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAKS = {
+    "hbm": (8000.0, "GB/s"),
+    "mfma_f64": (78.6, "TFLOP/s"),
+    "mfma_f32": (157.3, "TFLOP/s"),
+    "mfma_bf16": (2500.0, "TFLOP/s"),
+}
+# kernel family -> (bound, peak key, work unit scale to the peak's unit)
+FAMILIES = {
+    "gemm_trail": ("mfma", "mfma_f64", 1e-12),
+    "gemm_y": ("mfma", "mfma_f64", 1e-12),
+    "gemm_chol": ("mfma", "mfma_f64", 1e-12),
+    "gemm_dist": ("mfma", "mfma_f64", 1e-12),
+    "syrk_bf16": ("mfma", "mfma_bf16", 1e-12),
+    "sic_leaf": ("hbm", "hbm", 1e-9),
+    "hist": ("hbm", "hbm", 1e-9),
+    "dist_resid": ("hbm", "hbm", 1e-9),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="attn_4096")
+    ap.add_argument("--target", type=float, default=2.0)
+    ap.add_argument("--mode", default="auto", choices=["auto", "secant", "bisect"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=32)
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
+    return ap.parse_args()
+
+
+def cpu_baseline(layer, target, sample_rows):
+    """The oracle as it stands, on the host: full covariance and factorization of the layer's
+    calibration data, and the waterfill search on `sample_rows` rows of W; the per-row part is
+    scaled to all rows."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = min(16, len(os.sched_getaffinity(0)))
+    ctx = threadpool_limits(cores) if threadpool_limits else None
+    try:
+        t0 = time.perf_counter()
+        sigma = oracle.covariance(layer.x_chunks)
+        t1 = time.perf_counter()
+        L, info = oracle.cholesky_lower(sigma)
+        t2 = time.perf_counter()
+        rows = np.linspace(0, layer.n_out - 1, sample_rows).astype(np.int64)
+        wf = oracle.waterfill(layer.w[rows], L, target)
+        t3 = time.perf_counter()
+    finally:
+        if ctx is not None:
+            ctx.unregister() if hasattr(ctx, "unregister") else None
+    t_cov, t_chol, t_wf = t1 - t0, t2 - t1, t3 - t2
+    t_full = t_cov + t_chol + t_wf * (layer.n_out / sample_rows)
+    return {
+        "value": layer.n_out * layer.n_in / t_full / 1e9,
+        "unit": "Gparams/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"full covariance ({t_cov:.2f} s) and Cholesky ({t_chol:.2f} s) of {layer.n_rows}x{layer.n_in}; "
+                   f"waterfill on {sample_rows} of {layer.n_out} rows ({t_wf:.2f} s, {len(wf['trace'])} passes), "
+                   f"scaled by {layer.n_out / sample_rows:.0f} to the whole layer"),
+        "seconds": round(t_cov + t_chol + t_wf, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(rows of W would shard across GPUs with U replicated; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from rate_allocated_weight_amd import _lib as L
+    from rate_allocated_weight_amd import workloads
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    layer = workloads.named_workload(args.workload)
+    if layer.dtype == "bf16":
+        W = L.bf16_from_bits(layer.w_bits, dev)
+        X = [L.bf16_from_bits(b, dev) for b in layer.x_bits_chunks]
+    else:
+        W = torch.from_numpy(layer.w).to(dev)
+        X = [torch.from_numpy(c).to(dev) for c in layer.x_chunks]
+    n_out, n_in = layer.n_out, layer.n_in
+    n_rows = layer.n_rows
+
+    # buffers allocated once
+    sigma = torch.empty((n_in, n_in), dtype=torch.float64, device=dev)
+    codes = torch.empty((n_out, n_in), dtype=torch.int32, device=dev)
+    resid = torch.empty((n_out, n_in), dtype=torch.float32, device=dev)
+    ws_cov = L.workspace(L.OP_COVARIANCE, 1, n_in, dev)
+    ws_chol = L.workspace(L.OP_CHOLESKY, 1, n_in, dev)
+    ws_wf = L.workspace(L.OP_WATERFILL, n_out, n_in, dev)
+    ws_ent = L.workspace(L.OP_ENTROPY, n_out, n_in, dev)
+    ws_dist = L.workspace(L.OP_DISTORTION, n_out, n_in, dev)
+
+    def step():
+        for i, c in enumerate(X):
+            L.covariance(c, sigma, alpha=1.0 / n_rows, beta=0.0 if i == 0 else 1.0, ws=ws_cov)
+        U, _ = L.cholesky(sigma, ws=ws_chol)
+        wf = L.waterfill(W, U, args.target, mode=args.mode, codes=codes, resid=resid, ws=ws_wf)
+        h, _ = L.entropy(codes, ws=ws_ent)
+        D, _ = L.distortion(W, codes, U, wf["c"], resid=resid, ws=ws_dist)
+        return wf, h, D
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not args.no_profile:
+        L.profile_reset()
+        L.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    results = [step() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if not args.no_profile:
+        L.profile_enable(False)
+    elapsed = t1 - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    wf, h, D = results[-1]
+
+    kernels = {}
+    roofline = None
+    if not args.no_profile:
+        for name in L.profile_names():
+            p = L.profile_read(name)
+            kernels[name] = {"launches": p["launches"], "ms": round(p["ms"], 4),
+                             "avg_us": round(1e3 * p["ms"] / max(1, p["launches"]), 3), "work": p["work"]}
+        cand = [(k, v) for k, v in kernels.items() if k in FAMILIES]
+        if cand:
+            dom, v = max(cand, key=lambda kv: kv[1]["ms"])
+            bound, peak_key, scale = FAMILIES[dom]
+            peak, unit = PEAKS[peak_key]
+            achieved = v["work"] * scale / (v["ms"] * 1e-3)
+            roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                        "frac": round(achieved / peak, 4), "traffic": None,
+                        "avg_launch_us": v["avg_us"], "launches": v["launches"],
+                        "share_of_step": round(v["ms"] / (elapsed * 1e3), 4)}
+
+    out = {
+        "metric": "Gparams/s waterfill+SIC quantize (4096x4096, 2 bit/param); % MFMA/HBM roofline",
+        "value": round(n_out * n_in * args.steps / elapsed / 1e9, 6),
+        "unit": "Gparams/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n_out": n_out, "n_in": n_in, "calib_rows": n_rows,
+                   "w_dtype": layer.dtype, "target_bits": args.target, "controller": args.mode,
+                   "step": "covariance+cholesky+waterfill+entropy+distortion"},
+        "result": {"c": wf["c"], "rate": wf["rate"], "entropy": h, "passes": wf["passes"], "D": D},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(layer, args.target, args.cpu_sample_rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

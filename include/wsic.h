@@ -1,0 +1,196 @@
+/*
+ * wsic.h -- C ABI of libwsic: WaterSIC quantization of one linear layer on an MI355X (gfx950).
+ *
+ * Method (web page "WaterSIC: information-theoretically (near) optimal linear layer
+ * quantization", gist.science; sections cited as [WaterSIC <section>]):
+ *   Sigma = X^T X / N                         calibration covariance  [Sommario tecnico §2 item 1]
+ *   Sigma = U^T U, U upper, U_jj > 0           Cholesky (the page's L L^T with U = L^T) [§2 item 1]
+ *   Delta_j = c / U_jj                         waterfilling steps, alpha_i ~ 1/|l_ii| [§2 item 2]
+ *   SIC, columns j = n_in-1 ... 0:             interference cancellation in reverse order [§2 item 1]
+ *       t_j = w_j + sum_{k>j} (U_jk/U_jj) (w_k - Delta_k q_k),  q_j = rint(t_j / Delta_j)
+ *   rate = empirical entropy of the pooled codes (unbounded integers, entropy coded) [§2 item 3]
+ *   distortion = tr((W - W_hat) Sigma (W - W_hat)^T)  (output error of Y = W X) [§1]
+ *
+ * Conventions for every call:
+ *   - Return value: WSIC_OK (0) or a negative WSIC_E_* status. Nothing is thrown across the ABI.
+ *     wsic_last_error() gives a message for the last failing call on the calling thread.
+ *   - Array arguments are DEVICE pointers owned by the caller, row-major, with explicit
+ *     leading dimensions in elements (ld >= number of columns). Host pointers are marked
+ *     "host". Inputs are const and never written.
+ *   - Scratch memory is the caller's: query wsic_workspace_bytes(op, n_out, n_in) and pass
+ *     ws / ws_bytes. A smaller ws_bytes returns WSIC_E_WORKSPACE. The library allocates no
+ *     device memory of its own.
+ *   - stream is a hipStream_t (NULL = legacy default stream). All device work is enqueued on
+ *     it. Calls that return host scalars synchronize that stream before returning.
+ *   - dtype selects the element type of W / X: WSIC_F32 (float) or WSIC_BF16 (bfloat16 bits).
+ *   - Sigma and U are fp64 n_in x n_in.
+ *   - Calls are re-entrant only on distinct workspaces.
+ */
+#ifndef WSIC_H
+#define WSIC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WSIC_VERSION 100
+
+enum wsic_status {
+  WSIC_OK = 0,
+  WSIC_E_INVAL = -1,       /* bad argument: null pointer, size <= 0, ld too small, bad enum */
+  WSIC_E_NOT_PD = -2,      /* covariance not positive definite (see info) */
+  WSIC_E_NONFINITE = -3,   /* NaN / Inf in an input */
+  WSIC_E_NO_BRACKET = -4,  /* target rate not reachable by any grid scale */
+  WSIC_E_RANGE = -5,       /* a code does not fit int32, or too many distinct large codes */
+  WSIC_E_WORKSPACE = -6,   /* ws_bytes smaller than wsic_workspace_bytes() */
+  WSIC_E_HIP = -7          /* a HIP runtime call failed */
+};
+
+enum wsic_dtype { WSIC_F32 = 0, WSIC_BF16 = 1 };
+
+enum wsic_op {
+  WSIC_OP_COVARIANCE = 0,
+  WSIC_OP_CHOLESKY = 1,
+  WSIC_OP_SIC = 2,
+  WSIC_OP_WATERFILL = 3,
+  WSIC_OP_ENTROPY = 4,
+  WSIC_OP_DISTORTION = 5
+};
+
+enum wsic_dmode { WSIC_D_RESID = 0, WSIC_D_DIRECT = 1 };
+enum wsic_wfmode { WSIC_WF_AUTO = 0, WSIC_WF_SECANT = 1, WSIC_WF_BISECT = 2 };
+
+/* WSIC_WF_AUTO picks BISECT for layers of fewer than WSIC_WF_AUTO_PARAMS weights, SECANT
+ * otherwise. */
+#define WSIC_WF_AUTO_PARAMS (1LL << 20)
+
+/* Library version (WSIC_VERSION). */
+int wsic_version(void);
+
+/* Message for the last failing call on this thread ("" if none). Owned by the library. */
+const char* wsic_last_error(void);
+
+/* Static name of a status code. */
+const char* wsic_status_str(int status);
+
+/* Bytes of device workspace that call `op` needs for an n_out x n_in layer (n_out is ignored
+ * by WSIC_OP_COVARIANCE / WSIC_OP_CHOLESKY; for WSIC_OP_ENTROPY pass the code matrix shape).
+ * Returns 0 for an unknown op. */
+size_t wsic_workspace_bytes(int op, int64_t n_out, int64_t n_in);
+
+/*
+ * Calibration covariance [WaterSIC §2 item 1], SYRK semantics:
+ *     Sigma <- beta * Sigma + alpha * X^T X
+ * X: rows x n_in, ldx >= n_in, dtype f32 or bf16. Sigma: n_in x n_in fp64, lds >= n_in.
+ * To accumulate Sigma = X^T X / N over streamed chunks, pass alpha = 1/N for every chunk,
+ * beta = 0 for the first chunk and beta = 1 afterwards. Only the upper triangle of the old
+ * Sigma is read; the full symmetric result is written. bf16 chunks run on bf16 MFMA with
+ * fp32 partial sums over at most 64 rows folded into fp64; f32 chunks run in fp64.
+ * Errors: WSIC_E_INVAL; WSIC_E_NONFINITE if X holds NaN/Inf (Sigma is then unspecified).
+ */
+int wsic_covariance(const void* X, int dtype, int64_t rows, int64_t n_in, int64_t ldx,
+                    double alpha, double beta, double* Sigma, int64_t lds,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Cholesky factorization in place [WaterSIC §2 item 1]: on return the upper triangle of A
+ * holds U with Sigma = U^T U and U_jj > 0, and the strict lower triangle is zero.
+ * A: n x n fp64, lda >= n. Only the upper triangle of the input is read.
+ * *info (host): 0 on success, else the 1-based index of the first pivot that is not positive
+ * (or not finite); the call then returns WSIC_E_NOT_PD and A is unspecified.
+ */
+int wsic_cholesky(double* A, int64_t n, int64_t lda, int64_t* info,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One SIC pass at grid scale c [WaterSIC §2 items 1-2]: steps Delta_j = c / U_jj, columns
+ * visited j = n_in-1 ... 0, each rounded (ties to even) after cancelling the interference of
+ * the columns already quantized. Computed in fp64.
+ * W: n_out x n_in (dtype), ldw >= n_in. U: upper factor from wsic_cholesky, ldu >= n_in.
+ * codes (out): n_out x n_in int32, ldq >= n_in.
+ * resid (out, nullable): n_out x n_in float, ldr >= n_in, r_j = t_j - Delta_j q_j in the
+ * units of W (|r_j| <= Delta_j / 2); sum_j U_jj^2 ||r_:,j||^2 is the layer distortion.
+ * Errors: WSIC_E_INVAL (c <= 0 or not finite), WSIC_E_NONFINITE (W), WSIC_E_RANGE (a code
+ * outside int32).
+ */
+int wsic_sic_quantize(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                      const double* U, int64_t ldu, double c,
+                      int32_t* codes, int64_t ldq, float* resid, int64_t ldr,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Options of the rate controller; pass NULL for the defaults shown. */
+typedef struct wsic_wf_opts {
+  double rate_tol;     /* accept c once R - rate_tol < H(c) <= R (default 2e-5 bits)        */
+  double bracket_log2; /* or once log2(c_hi / c_lo) <= bracket_log2 (default 2^-20)          */
+  int32_t max_passes;  /* SIC passes allowed (default 64)                                   */
+  int32_t mode;        /* WSIC_WF_BISECT: start at c_init, double (halve) c until the rate
+                          is bracketed, then geometric bisection, stopping only on
+                          bracket_log2 -- the reference search, whose sequence of grid
+                          scales is fully determined by the code entropies it sees;
+                          WSIC_WF_SECANT: safeguarded regula falsi (Illinois) on log2 c,
+                          far fewer passes once H(c) is smooth (large layers);
+                          WSIC_WF_AUTO (default): BISECT below WSIC_WF_AUTO_PARAMS weights,
+                          where H(c) moves in visible non-monotone steps, else SECANT     */
+  double c_init;       /* > 0: first grid scale tried; 0: high-rate estimate
+                          sqrt(2 pi e mean_j(var(W_:,j) U_jj^2)) 2^-R                        */
+} wsic_wf_opts;
+
+/*
+ * Waterfilling rate allocation [WaterSIC §2 items 2-3]: finds the grid scale c (the smallest,
+ * to the controller's tolerance) whose SIC codes have pooled empirical entropy
+ * H(c) <= target_bits, and returns those codes.
+ * Outputs (host): *c_out, *rate_out = H(c) in bits per weight, *passes_out = SIC passes run.
+ * codes (out, required) / resid (out, nullable): as in wsic_sic_quantize, at c_out.
+ * Errors: as wsic_sic_quantize, WSIC_E_INVAL for target_bits <= 0, WSIC_E_NO_BRACKET when
+ * the target cannot be met within max_passes / 64 doublings.
+ */
+int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                   const double* U, int64_t ldu, double target_bits, const wsic_wf_opts* opts,
+                   double* c_out, double* rate_out, int32_t* passes_out,
+                   int32_t* codes, int64_t ldq, float* resid, int64_t ldr,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Zeroth-order empirical entropy of the pooled codes [WaterSIC §2 item 3]:
+ *   H = log2(N) - (1/N) sum_k n_k log2 n_k   bits per code, N = n_out * n_in.
+ * codes: n_out x n_in int32, ldq >= n_in. *bits_per_param (host). *n_symbols (host,
+ * nullable): number of distinct codes. Codes beyond +-2047 are counted through an overflow
+ * list of bounded size (WSIC_E_RANGE if more than 2^20 such codes).
+ */
+int wsic_entropy(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
+                 double* bits_per_param, int64_t* n_symbols,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Layer distortion [WaterSIC §1]: D = tr((W - W_hat) Sigma (W - W_hat)^T), W_hat_ij = Delta_j q_ij.
+ *   mode WSIC_D_RESID : D = sum_j U_jj^2 sum_i r_ij^2 from the SIC residuals (resid required);
+ *                       a streaming pass.
+ *   mode WSIC_D_DIRECT: D = ||(W - W_hat) U^T||_F^2 by an fp64 MFMA product (resid ignored).
+ * W_hat (out, nullable): n_out x n_in of dtype w_hat_dtype, ldh >= n_in.
+ * *D_out (host).
+ */
+int wsic_distortion(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                    const int32_t* codes, int64_t ldq, const double* U, int64_t ldu, double c,
+                    const float* resid, int64_t ldr, int mode, double* D_out,
+                    void* W_hat, int w_hat_dtype, int64_t ldh,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel timing. While enabled, every kernel launch is bracketed by HIP events on its own
+ * stream; wsic_profile_read synchronizes and returns, for the kernel family `name`, the
+ * launch count, the summed event time in ms and the summed algorithmic work (flops for the
+ * MFMA kernels, bytes for the streaming kernels). wsic_profile_names writes a
+ * comma-separated list of the families seen into buf. Not thread-safe.
+ */
+int wsic_profile_enable(int on);
+int wsic_profile_reset(void);
+int wsic_profile_read(const char* name, int64_t* launches, double* total_ms, double* total_work);
+int wsic_profile_names(char* buf, size_t buf_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WSIC_H */

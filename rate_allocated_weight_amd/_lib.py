@@ -1,0 +1,310 @@
+"""ctypes binding of libwsic (the C ABI in include/wsic.h).
+
+Argument marshalling only: every step runs in the HIP library. Tensors must live on a ROCm
+device; workspaces are allocated here with torch and handed to the library. There is no CPU
+fallback: importing succeeds without a GPU, but any call raises if libwsic.so is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwsic.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "wsic.h")
+
+OK, E_INVAL, E_NOT_PD, E_NONFINITE, E_NO_BRACKET, E_RANGE, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7
+F32, BF16 = 0, 1
+OP_COVARIANCE, OP_CHOLESKY, OP_SIC, OP_WATERFILL, OP_ENTROPY, OP_DISTORTION = range(6)
+D_RESID, D_DIRECT = 0, 1
+WF_AUTO, WF_SECANT, WF_BISECT = 0, 1, 2
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+_d = ctypes.c_double
+_sz = ctypes.c_size_t
+
+
+class WsicError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [{status_name(status)}]")
+        self.status = status
+        self.message = message
+
+
+class WfOpts(ctypes.Structure):
+    _fields_ = [("rate_tol", ctypes.c_double), ("bracket_log2", ctypes.c_double),
+                ("max_passes", ctypes.c_int32), ("mode", ctypes.c_int32), ("c_init", ctypes.c_double)]
+
+
+_SIGS = {
+    "wsic_version": (ctypes.c_int, []),
+    "wsic_last_error": (ctypes.c_char_p, []),
+    "wsic_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "wsic_workspace_bytes": (_sz, [ctypes.c_int, _i64, _i64]),
+    "wsic_covariance": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _d, _d, _p, _i64, _p, _sz, _p]),
+    "wsic_cholesky": (ctypes.c_int, [_p, _i64, _i64, ctypes.POINTER(_i64), _p, _sz, _p]),
+    "wsic_sic_quantize": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _d, _p, _i64, _p,
+                                         _i64, _p, _sz, _p]),
+    "wsic_waterfill": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _d, ctypes.POINTER(WfOpts),
+                                      ctypes.POINTER(_d), ctypes.POINTER(_d), ctypes.POINTER(ctypes.c_int32),
+                                      _p, _i64, _p, _i64, _p, _sz, _p]),
+    "wsic_entropy": (ctypes.c_int, [_p, _i64, _i64, _i64, ctypes.POINTER(_d), ctypes.POINTER(_i64), _p, _sz, _p]),
+    "wsic_distortion": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, _i64, _d, _p, _i64,
+                                       ctypes.c_int, ctypes.POINTER(_d), _p, ctypes.c_int, _i64, _p, _sz, _p]),
+    "wsic_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+    "wsic_profile_reset": (ctypes.c_int, []),
+    "wsic_profile_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(_i64), ctypes.POINTER(_d),
+                                         ctypes.POINTER(_d)]),
+    "wsic_profile_names": (ctypes.c_int, [ctypes.c_char_p, _sz]),
+}
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libwsic.so (built in-tree by rate_allocated_weight_amd.build)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m rate_allocated_weight_amd.build` (there is no CPU fallback)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = h
+    return _LIB
+
+
+def header_functions() -> List[str]:
+    """Names of the functions declared in include/wsic.h."""
+    txt = open(HEADER_PATH).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(wsic_[a-z_0-9]+)\s*\(", txt)))
+
+
+def status_name(s: int) -> str:
+    try:
+        return lib().wsic_status_str(s).decode()
+    except ImportError:
+        return str(s)
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        msg = lib().wsic_last_error().decode()
+        raise WsicError(status, msg)
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _need_cuda(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libwsic works on device tensors only")
+
+
+def _rowmajor(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def workspace_bytes(op: int, n_out: int, n_in: int) -> int:
+    return int(lib().wsic_workspace_bytes(op, n_out, n_in))
+
+
+def workspace(op: int, n_out: int, n_in: int, device) -> torch.Tensor:
+    nb = workspace_bytes(op, n_out, n_in)
+    if nb == 0:
+        raise ValueError("bad workspace query")
+    return torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def _ws_args(ws: torch.Tensor):
+    return ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel())
+
+
+# ------------------------------------------------------------------------------ entry points
+def covariance(X: torch.Tensor, sigma: Optional[torch.Tensor] = None, alpha: float = 1.0,
+               beta: float = 0.0, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sigma <- beta*Sigma + alpha*X^T X (fp64, full symmetric)."""
+    _need_cuda(X)
+    ldx = _rowmajor(X)
+    rows, n = X.shape
+    if sigma is None:
+        sigma = torch.empty((n, n), dtype=torch.float64, device=X.device)
+    ws = ws if ws is not None else workspace(OP_COVARIANCE, 1, n, X.device)
+    _check(lib().wsic_covariance(_p(X.data_ptr()), _dtype_code(X), rows, n, ldx, alpha, beta,
+                                 _p(sigma.data_ptr()), _rowmajor(sigma), *_ws_args(ws), _stream(X)))
+    return sigma
+
+
+def covariance_chunks(chunks: Sequence[torch.Tensor]) -> torch.Tensor:
+    """Sigma = X^T X / N over streamed row chunks."""
+    n_total = sum(int(c.shape[0]) for c in chunks)
+    sigma = None
+    ws = None
+    for i, c in enumerate(chunks):
+        if ws is None:
+            ws = workspace(OP_COVARIANCE, 1, c.shape[1], c.device)
+        sigma = covariance(c, sigma, alpha=1.0 / n_total, beta=0.0 if i == 0 else 1.0, ws=ws)
+    return sigma
+
+
+def cholesky(A: torch.Tensor, ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, int]:
+    """In place: upper(A) <- U with Sigma = U^T U, lower zeroed. Returns (A, info); raises on
+    failure with the pivot in the message."""
+    _need_cuda(A)
+    if A.dtype != torch.float64:
+        raise TypeError("cholesky expects float64")
+    n = A.shape[0]
+    ws = ws if ws is not None else workspace(OP_CHOLESKY, 1, n, A.device)
+    info = _i64(0)
+    st = lib().wsic_cholesky(_p(A.data_ptr()), n, _rowmajor(A), ctypes.byref(info), *_ws_args(ws), _stream(A))
+    if st == E_NOT_PD:
+        err = WsicError(st, lib().wsic_last_error().decode())
+        err.info = int(info.value)
+        raise err
+    _check(st)
+    return A, int(info.value)
+
+
+def sic_quantize(W: torch.Tensor, U: torch.Tensor, c: float, want_resid: bool = False,
+                 codes: Optional[torch.Tensor] = None, resid: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None):
+    """One SIC pass at grid scale c. Returns (codes int32, resid float32 or None)."""
+    _need_cuda(W, U)
+    n_out, n_in = W.shape
+    if codes is None:
+        codes = torch.empty((n_out, n_in), dtype=torch.int32, device=W.device)
+    if want_resid and resid is None:
+        resid = torch.empty((n_out, n_in), dtype=torch.float32, device=W.device)
+    ws = ws if ws is not None else workspace(OP_SIC, n_out, n_in, W.device)
+    _check(lib().wsic_sic_quantize(
+        _p(W.data_ptr()), _dtype_code(W), n_out, n_in, _rowmajor(W), _p(U.data_ptr()), _rowmajor(U), float(c),
+        _p(codes.data_ptr()), _rowmajor(codes), _p(resid.data_ptr() if resid is not None else 0),
+        _rowmajor(resid) if resid is not None else n_in, *_ws_args(ws), _stream(W)))
+    return codes, resid
+
+
+_MODES = {"auto": WF_AUTO, "secant": WF_SECANT, "bisect": WF_BISECT}
+
+
+def waterfill(W: torch.Tensor, U: torch.Tensor, target_bits: float, *, mode: str = "auto",
+              rate_tol: float = 2e-5, bracket_log2: float = 2.0 ** -20, max_passes: int = 64,
+              c_init: float = 0.0, want_resid: bool = True, codes: Optional[torch.Tensor] = None,
+              resid: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> Dict[str, object]:
+    """Grid scale c with pooled code entropy H(c) <= target_bits, and its codes."""
+    _need_cuda(W, U)
+    n_out, n_in = W.shape
+    if codes is None:
+        codes = torch.empty((n_out, n_in), dtype=torch.int32, device=W.device)
+    if want_resid and resid is None:
+        resid = torch.empty((n_out, n_in), dtype=torch.float32, device=W.device)
+    ws = ws if ws is not None else workspace(OP_WATERFILL, n_out, n_in, W.device)
+    opts = WfOpts(rate_tol, bracket_log2, max_passes, _MODES[mode], c_init)
+    c_out, rate_out, passes = _d(0), _d(0), ctypes.c_int32(0)
+    _check(lib().wsic_waterfill(
+        _p(W.data_ptr()), _dtype_code(W), n_out, n_in, _rowmajor(W), _p(U.data_ptr()), _rowmajor(U),
+        float(target_bits), ctypes.byref(opts), ctypes.byref(c_out), ctypes.byref(rate_out), ctypes.byref(passes),
+        _p(codes.data_ptr()), _rowmajor(codes), _p(resid.data_ptr() if resid is not None else 0),
+        _rowmajor(resid) if resid is not None else n_in, *_ws_args(ws), _stream(W)))
+    return {"c": c_out.value, "rate": rate_out.value, "passes": int(passes.value), "codes": codes,
+            "resid": resid}
+
+
+def entropy(codes: torch.Tensor, ws: Optional[torch.Tensor] = None) -> Tuple[float, int]:
+    """Pooled empirical entropy (bits per code) and number of distinct codes."""
+    _need_cuda(codes)
+    if codes.dtype != torch.int32:
+        raise TypeError("codes must be int32")
+    n_out, n_in = codes.shape
+    ws = ws if ws is not None else workspace(OP_ENTROPY, n_out, n_in, codes.device)
+    h, ns = _d(0), _i64(0)
+    _check(lib().wsic_entropy(_p(codes.data_ptr()), n_out, n_in, _rowmajor(codes), ctypes.byref(h),
+                              ctypes.byref(ns), *_ws_args(ws), _stream(codes)))
+    return h.value, int(ns.value)
+
+
+def distortion(W: torch.Tensor, codes: torch.Tensor, U: torch.Tensor, c: float,
+               resid: Optional[torch.Tensor] = None, mode: str = "resid",
+               w_hat_dtype: Optional[torch.dtype] = None, ws: Optional[torch.Tensor] = None):
+    """Layer distortion tr((W - W_hat) Sigma (W - W_hat)^T); optionally W_hat."""
+    _need_cuda(W, codes, U)
+    n_out, n_in = W.shape
+    w_hat = None
+    wdt = F32
+    if w_hat_dtype is not None:
+        w_hat = torch.empty((n_out, n_in), dtype=w_hat_dtype, device=W.device)
+        wdt = _dtype_code(w_hat)
+    ws = ws if ws is not None else workspace(OP_DISTORTION, n_out, n_in, W.device)
+    d = _d(0)
+    _check(lib().wsic_distortion(
+        _p(W.data_ptr()), _dtype_code(W), n_out, n_in, _rowmajor(W), _p(codes.data_ptr()), _rowmajor(codes),
+        _p(U.data_ptr()), _rowmajor(U), float(c), _p(resid.data_ptr() if resid is not None else 0),
+        _rowmajor(resid) if resid is not None else n_in, D_DIRECT if mode == "direct" else D_RESID,
+        ctypes.byref(d), _p(w_hat.data_ptr() if w_hat is not None else 0), wdt,
+        _rowmajor(w_hat) if w_hat is not None else n_in, *_ws_args(ws), _stream(W)))
+    return d.value, w_hat
+
+
+# ------------------------------------------------------------------------------ kernel timing
+def profile_enable(on: bool = True) -> None:
+    _check(lib().wsic_profile_enable(1 if on else 0))
+
+
+def profile_reset() -> None:
+    _check(lib().wsic_profile_reset())
+
+
+def profile_read(name: str) -> Dict[str, float]:
+    n, ms, work = _i64(0), _d(0), _d(0)
+    _check(lib().wsic_profile_read(name.encode(), ctypes.byref(n), ctypes.byref(ms), ctypes.byref(work)))
+    return {"launches": int(n.value), "ms": ms.value, "work": work.value}
+
+
+def profile_names() -> List[str]:
+    buf = ctypes.create_string_buffer(4096)
+    _check(lib().wsic_profile_names(buf, 4096))
+    s = buf.value.decode()
+    return [x for x in s.split(",") if x]
+
+
+# ------------------------------------------------------------------------------ whole layer
+def quantize_layer(W: torch.Tensor, x_chunks: Sequence[torch.Tensor], target_bits: float,
+                   **wf_kw) -> Dict[str, object]:
+    """Covariance -> Cholesky -> waterfill -> entropy -> distortion, all on the device."""
+    sigma = covariance_chunks(x_chunks)
+    U, _ = cholesky(sigma)
+    wf = waterfill(W, U, target_bits, **wf_kw)
+    h, nsym = entropy(wf["codes"])
+    D, _ = distortion(W, wf["codes"], U, wf["c"], resid=wf["resid"])
+    out = dict(wf)
+    out.update({"U": U, "entropy": h, "n_symbols": nsym, "D": D})
+    return out
+
+
+def bf16_from_bits(bits, device) -> torch.Tensor:
+    """uint16 numpy bf16 bit patterns -> device bfloat16 tensor (bit-exact)."""
+    import numpy as np
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+

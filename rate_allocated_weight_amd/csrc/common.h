@@ -1,0 +1,155 @@
+// Internal declarations shared by the libwsic translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "wsic.h"
+
+namespace wsic {
+
+// ---------------------------------------------------------------- host-side error state
+void set_error(const char* fmt, ...);
+void clear_error();
+const char* last_error();
+
+#define WSIC_HIP_TRY(expr)                                                      \
+  do {                                                                          \
+    hipError_t _e = (expr);                                                     \
+    if (_e != hipSuccess) {                                                     \
+      ::wsic::set_error("%s failed: %s (%s:%d)", #expr, hipGetErrorString(_e),  \
+                        __FILE__, __LINE__);                                    \
+      return WSIC_E_HIP;                                                        \
+    }                                                                           \
+  } while (0)
+
+// ---------------------------------------------------------------- launch timing
+// A launch bracketed by HIP events on its own stream when profiling is on.
+struct ProfToken {
+  int slot;
+};
+ProfToken prof_begin(const char* family, hipStream_t st);
+void prof_end(ProfToken t, hipStream_t st, double work);
+
+#define WSIC_LAUNCH(family, work, stream, kernel, grid, block, shmem, ...)      \
+  do {                                                                          \
+    ::wsic::ProfToken _tok = ::wsic::prof_begin(family, stream);                \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);        \
+    ::wsic::prof_end(_tok, stream, (double)(work));                             \
+    hipError_t _le = hipGetLastError();                                         \
+    if (_le != hipSuccess) {                                                    \
+      ::wsic::set_error("launch of %s failed: %s", #kernel,                     \
+                        hipGetErrorString(_le));                                \
+      return WSIC_E_HIP;                                                        \
+    }                                                                           \
+  } while (0)
+
+// ---------------------------------------------------------------- device flags
+// Small int array at the head of every workspace; kernels raise bits with atomicOr.
+enum FlagBits : int {
+  FLAG_NONFINITE = 1,
+  FLAG_RANGE = 2,
+  FLAG_BAD_DIAG = 4,
+  FLAG_OVERFLOW_LIST = 8,
+};
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- element access
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// ---------------------------------------------------------------- kernel launchers
+// Each returns a wsic status; all work is enqueued on `st`.
+
+// fp64 MFMA GEMM family: C[M x N] = beta*C + alpha * sum_k A'(m,k) B(n,k)
+enum AMode : int {
+  A_F64 = 0,      // A double, A'(m,k) = A[m*lda + k]
+  A_F32 = 1,      // A float
+  A_BF16 = 2,     // A bf16 bits
+  A_CODES = 3,    // A int32 codes, A'(m,k) = vec[k] * A[m*lda + k]
+  A_ERR_F32 = 4,  // A'(m,k) = W[m*lda+k] - vec[k] * Q[m*ldq+k], W float
+  A_ERR_BF16 = 5, // same with W bf16
+  A_F64_T = 6,    // A double stored k-major: A'(m,k) = A[k*lda + m]; B likewise B[k*ldb + n]
+};
+enum Epilogue : int { EPI_STORE = 0, EPI_SUMSQ = 1 };
+
+struct GemmArgs {
+  int64_t M, N, K;
+  const void* A;
+  int64_t lda;
+  const int32_t* Q;
+  int64_t ldq;
+  const double* vec;
+  const double* B;
+  int64_t ldb;
+  double* C;
+  int64_t ldc;
+  double alpha, beta;
+  int tri;         // B(n,k) == 0 for k < n: each N-tile starts its K loop at its first column
+  int upper_only;  // only tiles holding some n >= m are computed
+  double* partial; // EPI_SUMSQ: one fp64 per tile
+};
+int gemm_tiles(const GemmArgs& g);  // number of tiles (size of `partial`)
+// `work` = algorithmic flops of the call, recorded by the launch timer
+int launch_gemm(int amode, int epi, const GemmArgs& g, const char* family, double work,
+                hipStream_t st);
+
+// covariance
+int launch_syrk(const void* X, int dtype, int64_t rows, int64_t n, int64_t ldx, double alpha,
+                double beta, double* S, int64_t lds, hipStream_t st);
+int launch_mirror_upper(double* S, int64_t n, int64_t lds, hipStream_t st);
+int launch_diag_check(const double* S, int64_t n, int64_t lds, int* flags, hipStream_t st);
+
+// cholesky
+int launch_potrf_diag(double* A, int64_t lda, int64_t kb, int nbk, int64_t* info, hipStream_t st);
+int launch_trsm_row(double* A, int64_t lda, int64_t kb, int nbk, int64_t n, const int64_t* info,
+                    hipStream_t st);
+int launch_zero_lower(double* A, int64_t n, int64_t lda, hipStream_t st);
+
+// SIC
+int launch_prep(const double* U, int64_t ldu, int64_t n, double* invd, int* flags, hipStream_t st);
+// delta_j = c / U_jj (nullable), diag_j = U_jj (nullable)
+int launch_delta(const double* U, int64_t ldu, int64_t n, double c, double* delta, double* diag,
+                 hipStream_t st);
+int launch_check_finite(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                        int* flags, hipStream_t st);
+// packed diagonal blocks of B = U diag(1/U_jj) (c-independent), consumed by the leaf
+int sic_pack_doubles(int64_t n_in);
+int launch_pack_blocks(const double* U, int64_t ldu, int64_t n, const double* invd, double* Bpk,
+                       hipStream_t st);
+int launch_sic_leaf(int64_t n_out, int64_t j0, int w, const double* Y, int64_t ldy,
+                    const double* G, int64_t ldg, const double* Bpk, const double* invd, double c,
+                    int32_t* codes, int64_t ldq, float* resid, int64_t ldr, int* flags,
+                    hipStream_t st);
+int colstats_doubles(int64_t n_out, int64_t n_in);
+int launch_colstats(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                    double* part, double* colvar, hipStream_t st);
+
+// histogram / entropy
+constexpr int HIST_HALF = 2047;
+constexpr int HIST_BINS = 2 * HIST_HALF + 1;
+constexpr unsigned OVF_CAP = 1u << 20;
+struct EntropyResult {
+  double sum_nlogn;            // sum over window bins of n log2 n
+  unsigned long long nsym;     // non-empty window bins
+  unsigned int ovf_count;      // codes outside the window
+  int flags;
+};
+int launch_hist(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
+                unsigned long long* bins, int32_t* ovf, unsigned int* ovf_count, hipStream_t st);
+int launch_entropy_reduce(const unsigned long long* bins, const unsigned int* ovf_count,
+                          const int* flags, EntropyResult* res, hipStream_t st);
+int launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+// distortion
+int launch_dist_resid(const float* resid, int64_t n_out, int64_t n_in, int64_t ldr,
+                      const double* U, int64_t ldu, double* partial, int nblk, hipStream_t st);
+int launch_dequant(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
+                   const double* invd, double c, void* W_hat, int w_hat_dtype, int64_t ldh,
+                   hipStream_t st);
+int launch_sum_partials(const double* partial, int64_t n, double* out, hipStream_t st);
+
+}  // namespace wsic

@@ -1,0 +1,117 @@
+// Distortion and dequantization passes.
+//
+// The layer distortion tr((W - W_hat) Sigma (W - W_hat)^T) (the output error of Y = W X,
+// WaterSIC page, Sommario tecnico §1) splits per column over the SIC residuals:
+//     D = sum_j U_jj^2 sum_i r_ij^2 .
+// k_dist_resid streams the fp32 residuals once: a workgroup owns a 256-column strip and a
+// slab of rows; each thread keeps one column's sum of squares (fp64), scales it by U_jj^2 and
+// the workgroup writes one partial. Partials are summed in a fixed order by
+// k_sum_partials, so the result is deterministic.
+#include "common.h"
+
+namespace wsic {
+namespace {
+
+constexpr int ROWS_PER_BLOCK = 256;
+
+__global__ __launch_bounds__(256) void k_dist_resid(const float* __restrict__ resid,
+                                                    int64_t n_out, int64_t n_in, int64_t ldr,
+                                                    const double* __restrict__ U, int64_t ldu,
+                                                    double* __restrict__ partial) {
+  __shared__ double red[256];
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * ROWS_PER_BLOCK;
+  double s = 0.0;
+  if (j < n_in) {
+    int64_t r1 = r0 + ROWS_PER_BLOCK;
+    if (r1 > n_out) r1 = n_out;
+#pragma unroll 16
+    for (int64_t r = r0; r < r1; ++r) {
+      const double v = (double)resid[r * ldr + j];
+      s = fma(v, v, s);
+    }
+    const double d = U[j * ldu + j];
+    s *= d * d;
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void k_sum_partials(const double* partial, int64_t n,
+                                                      double* out) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) s += partial[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = red[0];
+}
+
+// W_hat_ij = Delta_j q_ij with Delta_j = c / U_jj, written as float or bf16 (round to nearest
+// even).
+template <bool BF16>
+__global__ void k_dequant(const int32_t* __restrict__ codes, int64_t n_out, int64_t n_in,
+                          int64_t ldq, const double* __restrict__ invd, double c, void* W_hat,
+                          int64_t ldh) {
+  const int64_t total = n_out * n_in;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / n_in, j = e % n_in;
+    const float v = (float)((c * invd[j]) * (double)codes[r * ldq + j]);
+    if (BF16) {
+      uint32_t u = __float_as_uint(v);
+      u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+      ((uint16_t*)W_hat)[r * ldh + j] = (uint16_t)u;
+    } else {
+      ((float*)W_hat)[r * ldh + j] = v;
+    }
+  }
+}
+
+}  // namespace
+
+int launch_dist_resid(const float* resid, int64_t n_out, int64_t n_in, int64_t ldr,
+                      const double* U, int64_t ldu, double* partial, int nblk, hipStream_t st) {
+  const unsigned gx = (unsigned)((n_in + 255) / 256);
+  const unsigned gy = (unsigned)((n_out + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK);
+  if ((int64_t)gx * gy > nblk) {
+    set_error("internal: distortion partials %u x %u > %d", gx, gy, nblk);
+    return WSIC_E_WORKSPACE;
+  }
+  WSIC_LAUNCH("dist_resid", 4.0 * (double)n_out * n_in, st, k_dist_resid, dim3(gx, gy), dim3(256),
+              0, resid, n_out, n_in, ldr, U, ldu, partial);
+  return WSIC_OK;
+}
+
+int launch_sum_partials(const double* partial, int64_t n, double* out, hipStream_t st) {
+  WSIC_LAUNCH("sum_partials", 8.0 * n, st, k_sum_partials, dim3(1), dim3(256), 0, partial, n, out);
+  return WSIC_OK;
+}
+
+int launch_dequant(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
+                   const double* invd, double c, void* W_hat, int w_hat_dtype, int64_t ldh,
+                   hipStream_t st) {
+  const int64_t total = n_out * n_in;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  const double work = (double)total * (4.0 + (w_hat_dtype == WSIC_BF16 ? 2.0 : 4.0));
+  if (w_hat_dtype == WSIC_BF16)
+    WSIC_LAUNCH("dequant", work, st, k_dequant<true>, dim3((unsigned)blocks), dim3(256), 0, codes,
+                n_out, n_in, ldq, invd, c, W_hat, ldh);
+  else
+    WSIC_LAUNCH("dequant", work, st, k_dequant<false>, dim3((unsigned)blocks), dim3(256), 0, codes,
+                n_out, n_in, ldq, invd, c, W_hat, ldh);
+  return WSIC_OK;
+}
+
+}  // namespace wsic

@@ -1,0 +1,149 @@
+// Code histogram and empirical entropy (WaterSIC page, Sommario tecnico §2 item 3: the
+// integer codes are unbounded and entropy coded, so the rate is the entropy of the code
+// histogram).
+//
+// k_hist: each workgroup counts its share of the codes in an LDS window of +-HIST_HALF bins;
+// codes in [-7, 7] (the bulk at 1-4 bits per weight) are first tallied in per-thread
+// registers to avoid LDS atomic contention on a handful of bins. Window counts are then added
+// to a global u64 window; codes outside the window are appended to an overflow list that the
+// host counts exactly.
+// k_entropy_reduce: one workgroup forms sum_k n_k log2 n_k over the window in fp64.
+#include "common.h"
+
+namespace wsic {
+namespace {
+
+constexpr int REG_HALF = 7;  // codes tallied in registers: [-7, 7]
+
+__global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ codes, int64_t n_out,
+                                              int64_t n_in, int64_t ldq,
+                                              unsigned long long* __restrict__ bins,
+                                              int32_t* __restrict__ ovf,
+                                              unsigned int* __restrict__ ovf_count) {
+  __shared__ unsigned int lb[HIST_BINS];
+  for (int b = threadIdx.x; b < HIST_BINS; b += blockDim.x) lb[b] = 0u;
+  __syncthreads();
+
+  unsigned int reg[2 * REG_HALF + 1];
+#pragma unroll
+  for (int k = 0; k < 2 * REG_HALF + 1; ++k) reg[k] = 0u;
+
+  auto count = [&](int v) {
+    if (v >= -REG_HALF && v <= REG_HALF) {
+#pragma unroll
+      for (int k = -REG_HALF; k <= REG_HALF; ++k) reg[k + REG_HALF] += (v == k) ? 1u : 0u;
+    } else if (v >= -HIST_HALF && v <= HIST_HALF) {
+      atomicAdd(&lb[v + HIST_HALF], 1u);
+    } else {
+      const unsigned int slot = atomicAdd(ovf_count, 1u);
+      if (slot < OVF_CAP) ovf[slot] = v;
+    }
+  };
+  const int64_t total = n_out * n_in;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if (ldq == n_in && (((uintptr_t)codes) & 15) == 0) {
+    // dense: 16-byte loads, UNR of them in flight per thread
+    constexpr int UNR = 4;
+    const int4* c4 = reinterpret_cast<const int4*>(codes);
+    const int64_t n4 = total / 4;
+    for (int64_t e = gid; e < n4; e += stride * UNR) {
+      int4 v[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) v[u] = (e + u * stride < n4) ? c4[e + u * stride] : make_int4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        if (e + u * stride < n4) {
+          count(v[u].x);
+          count(v[u].y);
+          count(v[u].z);
+          count(v[u].w);
+        }
+      }
+    }
+    for (int64_t e = n4 * 4 + gid; e < total; e += stride) count(codes[e]);
+  } else {
+    for (int64_t e = gid; e < total; e += stride) count(codes[(e / n_in) * ldq + (e % n_in)]);
+  }
+#pragma unroll
+  for (int k = 0; k < 2 * REG_HALF + 1; ++k)
+    if (reg[k]) atomicAdd(&lb[k - REG_HALF + HIST_HALF], reg[k]);
+  __syncthreads();
+  for (int b = threadIdx.x; b < HIST_BINS; b += blockDim.x)
+    if (lb[b]) atomicAdd(&bins[b], (unsigned long long)lb[b]);
+}
+
+__global__ __launch_bounds__(256) void k_entropy_reduce(const unsigned long long* bins,
+                                                        const unsigned int* ovf_count,
+                                                        const int* flags, EntropyResult* res) {
+  __shared__ double sd[256];
+  __shared__ unsigned long long sn[256];
+  double s = 0.0;
+  unsigned long long nsym = 0;
+  for (int b = threadIdx.x; b < HIST_BINS; b += blockDim.x) {
+    const unsigned long long n = bins[b];
+    if (n) {
+      s += (double)n * log2((double)n);
+      ++nsym;
+    }
+  }
+  sd[threadIdx.x] = s;
+  sn[threadIdx.x] = nsym;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) {
+      sd[threadIdx.x] += sd[threadIdx.x + off];
+      sn[threadIdx.x] += sn[threadIdx.x + off];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    res->sum_nlogn = sd[0];
+    res->nsym = sn[0];
+    res->ovf_count = *ovf_count;
+    res->flags = flags ? *flags : 0;
+  }
+}
+
+__global__ void k_fill_zero(uint32_t* p, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+}  // namespace
+
+int launch_hist(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
+                unsigned long long* bins, int32_t* ovf, unsigned int* ovf_count, hipStream_t st) {
+  const int64_t total = n_out * n_in;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  WSIC_LAUNCH("hist", 4.0 * (double)total, st, k_hist, dim3((unsigned)blocks), dim3(256), 0,
+              codes, n_out, n_in, ldq, bins, ovf, ovf_count);
+  return WSIC_OK;
+}
+
+int launch_entropy_reduce(const unsigned long long* bins, const unsigned int* ovf_count,
+                          const int* flags, EntropyResult* res, hipStream_t st) {
+  WSIC_LAUNCH("entropy", 8.0 * HIST_BINS, st, k_entropy_reduce, dim3(1), dim3(256), 0, bins,
+              ovf_count, flags, res);
+  return WSIC_OK;
+}
+
+// Zero-fill with a kernel (not hipMemsetAsync) so the call stays valid inside graph capture.
+int launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+  if (bytes == 0) return WSIC_OK;
+  if (bytes % 4 != 0) {
+    set_error("internal: fill of %zu bytes", bytes);
+    return WSIC_E_INVAL;
+  }
+  const size_t words = bytes / 4;
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  WSIC_LAUNCH("fill_zero", (double)bytes, st, k_fill_zero, dim3((unsigned)blocks), dim3(256), 0,
+              (uint32_t*)p, words);
+  return WSIC_OK;
+}
+
+}  // namespace wsic

@@ -1,0 +1,848 @@
+// libwsic C ABI: argument checks, workspace layout, the SIC pass driver and the rate
+// controller. All arithmetic runs in the kernels of this library; this file only orders
+// launches on the caller's stream and reads back scalars.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace wsic {
+
+// ============================================================== error state
+static thread_local char g_err[1024] = {0};
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+}
+void clear_error() { g_err[0] = 0; }
+const char* last_error() { return g_err; }
+
+// ============================================================== launch timing
+namespace {
+struct PendingEvent {
+  std::string family;
+  hipEvent_t a, b;
+  double work;
+};
+struct ProfAcc {
+  int64_t launches = 0;
+  double ms = 0.0, work = 0.0;
+};
+bool g_prof = false;
+std::vector<PendingEvent> g_pending;
+std::map<std::string, ProfAcc> g_acc;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pool_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+int prof_collect() {
+  for (auto& p : g_pending) {
+    if (!p.a || !p.b) continue;
+    WSIC_HIP_TRY(hipEventSynchronize(p.b));
+    float ms = 0.f;
+    WSIC_HIP_TRY(hipEventElapsedTime(&ms, p.a, p.b));
+    ProfAcc& acc = g_acc[p.family];
+    acc.launches += 1;
+    acc.ms += ms;
+    acc.work += p.work;
+    g_event_pool.push_back(p.a);
+    g_event_pool.push_back(p.b);
+  }
+  g_pending.clear();
+  return WSIC_OK;
+}
+}  // namespace
+
+ProfToken prof_begin(const char* family, hipStream_t st) {
+  if (!g_prof) return ProfToken{-1};
+  PendingEvent p{family, pool_event(), pool_event(), 0.0};
+  if (p.a) (void)hipEventRecord(p.a, st);
+  g_pending.push_back(p);
+  return ProfToken{(int)g_pending.size() - 1};
+}
+
+void prof_end(ProfToken t, hipStream_t st, double work) {
+  if (t.slot < 0 || t.slot >= (int)g_pending.size()) return;
+  PendingEvent& p = g_pending[t.slot];
+  if (p.b) (void)hipEventRecord(p.b, st);
+  p.work = work;
+}
+
+// ============================================================== workspace layouts
+namespace {
+
+constexpr size_t FLAGS_BYTES = 256;
+constexpr int BW = 128;  // SIC leaf width
+
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* p) : base((char*)p) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+struct SicWs {
+  int* flags;
+  double* invd;
+  double* Y;
+  double* G;
+  double* Bpk;
+};
+SicWs carve_sic(Carve& cv, int64_t n_out, int64_t n_in) {
+  SicWs w;
+  w.flags = cv.take<int>(FLAGS_BYTES / sizeof(int));
+  w.invd = cv.take<double>((size_t)n_in);
+  w.Y = cv.take<double>((size_t)n_out * n_in);
+  w.G = cv.take<double>((size_t)n_out * n_in);
+  w.Bpk = cv.take<double>((size_t)sic_pack_doubles(n_in));
+  return w;
+}
+
+struct HistWs {
+  unsigned long long* bins;
+  unsigned int* ovf_count;
+  int32_t* ovf;
+  EntropyResult* res;
+};
+HistWs carve_hist(Carve& cv) {
+  HistWs h;
+  // bins and the overflow counter are adjacent so one fill clears both
+  h.bins = cv.take<unsigned long long>(HIST_BINS + 32);
+  h.ovf_count = (unsigned int*)(h.bins ? h.bins + HIST_BINS : nullptr);
+  h.ovf = cv.take<int32_t>(OVF_CAP);
+  h.res = cv.take<EntropyResult>(1);
+  return h;
+}
+constexpr size_t HIST_CLEAR_BYTES = (HIST_BINS + 32) * sizeof(unsigned long long);
+
+struct WfWs {
+  SicWs sic;
+  int32_t* codes2;
+  float* resid2;
+  double* colvar;
+  double* diag;
+  HistWs hist;
+};
+WfWs carve_wf(Carve& cv, int64_t n_out, int64_t n_in) {
+  WfWs w;
+  w.sic = carve_sic(cv, n_out, n_in);
+  w.codes2 = cv.take<int32_t>((size_t)n_out * n_in);
+  w.resid2 = cv.take<float>((size_t)n_out * n_in);
+  w.colvar = cv.take<double>((size_t)colstats_doubles(n_out, n_in) + n_in);
+  w.diag = cv.take<double>((size_t)n_in);
+  w.hist = carve_hist(cv);
+  return w;
+}
+
+int64_t dist_partials(int64_t n_out, int64_t n_in) {
+  const int64_t a = ((n_in + 255) / 256) * ((n_out + 255) / 256);
+  const int64_t b = ((n_out + 63) / 64) * ((n_in + 63) / 64);
+  return std::max(a, b);
+}
+struct DistWs {
+  int* flags;
+  double* invd;
+  double* delta;
+  double* partial;
+  double* out;
+};
+DistWs carve_dist(Carve& cv, int64_t n_out, int64_t n_in) {
+  DistWs d;
+  d.flags = cv.take<int>(FLAGS_BYTES / sizeof(int));
+  d.invd = cv.take<double>((size_t)n_in);
+  d.delta = cv.take<double>((size_t)n_in);
+  d.partial = cv.take<double>((size_t)dist_partials(n_out, n_in));
+  d.out = cv.take<double>(1);
+  return d;
+}
+
+size_t ws_bytes_for(int op, int64_t n_out, int64_t n_in) {
+  Carve cv(nullptr);
+  switch (op) {
+    case WSIC_OP_COVARIANCE:
+    case WSIC_OP_CHOLESKY:
+      cv.take<int>(FLAGS_BYTES / sizeof(int));
+      break;
+    case WSIC_OP_SIC:
+      carve_sic(cv, n_out, n_in);
+      break;
+    case WSIC_OP_WATERFILL:
+      carve_wf(cv, n_out, n_in);
+      break;
+    case WSIC_OP_ENTROPY:
+      cv.take<int>(FLAGS_BYTES / sizeof(int));
+      carve_hist(cv);
+      break;
+    case WSIC_OP_DISTORTION:
+      carve_dist(cv, n_out, n_in);
+      break;
+    default:
+      return 0;
+  }
+  return cv.off;
+}
+
+// ============================================================== checks
+int check_ws(int op, int64_t n_out, int64_t n_in, void* ws, size_t ws_bytes) {
+  const size_t need = ws_bytes_for(op, n_out, n_in);
+  if (!ws || ws_bytes < need) {
+    set_error("workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
+    return WSIC_E_WORKSPACE;
+  }
+  if (((uintptr_t)ws) % 256 != 0) {
+    set_error("workspace must be 256-byte aligned");
+    return WSIC_E_INVAL;
+  }
+  return WSIC_OK;
+}
+
+int check_layer(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw) {
+  if (!W) {
+    set_error("W is null");
+    return WSIC_E_INVAL;
+  }
+  if (dtype != WSIC_F32 && dtype != WSIC_BF16) {
+    set_error("unknown dtype %d", dtype);
+    return WSIC_E_INVAL;
+  }
+  if (n_out <= 0 || n_in <= 0 || ldw < n_in) {
+    set_error("bad layer shape n_out=%lld n_in=%lld ldw=%lld", (long long)n_out, (long long)n_in,
+              (long long)ldw);
+    return WSIC_E_INVAL;
+  }
+  if (n_in > (int64_t)1 << 20 || n_out > (int64_t)1 << 28) {
+    set_error("layer too large");
+    return WSIC_E_INVAL;
+  }
+  return WSIC_OK;
+}
+
+#define WSIC_TRY(expr)         \
+  do {                         \
+    int _rc = (expr);          \
+    if (_rc != WSIC_OK) return _rc; \
+  } while (0)
+
+int read_flags(const int* dflags, int* out, hipStream_t st) {
+  WSIC_HIP_TRY(hipMemcpyAsync(out, dflags, sizeof(int), hipMemcpyDeviceToHost, st));
+  WSIC_HIP_TRY(hipStreamSynchronize(st));
+  return WSIC_OK;
+}
+
+int flags_status(int f, const char* what) {
+  if (f & FLAG_NONFINITE) {
+    set_error("%s: NaN or Inf in an input", what);
+    return WSIC_E_NONFINITE;
+  }
+  if (f & FLAG_BAD_DIAG) {
+    set_error("%s: U has a diagonal entry that is not positive and finite", what);
+    return WSIC_E_INVAL;
+  }
+  if (f & FLAG_RANGE) {
+    set_error("%s: a code does not fit int32 (grid scale too small)", what);
+    return WSIC_E_RANGE;
+  }
+  return WSIC_OK;
+}
+
+// ============================================================== SIC pass
+struct SicCtx {
+  int64_t n_out, n_in;
+  const void* W;
+  int dtype;
+  int64_t ldw;
+  const double* U;
+  int64_t ldu;
+  SicWs ws;
+  hipStream_t st;
+};
+
+// invd, Y = W U^T, input checks. Leaves flags on the device (read by the caller).
+int sic_setup(const SicCtx& x) {
+  WSIC_TRY(launch_fill_zero(x.ws.flags, FLAGS_BYTES, x.st));
+  WSIC_TRY(launch_check_finite(x.W, x.dtype, x.n_out, x.n_in, x.ldw, x.ws.flags, x.st));
+  WSIC_TRY(launch_prep(x.U, x.ldu, x.n_in, x.ws.invd, x.ws.flags, x.st));
+  WSIC_TRY(launch_pack_blocks(x.U, x.ldu, x.n_in, x.ws.invd, x.ws.Bpk, x.st));
+  GemmArgs g{};
+  g.M = x.n_out;
+  g.N = x.n_in;
+  g.K = x.n_in;
+  g.A = x.W;
+  g.lda = x.ldw;
+  g.B = x.U;
+  g.ldb = x.ldu;
+  g.C = x.ws.Y;
+  g.ldc = x.n_in;
+  g.alpha = 1.0;
+  g.beta = 0.0;
+  g.tri = 1;
+  const double work = (double)x.n_out * (double)x.n_in * (double)(x.n_in + 1);
+  WSIC_TRY(launch_gemm(x.dtype == WSIC_BF16 ? A_BF16 : A_F32, EPI_STORE, g, "gemm_y", work, x.st));
+  int f = 0;
+  WSIC_TRY(read_flags(x.ws.flags, &f, x.st));
+  return flags_status(f, "sic");
+}
+
+// Columns [lo, hi): G[:, lo:hi] holds the interference of every column >= hi (none when
+// hi == n_in). Right half first, then its interference on the left half, then the left half.
+int sic_range(const SicCtx& x, int64_t lo, int64_t hi, double c, int32_t* codes, int64_t ldq,
+              float* resid, int64_t ldr) {
+  const int64_t w = hi - lo;
+  const bool has_g = hi < x.n_in;
+  if (w <= BW)
+    return launch_sic_leaf(x.n_out, lo, (int)w, x.ws.Y, x.n_in, has_g ? x.ws.G : nullptr, x.n_in,
+                           x.ws.Bpk, x.ws.invd, c, codes, ldq, resid, ldr, x.ws.flags, x.st);
+  const int64_t nblk = (w + BW - 1) / BW;
+  const int64_t mid = lo + BW * ((nblk + 1) / 2);
+  WSIC_TRY(sic_range(x, mid, hi, c, codes, ldq, resid, ldr));
+  GemmArgs g{};
+  g.M = x.n_out;
+  g.N = mid - lo;
+  g.K = hi - mid;
+  g.A = codes + mid;
+  g.lda = ldq;
+  g.vec = x.ws.invd + mid;
+  g.B = x.U + lo * x.ldu + mid;
+  g.ldb = x.ldu;
+  g.C = x.ws.G + lo;
+  g.ldc = x.n_in;
+  g.alpha = 1.0;
+  g.beta = has_g ? 1.0 : 0.0;
+  const double work = 2.0 * (double)g.M * (double)g.N * (double)g.K;
+  WSIC_TRY(launch_gemm(A_CODES, EPI_STORE, g, "gemm_trail", work, x.st));
+  return sic_range(x, lo, mid, c, codes, ldq, resid, ldr);
+}
+
+int sic_pass(const SicCtx& x, double c, int32_t* codes, int64_t ldq, float* resid, int64_t ldr) {
+  return sic_range(x, 0, x.n_in, c, codes, ldq, resid, ldr);
+}
+
+// ============================================================== entropy
+int entropy_of(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq, const HistWs& h,
+               const int* dflags, hipStream_t st, double* H, int64_t* nsym, int* flags_out) {
+  WSIC_TRY(launch_fill_zero(h.bins, HIST_CLEAR_BYTES, st));
+  WSIC_TRY(launch_hist(codes, n_out, n_in, ldq, h.bins, h.ovf, h.ovf_count, st));
+  WSIC_TRY(launch_entropy_reduce(h.bins, h.ovf_count, dflags, h.res, st));
+  EntropyResult r;
+  WSIC_HIP_TRY(hipMemcpyAsync(&r, h.res, sizeof r, hipMemcpyDeviceToHost, st));
+  WSIC_HIP_TRY(hipStreamSynchronize(st));
+  if (flags_out) *flags_out = r.flags;
+  double s = r.sum_nlogn;
+  int64_t ns = (int64_t)r.nsym;
+  if (r.ovf_count > 0) {
+    if (r.ovf_count > OVF_CAP) {
+      set_error("entropy: %u codes beyond +-%d exceed the overflow list (%u)", r.ovf_count,
+                HIST_HALF, OVF_CAP);
+      return WSIC_E_RANGE;
+    }
+    std::vector<int32_t> v(r.ovf_count);
+    WSIC_HIP_TRY(hipMemcpyAsync(v.data(), h.ovf, v.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                                st));
+    WSIC_HIP_TRY(hipStreamSynchronize(st));
+    std::sort(v.begin(), v.end());
+    size_t i = 0;
+    while (i < v.size()) {
+      size_t j = i;
+      while (j < v.size() && v[j] == v[i]) ++j;
+      const double cnt = (double)(j - i);
+      s += cnt * std::log2(cnt);
+      ++ns;
+      i = j;
+    }
+  }
+  const double N = (double)n_out * (double)n_in;
+  *H = std::log2(N) - s / N;
+  if (nsym) *nsym = ns;
+  return WSIC_OK;
+}
+
+}  // namespace
+}  // namespace wsic
+
+using namespace wsic;
+
+// ============================================================== C ABI
+extern "C" {
+
+int wsic_version(void) { return WSIC_VERSION; }
+
+const char* wsic_last_error(void) { return wsic::last_error(); }
+
+const char* wsic_status_str(int s) {
+  switch (s) {
+    case WSIC_OK: return "WSIC_OK";
+    case WSIC_E_INVAL: return "WSIC_E_INVAL";
+    case WSIC_E_NOT_PD: return "WSIC_E_NOT_PD";
+    case WSIC_E_NONFINITE: return "WSIC_E_NONFINITE";
+    case WSIC_E_NO_BRACKET: return "WSIC_E_NO_BRACKET";
+    case WSIC_E_RANGE: return "WSIC_E_RANGE";
+    case WSIC_E_WORKSPACE: return "WSIC_E_WORKSPACE";
+    case WSIC_E_HIP: return "WSIC_E_HIP";
+    default: return "WSIC_E_UNKNOWN";
+  }
+}
+
+size_t wsic_workspace_bytes(int op, int64_t n_out, int64_t n_in) {
+  if (n_in <= 0 || (op != WSIC_OP_COVARIANCE && op != WSIC_OP_CHOLESKY && n_out <= 0)) return 0;
+  return ws_bytes_for(op, n_out, n_in);
+}
+
+int wsic_covariance(const void* X, int dtype, int64_t rows, int64_t n_in, int64_t ldx,
+                    double alpha, double beta, double* Sigma, int64_t lds, void* ws,
+                    size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    if (!X || !Sigma || rows <= 0 || n_in <= 0 || ldx < n_in || lds < n_in ||
+        (dtype != WSIC_F32 && dtype != WSIC_BF16) || !std::isfinite(alpha) || !std::isfinite(beta)) {
+      set_error("covariance: bad argument");
+      return WSIC_E_INVAL;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_COVARIANCE, 0, n_in, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    int* flags = (int*)ws;
+    WSIC_TRY(launch_fill_zero(flags, FLAGS_BYTES, st));
+    WSIC_TRY(launch_syrk(X, dtype, rows, n_in, ldx, alpha, beta, Sigma, lds, st));
+    WSIC_TRY(launch_mirror_upper(Sigma, n_in, lds, st));
+    WSIC_TRY(launch_diag_check(Sigma, n_in, lds, flags, st));
+    int f = 0;
+    WSIC_TRY(read_flags(flags, &f, st));
+    return flags_status(f, "covariance");
+  } catch (...) {
+    set_error("covariance: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_cholesky(double* A, int64_t n, int64_t lda, int64_t* info, void* ws, size_t ws_bytes,
+                  void* stream) {
+  try {
+    clear_error();
+    if (!A || !info || n <= 0 || lda < n) {
+      set_error("cholesky: bad argument");
+      return WSIC_E_INVAL;
+    }
+    *info = 0;
+    WSIC_TRY(check_ws(WSIC_OP_CHOLESKY, 0, n, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    int64_t* dinfo = (int64_t*)ws;
+    WSIC_TRY(launch_fill_zero(dinfo, FLAGS_BYTES, st));
+    constexpr int NBK = 64;
+    for (int64_t kb = 0; kb < n; kb += NBK) {
+      const int nbk = (int)std::min<int64_t>(NBK, n - kb);
+      WSIC_TRY(launch_potrf_diag(A, lda, kb, nbk, dinfo, st));
+      const int64_t m = n - kb - nbk;
+      if (m <= 0) break;
+      WSIC_TRY(launch_trsm_row(A, lda, kb, nbk, n, dinfo, st));
+      GemmArgs g{};
+      g.M = m;
+      g.N = m;
+      g.K = nbk;
+      g.A = A + kb * lda + kb + nbk;
+      g.lda = lda;
+      g.B = A + kb * lda + kb + nbk;
+      g.ldb = lda;
+      g.C = A + (kb + nbk) * lda + kb + nbk;
+      g.ldc = lda;
+      g.alpha = -1.0;
+      g.beta = 1.0;
+      g.upper_only = 1;
+      const double work = (double)m * (double)(m + 1) * (double)nbk;
+      WSIC_TRY(launch_gemm(A_F64_T, EPI_STORE, g, "gemm_chol", work, st));
+    }
+    WSIC_TRY(launch_zero_lower(A, n, lda, st));
+    WSIC_HIP_TRY(hipMemcpyAsync(info, dinfo, sizeof(int64_t), hipMemcpyDeviceToHost, st));
+    WSIC_HIP_TRY(hipStreamSynchronize(st));
+    if (*info != 0) {
+      set_error("cholesky: leading minor %lld is not positive definite", (long long)*info);
+      return WSIC_E_NOT_PD;
+    }
+    return WSIC_OK;
+  } catch (...) {
+    set_error("cholesky: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_sic_quantize(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                      const double* U, int64_t ldu, double c, int32_t* codes, int64_t ldq,
+                      float* resid, int64_t ldr, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    WSIC_TRY(check_layer(W, dtype, n_out, n_in, ldw));
+    if (!U || ldu < n_in || !codes || ldq < n_in || (resid && ldr < n_in) || !(c > 0.0) ||
+        !std::isfinite(c)) {
+      set_error("sic_quantize: bad argument");
+      return WSIC_E_INVAL;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_SIC, n_out, n_in, ws, ws_bytes));
+    Carve cv(ws);
+    SicCtx x{n_out, n_in, W, dtype, ldw, U, ldu, carve_sic(cv, n_out, n_in), (hipStream_t)stream};
+    WSIC_TRY(sic_setup(x));
+    WSIC_TRY(sic_pass(x, c, codes, ldq, resid, ldr));
+    int f = 0;
+    WSIC_TRY(read_flags(x.ws.flags, &f, x.st));
+    return flags_status(f, "sic_quantize");
+  } catch (...) {
+    set_error("sic_quantize: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                   const double* U, int64_t ldu, double target_bits, const wsic_wf_opts* opts,
+                   double* c_out, double* rate_out, int32_t* passes_out, int32_t* codes,
+                   int64_t ldq, float* resid, int64_t ldr, void* ws, size_t ws_bytes,
+                   void* stream) {
+  try {
+    clear_error();
+    WSIC_TRY(check_layer(W, dtype, n_out, n_in, ldw));
+    if (!U || ldu < n_in || !codes || ldq < n_in || (resid && ldr < n_in) || !c_out ||
+        !rate_out || !(target_bits > 0.0) || !std::isfinite(target_bits)) {
+      set_error("waterfill: bad argument");
+      return WSIC_E_INVAL;
+    }
+    wsic_wf_opts o{2e-5, std::ldexp(1.0, -20), 64, WSIC_WF_AUTO, 0.0};
+    if (opts) {
+      o = *opts;
+      if (!(o.rate_tol >= 0.0)) o.rate_tol = 2e-5;
+      if (!(o.bracket_log2 > 0.0)) o.bracket_log2 = std::ldexp(1.0, -20);
+      if (o.max_passes <= 0) o.max_passes = 64;
+      if (o.mode != WSIC_WF_AUTO && o.mode != WSIC_WF_SECANT && o.mode != WSIC_WF_BISECT) {
+        set_error("waterfill: unknown mode %d", o.mode);
+        return WSIC_E_INVAL;
+      }
+    }
+    if (o.mode == WSIC_WF_AUTO)
+      o.mode = (n_out * n_in < WSIC_WF_AUTO_PARAMS) ? WSIC_WF_BISECT : WSIC_WF_SECANT;
+    const bool trace = std::getenv("WSIC_TRACE") != nullptr;
+    WSIC_TRY(check_ws(WSIC_OP_WATERFILL, n_out, n_in, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    Carve cv(ws);
+    WfWs wf = carve_wf(cv, n_out, n_in);
+    SicCtx x{n_out, n_in, W, dtype, ldw, U, ldu, wf.sic, st};
+    WSIC_TRY(sic_setup(x));
+
+    const double R = target_bits;
+    // starting grid scale
+    double c0 = o.c_init;
+    if (!(c0 > 0.0)) {
+      WSIC_TRY(launch_colstats(W, dtype, n_out, n_in, ldw, wf.colvar + n_in, wf.colvar, st));
+      WSIC_TRY(launch_delta(U, ldu, n_in, 1.0, nullptr, wf.diag, st));
+      std::vector<double> var(n_in), diag(n_in);
+      WSIC_HIP_TRY(hipMemcpyAsync(var.data(), wf.colvar, n_in * sizeof(double),
+                                  hipMemcpyDeviceToHost, st));
+      WSIC_HIP_TRY(hipMemcpyAsync(diag.data(), wf.diag, n_in * sizeof(double),
+                                  hipMemcpyDeviceToHost, st));
+      WSIC_HIP_TRY(hipStreamSynchronize(st));
+      double m = 0.0;
+      for (int64_t j = 0; j < n_in; ++j) m += var[j] * diag[j] * diag[j];
+      m /= (double)n_in;
+      if (!(m > 0.0)) m = 1.0;
+      c0 = std::sqrt(2.0 * M_PI * M_E * m) * std::pow(2.0, -R);
+    }
+
+    // two code buffers: the caller's and one in the workspace; `hi_buf` holds the codes of
+    // the best grid scale so far with H <= R
+    int32_t* cbuf[2] = {codes, wf.codes2};
+    float* rbuf[2] = {resid, resid ? wf.resid2 : nullptr};
+    int passes = 0;
+    int hi_buf = -1;
+    double c_hi = 0, h_hi = 0, c_lo = 0, h_lo = 0;
+    bool have_hi = false, have_lo = false;
+
+    auto eval = [&](double c, int buf, double* H) -> int {
+      if (passes >= o.max_passes) {
+        set_error("waterfill: pass limit %d reached", o.max_passes);
+        return WSIC_E_NO_BRACKET;
+      }
+      ++passes;
+      WSIC_TRY(sic_pass(x, c, cbuf[buf], ldq, rbuf[buf], ldr));
+      int f = 0;
+      WSIC_TRY(entropy_of(cbuf[buf], n_out, n_in, ldq, wf.hist, wf.sic.flags, st, H, nullptr, &f));
+      if (trace) std::fprintf(stderr, "wsic waterfill pass %d: c=%.17g H=%.17g\n", passes, c, *H);
+      return flags_status(f, "waterfill");
+    };
+    auto free_buf = [&]() { return hi_buf == 0 ? 1 : 0; };
+    // record an evaluation at c into buffer b
+    auto take = [&](double c, double h, int b) {
+      if (h <= R) {
+        if (!have_hi || c < c_hi) {
+          c_hi = c;
+          h_hi = h;
+          hi_buf = b;
+          have_hi = true;
+        }
+      } else {
+        if (!have_lo || c > c_lo) {
+          c_lo = c;
+          h_lo = h;
+          have_lo = true;
+        }
+      }
+    };
+
+    int rc = WSIC_OK;
+    if (o.mode == WSIC_WF_BISECT) {
+      // doubling/halving bracket, then geometric bisection on the bracket
+      double c = c0, h;
+      int b = free_buf();
+      WSIC_TRY(eval(c, b, &h));
+      take(c, h, b);
+      int n = 0;
+      while (h > R) {
+        if (++n > 64) {
+          set_error("waterfill: no bracket (rate stays above target)");
+          return WSIC_E_NO_BRACKET;
+        }
+        c *= 2.0;
+        b = free_buf();
+        WSIC_TRY(eval(c, b, &h));
+        take(c, h, b);
+      }
+      c = c_hi / 2.0;
+      b = free_buf();
+      WSIC_TRY(eval(c, b, &h));
+      take(c, h, b);
+      n = 0;
+      while (h <= R) {
+        if (++n > 64) {
+          set_error("waterfill: no bracket (rate stays below target)");
+          return WSIC_E_NO_BRACKET;
+        }
+        c = c / 2.0;
+        b = free_buf();
+        WSIC_TRY(eval(c, b, &h));
+        take(c, h, b);
+      }
+      while (std::log2(c_hi / c_lo) > o.bracket_log2) {
+        const double m = std::sqrt(c_lo * c_hi);
+        b = free_buf();
+        WSIC_TRY(eval(m, b, &h));
+        take(m, h, b);
+      }
+    } else {
+      // secant on x = log2 c toward H = R - tol/2 through the two latest evaluations (slope -1,
+      // the high-rate law, until two points exist); once both sides of R are known the step must
+      // land strictly inside the bracket, else -- or when the bracket has not halved in two
+      // steps -- bisect.
+      const double Rt = R - 0.5 * o.rate_tol;
+      auto accept = [&]() { return have_hi && h_hi > R - o.rate_tol; };
+      double xa = std::log2(c0), ha = 0.0;
+      int b = free_buf();
+      WSIC_TRY(eval(c0, b, &ha));
+      take(c0, ha, b);
+      double xb = xa, hb = ha;
+      bool have_two = false;
+      double width_prev = INFINITY;
+      int slow = 0;
+      while (!accept()) {
+        const bool bracketed = have_hi && have_lo;
+        double xl = 0.0, xh = 0.0;
+        if (bracketed) {
+          xl = std::log2(c_lo);
+          xh = std::log2(c_hi);
+          if (xh - xl <= o.bracket_log2) break;
+        }
+        double slope = -1.0;
+        if (have_two && xb != xa) {
+          const double s = (hb - ha) / (xb - xa);
+          if (s < -1e-3) slope = s;
+        }
+        double xn = xb + (Rt - hb) / slope;
+        if (bracketed) {
+          if (!(xn > xl && xn < xh) || slow >= 2) {
+            xn = 0.5 * (xl + xh);
+            slow = 0;
+          }
+        } else {
+          xn = std::min(xb + 4.0, std::max(xb - 4.0, xn));
+          const double tiny = std::ldexp(1.0, -30);
+          if (!have_lo) xn = std::min(xn, xb - tiny);  // every H so far <= R: shrink c
+          if (!have_hi) xn = std::max(xn, xb + tiny);  // every H so far > R: grow c
+        }
+        const double cn = std::exp2(xn);
+        b = free_buf();
+        double hn;
+        WSIC_TRY(eval(cn, b, &hn));
+        take(cn, hn, b);
+        xa = xb;
+        ha = hb;
+        xb = xn;
+        hb = hn;
+        have_two = true;
+        if (have_hi && have_lo) {
+          const double width = std::log2(c_hi) - std::log2(c_lo);
+          slow = (width > 0.5 * width_prev) ? slow + 1 : 0;
+          width_prev = width;
+        }
+      }
+      if (!have_hi) {
+        set_error("waterfill: target not reached");
+        return WSIC_E_NO_BRACKET;
+      }
+    }
+    (void)h_lo;
+    // the accepted codes must end in the caller's buffers
+    if (hi_buf == 1) {
+      WSIC_HIP_TRY(hipMemcpy2DAsync(codes, ldq * sizeof(int32_t), wf.codes2, ldq * sizeof(int32_t),
+                                    n_in * sizeof(int32_t), n_out, hipMemcpyDeviceToDevice, st));
+      if (resid)
+        WSIC_HIP_TRY(hipMemcpy2DAsync(resid, ldr * sizeof(float), wf.resid2, ldr * sizeof(float),
+                                      n_in * sizeof(float), n_out, hipMemcpyDeviceToDevice, st));
+      WSIC_HIP_TRY(hipStreamSynchronize(st));
+    }
+    *c_out = c_hi;
+    *rate_out = h_hi;
+    if (passes_out) *passes_out = passes;
+    return rc;
+  } catch (...) {
+    set_error("waterfill: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_entropy(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
+                 double* bits_per_param, int64_t* n_symbols, void* ws, size_t ws_bytes,
+                 void* stream) {
+  try {
+    clear_error();
+    if (!codes || !bits_per_param || n_out <= 0 || n_in <= 0 || ldq < n_in) {
+      set_error("entropy: bad argument");
+      return WSIC_E_INVAL;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_ENTROPY, n_out, n_in, ws, ws_bytes));
+    Carve cv(ws);
+    int* flags = cv.take<int>(FLAGS_BYTES / sizeof(int));
+    HistWs h = carve_hist(cv);
+    (void)flags;
+    return entropy_of(codes, n_out, n_in, ldq, h, nullptr, (hipStream_t)stream, bits_per_param,
+                      n_symbols, nullptr);
+  } catch (...) {
+    set_error("entropy: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_distortion(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                    const int32_t* codes, int64_t ldq, const double* U, int64_t ldu, double c,
+                    const float* resid, int64_t ldr, int mode, double* D_out, void* W_hat,
+                    int w_hat_dtype, int64_t ldh, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    WSIC_TRY(check_layer(W, dtype, n_out, n_in, ldw));
+    if (!codes || ldq < n_in || !U || ldu < n_in || !(c > 0.0) || !std::isfinite(c) || !D_out ||
+        (mode != WSIC_D_RESID && mode != WSIC_D_DIRECT) || (mode == WSIC_D_RESID && !resid) ||
+        (resid && ldr < n_in) ||
+        (W_hat && (ldh < n_in || (w_hat_dtype != WSIC_F32 && w_hat_dtype != WSIC_BF16)))) {
+      set_error("distortion: bad argument");
+      return WSIC_E_INVAL;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_DISTORTION, n_out, n_in, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    Carve cv(ws);
+    DistWs d = carve_dist(cv, n_out, n_in);
+    WSIC_TRY(launch_fill_zero(d.flags, FLAGS_BYTES, st));
+    WSIC_TRY(launch_prep(U, ldu, n_in, d.invd, d.flags, st));
+    if (W_hat)
+      WSIC_TRY(launch_dequant(codes, n_out, n_in, ldq, d.invd, c, W_hat, w_hat_dtype, ldh, st));
+    int64_t np = 0;
+    if (mode == WSIC_D_RESID) {
+      np = ((n_in + 255) / 256) * ((n_out + 255) / 256);
+      WSIC_TRY(launch_dist_resid(resid, n_out, n_in, ldr, U, ldu, d.partial, (int)np, st));
+    } else {
+      WSIC_TRY(launch_delta(U, ldu, n_in, c, d.delta, nullptr, st));
+      GemmArgs g{};
+      g.M = n_out;
+      g.N = n_in;
+      g.K = n_in;
+      g.A = W;
+      g.lda = ldw;
+      g.Q = codes;
+      g.ldq = ldq;
+      g.vec = d.delta;
+      g.B = U;
+      g.ldb = ldu;
+      g.alpha = 1.0;
+      g.tri = 1;
+      g.partial = d.partial;
+      np = gemm_tiles(g);
+      const double work = (double)n_out * (double)n_in * (double)(n_in + 1);
+      WSIC_TRY(launch_gemm(dtype == WSIC_BF16 ? A_ERR_BF16 : A_ERR_F32, EPI_SUMSQ, g, "gemm_dist",
+                           work, st));
+    }
+    WSIC_TRY(launch_sum_partials(d.partial, np, d.out, st));
+    WSIC_HIP_TRY(hipMemcpyAsync(D_out, d.out, sizeof(double), hipMemcpyDeviceToHost, st));
+    int f = 0;
+    WSIC_TRY(read_flags(d.flags, &f, st));
+    return flags_status(f, "distortion");
+  } catch (...) {
+    set_error("distortion: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_profile_enable(int on) {
+  g_prof = on != 0;
+  return WSIC_OK;
+}
+
+int wsic_profile_reset(void) {
+  clear_error();
+  WSIC_TRY(prof_collect());
+  g_acc.clear();
+  return WSIC_OK;
+}
+
+int wsic_profile_read(const char* name, int64_t* launches, double* total_ms, double* total_work) {
+  clear_error();
+  if (!name) {
+    set_error("profile_read: null name");
+    return WSIC_E_INVAL;
+  }
+  WSIC_TRY(prof_collect());
+  auto it = g_acc.find(name);
+  const ProfAcc a = (it == g_acc.end()) ? ProfAcc{} : it->second;
+  if (launches) *launches = a.launches;
+  if (total_ms) *total_ms = a.ms;
+  if (total_work) *total_work = a.work;
+  return WSIC_OK;
+}
+
+int wsic_profile_names(char* buf, size_t buf_bytes) {
+  clear_error();
+  WSIC_TRY(prof_collect());
+  std::string s;
+  for (auto& kv : g_acc) {
+    if (!s.empty()) s += ",";
+    s += kv.first;
+  }
+  if (!buf || buf_bytes == 0) return WSIC_E_INVAL;
+  std::snprintf(buf, buf_bytes, "%s", s.c_str());
+  return WSIC_OK;
+}
+
+}  // extern "C"

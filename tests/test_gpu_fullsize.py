@@ -1,0 +1,112 @@
+"""Parity at the full attention-projection workload (W 4096 x 4096 bf16, X 8192 x 4096 bf16,
+R = 2 bits), in the launch configuration the benchmark times. The oracle cannot run the whole
+bisection at this size in test time, so it is checked on sampled rows (rows are independent)
+and through properties that hold at any size."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import DEV, RATE_TOL, REL_TOL, assert_codes_parity, say, w_tensor, x_tensors
+from rate_allocated_weight_amd import _lib as lib
+from rate_allocated_weight_amd import workloads
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+R = 2.0
+N_SAMPLE_ROWS = 16
+
+
+@pytest.fixture(scope="module")
+def run():
+    assert torch.cuda.is_available()
+    say("[fullsize] generating attn_4096")
+    layer = workloads.named_workload("attn_4096")
+    Wt = w_tensor(layer)
+    X = x_tensors(layer)
+    say("[fullsize] device: covariance, cholesky, waterfill (default controller), entropy, distortion")
+    sigma = lib.covariance_chunks(X)
+    sigma_host = sigma.cpu().numpy()
+    U, _ = lib.cholesky(sigma.clone())
+    wf = lib.waterfill(Wt, U, R)
+    h, nsym = lib.entropy(wf["codes"])
+    D, _ = lib.distortion(Wt, wf["codes"], U, wf["c"], resid=wf["resid"])
+    say(f"[fullsize] c={wf['c']:.9g} rate={wf['rate']:.7f} passes={wf['passes']} D={D:.6e} symbols={nsym}")
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, layer.n_out - 1],
+                                     rng.choice(layer.n_out, N_SAMPLE_ROWS - 2, replace=False)]))
+    return dict(layer=layer, Wt=Wt, sigma=sigma_host, U=U, wf=wf, h=h, D=D, rows=rows)
+
+
+def test_covariance_and_factor_fullsize(run):
+    layer = run["layer"]
+    say("[fullsize] oracle covariance + LAPACK factor")
+    sig_or = oracle.covariance(layer.x_chunks)
+    d = np.sqrt(np.diag(sig_or))
+    err = np.max(np.abs(run["sigma"] - sig_or) / np.outer(d, d))
+    say(f"  max normalized |dSigma| = {err:.3e}")
+    assert err <= 1e-6
+    U = run["U"].cpu().numpy()
+    L_or, info = oracle.cholesky_lower(run["sigma"])
+    assert info == 0
+    rel = np.linalg.norm(U - L_or.T) / np.linalg.norm(L_or)
+    say(f"  |U - L^T|/|L| = {rel:.3e}")
+    assert rel <= 1e-8
+
+
+def test_codes_on_sampled_rows(run):
+    layer, rows = run["layer"], run["rows"]
+    L = np.ascontiguousarray(run["U"].cpu().numpy().T)
+    say(f"[fullsize] oracle SIC on {len(rows)} sampled rows at the device's c")
+    sic = oracle.sic_quantize(layer.w[rows], L, run["wf"]["c"])
+    q = run["wf"]["codes"].cpu().numpy()
+    assert_codes_parity(q[rows], sic, label="attn_4096 sample")
+    # residuals of the same rows
+    r = run["wf"]["resid"].cpu().numpy()[rows].astype(np.float64)
+    err = np.abs(r - sic["r"]) / sic["alpha"][None, :]
+    assert err.max() < 1e-6
+    # per-row distortion (rows are independent): the device's residuals against the oracle's
+    # direct tr(E Sigma E^T) on each sampled row
+    d2 = np.diag(L) ** 2
+    for i, rr in enumerate(rows):
+        e = layer.w[rr].astype(np.float64) - sic["q"][i] * sic["alpha"]
+        d_or = float(e @ run["sigma"] @ e)
+        d_dev = float(np.sum(d2 * r[i] ** 2))
+        assert d_dev == pytest.approx(d_or, rel=1e-5)
+
+
+def test_rate_is_entropy_of_codes(run):
+    q = run["wf"]["codes"].cpu().numpy()
+    h_cpu = oracle.entropy_bits(q)
+    say(f"[fullsize] entropy device {run['h']:.12f} oracle {h_cpu:.12f} controller {run['wf']['rate']:.12f}")
+    assert run["h"] == pytest.approx(h_cpu, abs=1e-12)
+    assert run["wf"]["rate"] == pytest.approx(h_cpu, abs=1e-12)
+    assert R - RATE_TOL < run["wf"]["rate"] <= R
+
+
+def test_grid_scale_is_the_crossing(run):
+    """c is where the rate crosses the budget: a pass at c (1 - 1e-3) exceeds it."""
+    c = run["wf"]["c"]
+    codes, _ = lib.sic_quantize(run["Wt"], run["U"], c * (1 - REL_TOL))
+    h_below, _ = lib.entropy(codes)
+    say(f"[fullsize] H(c(1-1e-3)) = {h_below:.7f}")
+    assert h_below > R
+
+
+def test_default_controller_matches_bisection(run):
+    """The reference bisection (the oracle's search, run on the device) lands within the
+    parity tolerances of the fast controller at this size."""
+    wf_b = lib.waterfill(run["Wt"], run["U"], R, mode="bisect", want_resid=False)
+    say(f"[fullsize] bisect c={wf_b['c']:.9g} rate={wf_b['rate']:.7f} passes={wf_b['passes']}")
+    assert abs(wf_b["c"] / run["wf"]["c"] - 1) <= REL_TOL
+    assert abs(wf_b["rate"] - run["wf"]["rate"]) <= RATE_TOL
+
+
+def test_distortion_modes_agree(run):
+    D_dir, _ = lib.distortion(run["Wt"], run["wf"]["codes"], run["U"], run["wf"]["c"], mode="direct")
+    n_p = run["layer"].n_out * run["layer"].n_in
+    say(f"[fullsize] D resid {run['D']:.9e} direct {D_dir:.9e}; D/(N c^2/12) = "
+        f"{run['D'] / (n_p * run['wf']['c'] ** 2 / 12):.4f}")
+    assert run["D"] == pytest.approx(D_dir, rel=1e-5)

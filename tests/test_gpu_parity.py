@@ -1,0 +1,291 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, element by element, at
+sizes the oracle finishes in seconds: several 64/128-wide tiles and a ragged tail."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import (DEV, RATE_TOL, REL_TOL, assert_codes_parity, say, w_tensor, x_tensors)
+from rate_allocated_weight_amd import _lib as lib
+from rate_allocated_weight_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+LAYERS = {
+    # name: (recipe, n_out, n_in, n_rows, kwargs)
+    "ar1_256_f32": ("ar1", 256, 256, 1024, dict(dtype="f32", rho=0.9)),
+    "spiked_300x333": ("spiked", 300, 333, 900, dict(dtype="bf16", rank=16)),
+    "blockar1_77x520": ("blockar1", 77, 520, 1100, dict(dtype="bf16", block=96, chunk_rows=400)),
+    "outliers_130x200": ("ar1", 130, 200, 600, dict(dtype="bf16", rho=0.95, scale_sigma=0.5,
+                                                   outlier_cols=3)),
+}
+
+
+def _layer(name, seed=0):
+    recipe, n_out, n_in, n_rows, kw = LAYERS[name]
+    return workloads.make_layer(recipe, n_out, n_in, n_rows, seed=seed, name=name, **kw)
+
+
+def _sigma_oracle(layer):
+    return oracle.covariance(layer.x_chunks)
+
+
+@pytest.fixture(scope="module")
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    lib.lib()
+    return torch.device(DEV)
+
+
+# ------------------------------------------------------------------ covariance
+@pytest.mark.parametrize("name", list(LAYERS))
+def test_covariance_parity(device, name):
+    layer = _layer(name)
+    say(f"[covariance] {name} rows={layer.n_rows} n_in={layer.n_in} chunks={len(layer.x_chunks)}")
+    sig_gpu = lib.covariance_chunks(x_tensors(layer)).cpu().numpy()
+    sig_or = _sigma_oracle(layer)
+    scale = np.sqrt(np.outer(np.diag(sig_or), np.diag(sig_or)))
+    err = np.max(np.abs(sig_gpu - sig_or) / scale)
+    say(f"  max normalized |dSigma| = {err:.3e}")
+    assert np.array_equal(sig_gpu, sig_gpu.T)
+    tol = 1e-12 if layer.dtype == "f32" else 1e-6
+    assert err <= tol
+
+
+def test_covariance_streaming_beta(device):
+    layer = _layer("spiked_300x333")
+    X = x_tensors(layer)[0]
+    s1 = lib.covariance(X, alpha=0.5)
+    s2 = lib.covariance(X, sigma=s1.clone(), alpha=0.25, beta=2.0)  # 2*(0.5 G) + 0.25 G
+    ref = s1 * 2.5
+    assert torch.allclose(s2, ref, rtol=1e-12, atol=0)
+
+
+# ------------------------------------------------------------------ cholesky
+@pytest.mark.parametrize("n,kind", [(64, "ar1"), (200, "spd"), (333, "spd"), (1000, "ar1"), (1031, "spd")])
+def test_cholesky_parity(device, n, kind):
+    say(f"[cholesky] n={n} {kind}")
+    rng = np.random.default_rng(n)
+    if kind == "ar1":
+        idx = np.arange(n)
+        sig = 0.9 ** np.abs(idx[:, None] - idx[None, :])
+    else:
+        g = rng.standard_normal((n, n + 20))
+        d = np.exp(rng.standard_normal(n))
+        sig = (g @ g.T) / (n + 20) * np.outer(d, d)
+    L, info = oracle.cholesky_lower(sig)
+    assert info == 0
+    A = torch.from_numpy(sig.copy()).to(device)
+    A[torch.tril(torch.ones(n, n, dtype=torch.bool, device=device), -1)] = float("nan")  # lower is never read
+    U, info_gpu = lib.cholesky(A)
+    assert info_gpu == 0
+    U = U.cpu().numpy()
+    assert np.all(np.tril(U, -1) == 0.0)
+    rel = np.linalg.norm(U - L.T) / np.linalg.norm(L)
+    back = np.linalg.norm(U.T @ U - sig) / np.linalg.norm(sig)
+    say(f"  |U - L^T|/|L| = {rel:.3e}, |U^T U - Sigma|/|Sigma| = {back:.3e}")
+    assert back <= 4 * n * 2.2e-16
+    assert rel <= 1e-9
+
+
+@pytest.mark.parametrize("n,bad", [(40, 7), (300, 117), (300, 1)])
+def test_cholesky_reports_pivot(device, n, bad):
+    say(f"[cholesky-not-pd] n={n} pivot={bad}")
+    idx = np.arange(n)
+    sig = 0.5 ** np.abs(idx[:, None] - idx[None, :])
+    sig[bad - 1, :] = 0.0
+    sig[:, bad - 1] = 0.0
+    _, info_or = oracle.cholesky_lower(sig)
+    with pytest.raises(lib.WsicError) as ei:
+        lib.cholesky(torch.from_numpy(sig).to(device))
+    assert ei.value.status == lib.E_NOT_PD
+    assert ei.value.info == info_or == bad
+
+
+# ------------------------------------------------------------------ SIC pass
+def _oracle_factor_on_device(layer):
+    L, info = oracle.cholesky_lower(_sigma_oracle(layer))
+    assert info == 0
+    return L, torch.from_numpy(np.ascontiguousarray(L.T)).to(DEV)
+
+
+@pytest.mark.parametrize("name", list(LAYERS))
+@pytest.mark.parametrize("bits", [1.0, 2.5, 5.0])
+def test_sic_codes_parity(device, name, bits):
+    layer = _layer(name)
+    L, U = _oracle_factor_on_device(layer)
+    c = oracle.initial_scale(layer.w, L, bits)
+    say(f"[sic] {name} {layer.n_out}x{layer.n_in} c={c:.6g}")
+    codes, resid = lib.sic_quantize(w_tensor(layer), U, c, want_resid=True)
+    sic = oracle.sic_quantize(layer.w, L, c)
+    assert_codes_parity(codes.cpu().numpy(), sic, label=name)
+    r = resid.cpu().numpy().astype(np.float64)
+    same = np.all(codes.cpu().numpy() == sic["q"], axis=1)
+    err = np.abs(r[same] - sic["r"][same]) / sic["alpha"][None, :]
+    say(f"  max |dr|/alpha = {err.max():.3e}")
+    assert err.max() < 1e-6
+
+
+def test_sic_identity_factor_is_rtn(device):
+    layer = _layer("spiked_300x333")
+    n = layer.n_in
+    U = torch.eye(n, dtype=torch.float64, device=device)
+    c = 0.01
+    codes, _ = lib.sic_quantize(w_tensor(layer), U, c)
+    ref = np.rint(layer.w.astype(np.float64) / c).astype(np.int64)
+    assert np.array_equal(codes.cpu().numpy().astype(np.int64), ref)
+
+
+def test_sic_strided_inputs(device):
+    layer = _layer("blockar1_77x520")
+    L, U = _oracle_factor_on_device(layer)
+    n_out, n_in = layer.n_out, layer.n_in
+    big = torch.zeros((n_out, n_in + 40), dtype=torch.bfloat16, device=device)
+    big[:, 7:7 + n_in] = w_tensor(layer)
+    Wv = big[:, 7:7 + n_in]
+    Ubig = torch.zeros((n_in, n_in + 3), dtype=torch.float64, device=device)
+    Ubig[:, :n_in] = U
+    codes_big = torch.full((n_out, n_in + 5), -99, dtype=torch.int32, device=device)
+    c = oracle.initial_scale(layer.w, L, 2.0)
+    lib.sic_quantize(Wv, Ubig[:, :n_in], c, codes=codes_big[:, :n_in])
+    sic = oracle.sic_quantize(layer.w, L, c)
+    assert_codes_parity(codes_big[:, :n_in].cpu().numpy(), sic, label="strided")
+    assert torch.all(codes_big[:, n_in:] == -99)
+
+
+# ------------------------------------------------------------------ controller
+@pytest.mark.parametrize("name", ["ar1_256_f32", "spiked_300x333", "blockar1_77x520"])
+def test_waterfill_bisect_follows_oracle(device, name):
+    layer = _layer(name)
+    L, U = _oracle_factor_on_device(layer)
+    R = 2.0
+    say(f"[waterfill-bisect] {name} R={R}")
+    wf = lib.waterfill(w_tensor(layer), U, R, mode="bisect")
+    ref = oracle.waterfill(layer.w, L, R)
+    say(f"  gpu c={wf['c']!r} H={wf['rate']!r} passes={wf['passes']}; oracle c={ref['c']!r} H={ref['rate']!r}")
+    assert wf["c"] == pytest.approx(ref["c"], rel=1e-12)
+    assert wf["rate"] == pytest.approx(ref["rate"], abs=1e-12)
+    assert_codes_parity(wf["codes"].cpu().numpy(), ref["sic"], label=name)
+
+
+@pytest.mark.parametrize("name", list(LAYERS))
+@pytest.mark.parametrize("R", [1.0, 2.0, 3.5])
+def test_waterfill_default_parity(device, name, R):
+    """The default controller on these small layers meets the rate / c / codes bar."""
+    layer = _layer(name)
+    L, U = _oracle_factor_on_device(layer)
+    say(f"[waterfill-auto] {name} R={R}")
+    wf = lib.waterfill(w_tensor(layer), U, R)
+    ref = oracle.waterfill(layer.w, L, R)
+    say(f"  gpu c={wf['c']:.9g} H={wf['rate']:.7f} passes={wf['passes']}; oracle c={ref['c']:.9g} "
+        f"H={ref['rate']:.7f} passes={len(ref['trace'])}")
+    assert wf["rate"] <= R
+    assert abs(wf["rate"] - ref["rate"]) <= RATE_TOL
+    assert abs(wf["c"] / ref["c"] - 1) <= REL_TOL
+    # the returned codes are the oracle's codes at the returned grid scale
+    sic = oracle.sic_quantize(layer.w, L, wf["c"])
+    assert_codes_parity(wf["codes"].cpu().numpy(), sic, label=name)
+    assert wf["rate"] == pytest.approx(oracle.entropy_bits(sic["q"]), abs=1e-12)
+
+
+@pytest.mark.parametrize("name", list(LAYERS))
+@pytest.mark.parametrize("R", [1.0, 2.0, 3.5])
+def test_waterfill_secant_small_layers(device, name, R):
+    """On small layers H(c) moves in visible non-monotone steps, so the fast controller may stop
+    at a neighbouring crossing: it must still respect the budget, return the oracle's codes at
+    its own c, and sit close to the oracle's c."""
+    layer = _layer(name)
+    L, U = _oracle_factor_on_device(layer)
+    say(f"[waterfill-secant] {name} R={R}")
+    wf = lib.waterfill(w_tensor(layer), U, R, mode="secant")
+    ref = oracle.waterfill(layer.w, L, R)
+    say(f"  gpu c={wf['c']:.9g} H={wf['rate']:.7f} passes={wf['passes']}; oracle c={ref['c']:.9g} "
+        f"H={ref['rate']:.7f}")
+    assert wf["rate"] <= R
+    assert R - wf["rate"] < 2e-3
+    assert abs(wf["c"] / ref["c"] - 1) <= 2e-2  # jumps of H here reach 1e-3 bit
+    sic = oracle.sic_quantize(layer.w, L, wf["c"])
+    assert_codes_parity(wf["codes"].cpu().numpy(), sic, label=name)
+    assert wf["rate"] == pytest.approx(oracle.entropy_bits(sic["q"]), abs=1e-12)
+
+
+# ------------------------------------------------------------------ entropy
+@pytest.mark.parametrize("case", ["narrow", "wide", "overflow", "single", "ragged"])
+def test_entropy_parity(device, case):
+    rng = np.random.default_rng(5)
+    if case == "narrow":
+        q = np.rint(rng.standard_normal((513, 300)) * 1.3)
+    elif case == "wide":
+        q = np.rint(rng.standard_normal((200, 1000)) * 500.0)
+    elif case == "overflow":
+        q = np.rint(rng.standard_t(2, (300, 301)) * 800.0)
+        q[0, :5] = [2 ** 31 - 1, -(2 ** 31 - 1), 2048, -2048, 2047]
+    elif case == "single":
+        q = np.full((64, 64), -3.0)
+    else:
+        q = np.rint(rng.laplace(0, 3, (7, 5)))
+    q = q.astype(np.int32)
+    say(f"[entropy] {case} {q.shape}, |q|max={np.abs(q.astype(np.int64)).max()}")
+    h, ns = lib.entropy(torch.from_numpy(q).to(device))
+    assert h == pytest.approx(oracle.entropy_bits(q), abs=1e-12)
+    assert ns == len(np.unique(q))
+
+
+# ------------------------------------------------------------------ distortion
+@pytest.mark.parametrize("name", list(LAYERS))
+def test_distortion_parity(device, name):
+    layer = _layer(name)
+    sig = _sigma_oracle(layer)
+    L, U = _oracle_factor_on_device(layer)
+    c = oracle.initial_scale(layer.w, L, 2.0)
+    say(f"[distortion] {name}")
+    Wt = w_tensor(layer)
+    codes, resid = lib.sic_quantize(Wt, U, c, want_resid=True)
+    q = codes.cpu().numpy().astype(np.int64)
+    alpha = oracle.grid_steps(L, c)
+    d_or = oracle.distortion_direct(layer.w, q, alpha, sig)
+    d_res, w_hat = lib.distortion(Wt, codes, U, c, resid=resid, w_hat_dtype=torch.float32)
+    d_dir, _ = lib.distortion(Wt, codes, U, c, mode="direct")
+    say(f"  oracle {d_or:.9e}  resid {d_res:.9e}  direct {d_dir:.9e}")
+    assert d_res == pytest.approx(d_or, rel=1e-5)
+    assert d_dir == pytest.approx(d_or, rel=1e-10)
+    np.testing.assert_allclose(w_hat.cpu().numpy(), (q * alpha[None, :]).astype(np.float32), rtol=1e-6)
+
+
+# ------------------------------------------------------------------ error handling on the device
+def test_nonfinite_weight_is_reported(device):
+    layer = _layer("spiked_300x333")
+    L, U = _oracle_factor_on_device(layer)
+    Wt = w_tensor(layer)
+    Wt[3, 17] = float("nan")
+    with pytest.raises(lib.WsicError) as ei:
+        lib.sic_quantize(Wt, U, 0.1)
+    assert ei.value.status == lib.E_NONFINITE
+
+
+def test_nonfinite_activation_is_reported(device):
+    layer = _layer("spiked_300x333")
+    X = x_tensors(layer)[0]
+    X[5, 2] = float("inf")
+    with pytest.raises(lib.WsicError) as ei:
+        lib.covariance(X)
+    assert ei.value.status == lib.E_NONFINITE
+
+
+def test_code_range_is_reported(device):
+    layer = _layer("spiked_300x333")
+    L, U = _oracle_factor_on_device(layer)
+    with pytest.raises(lib.WsicError) as ei:
+        lib.sic_quantize(w_tensor(layer), U, 1e-15)
+    assert ei.value.status == lib.E_RANGE
+
+
+def test_bad_factor_diagonal_is_reported(device):
+    layer = _layer("spiked_300x333")
+    L, U = _oracle_factor_on_device(layer)
+    U[10, 10] = -1.0
+    with pytest.raises(lib.WsicError) as ei:
+        lib.sic_quantize(w_tensor(layer), U, 0.1)
+    assert ei.value.status == lib.E_INVAL
