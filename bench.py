@@ -43,6 +43,25 @@ FAMILIES = {
 }
 
 
+def measured_traffic(family: str, workload: str):
+    """HBM bytes per launch of `family` from the committed counter summary (rocprofv3
+    FETCH_SIZE + WRITE_SIZE scaled by a plain copy), or None when there is none for this
+    workload or the kernel's source has changed since it was taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))["families"][family]
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (KeyError, OSError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -54,7 +73,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=32)
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run one device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings scale the counters of
+    the other kernels to bytes."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n}), flush=True)
 
 
 def cpu_baseline(layer, target, sample_rows):
@@ -99,6 +134,9 @@ def cpu_baseline(layer, target, sample_rows):
 
 def main():
     args = parse()
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(rows of W would shard across GPUs with U replicated; see the design notes).",
@@ -172,8 +210,12 @@ def main():
             bound, peak_key, scale = FAMILIES[dom]
             peak, unit = PEAKS[peak_key]
             achieved = v["work"] * scale / (v["ms"] * 1e-3)
+            traffic = measured_traffic(dom, args.workload)
             roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-                        "frac": round(achieved / peak, 4), "traffic": None,
+                        "frac": round(achieved / peak, 4),
+                        "traffic": round(traffic) if traffic is not None else None,
+                        "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
+                        "work_per_launch": v["work"] / max(1, v["launches"]),
                         "avg_launch_us": v["avg_us"], "launches": v["launches"],
                         "share_of_step": round(v["ms"] / (elapsed * 1e3), 4)}
 
