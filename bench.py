@@ -29,9 +29,11 @@ PEAKS = {
     "mfma_f64": (78.6, "TFLOP/s"),
     "mfma_f32": (157.3, "TFLOP/s"),
     "mfma_bf16": (2500.0, "TFLOP/s"),
+    "mfma_i8": (5000.0, "TOP/s"),
 }
 # kernel family -> (bound, peak key, work unit scale to the peak's unit)
 FAMILIES = {
+    "gemm_trail_i8": ("mfma", "mfma_i8", 1e-12),
     "gemm_trail": ("mfma", "mfma_f64", 1e-12),
     "gemm_y": ("mfma", "mfma_f64", 1e-12),
     "gemm_chol": ("mfma", "mfma_f64", 1e-12),

@@ -120,10 +120,46 @@ int launch_check_finite(const void* W, int dtype, int64_t n_out, int64_t n_in, i
 int sic_pack_doubles(int64_t n_in);
 int launch_pack_blocks(const double* U, int64_t ldu, int64_t n, const double* invd, double* Bpk,
                        hipStream_t st);
-int launch_sic_leaf(int64_t n_out, int64_t j0, int w, const double* Y, int64_t ldy,
-                    const double* G, int64_t ldg, const double* Bpk, const double* invd, double c,
-                    int32_t* codes, int64_t ldq, float* resid, int64_t ldr, int* flags,
-                    hipStream_t st);
+// Integer form of the interference product: NL int8 digits per B entry (P = 8 NL - 2 bits
+// of fixed point per row), codes clamped to +-127 with the excess of larger codes kept in a
+// per-row list of OCAP entries.
+constexpr int LIMBS = 5;
+constexpr double LIMB_EPS = 1.0 / (double)(1ull << (8 * LIMBS - 2));  // 2^-P
+constexpr int OCAP = 64;
+
+struct LeafArgs {
+  int64_t n_out, n_in, j0;
+  int w;
+  const double* Y;
+  int64_t ldy;
+  const double* G;  // null for the rightmost block
+  int64_t ldg;
+  const double* Bpk;
+  const double* invd;
+  double c, invc;
+  int32_t* codes;
+  int64_t ldq;
+  float* resid;  // nullable
+  int64_t ldr;
+  int* flags;
+  // integer interference mode
+  const double* U;
+  int64_t ldu;
+  const double* bscale;  // 2^e_j
+  double guard_scale;    // multiplies the error bound (1 in normal use)
+  int8_t* q8;
+  int64_t ldq8;
+  double* absq;  // per row: sum |q| over the columns done so far in this pass
+  int* ocnt;     // per row: entries in the excess list
+  int2* olist;   // per row: OCAP (column, q - clamp(q)) pairs
+};
+int launch_sic_leaf(const LeafArgs& p, bool i8, hipStream_t st);
+
+int launch_limb_pack(const double* U, int64_t ldu, int64_t n, const double* invd, double* escale,
+                     double* bscale, int8_t* D, int64_t ldd, hipStream_t st);
+int launch_gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t* A8, int64_t lda, const int8_t* D,
+                   int64_t ldd, int64_t plane, const double* escale, double* C, int64_t ldc,
+                   double beta, hipStream_t st);
 int colstats_doubles(int64_t n_out, int64_t n_in);
 int launch_colstats(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
                     double* part, double* colvar, hipStream_t st);
@@ -136,7 +172,8 @@ struct EntropyResult {
   double sum_nlogn;            // sum over window bins of n log2 n
   unsigned long long nsym;     // non-empty window bins
   unsigned int ovf_count;      // codes outside the window
-  int flags;
+  int flags;                   // flags word of the pass (when given)
+  int aux;                     // its second word: workgroups re-derived in fp64
 };
 int launch_hist(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
                 unsigned long long* bins, int32_t* ovf, unsigned int* ovf_count, hipStream_t st);

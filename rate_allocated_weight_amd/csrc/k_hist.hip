@@ -101,7 +101,8 @@ __global__ __launch_bounds__(256) void k_entropy_reduce(const unsigned long long
     res->sum_nlogn = sd[0];
     res->nsym = sn[0];
     res->ovf_count = *ovf_count;
-    res->flags = flags ? *flags : 0;
+    res->flags = flags ? flags[0] : 0;
+    res->aux = flags ? flags[1] : 0;
   }
 }
 

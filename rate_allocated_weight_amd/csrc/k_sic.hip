@@ -37,40 +37,50 @@ __device__ __forceinline__ double bcast_row(double v) {
   return __hiloint2double(hi, lo);
 }
 
-// Step J of the in-block recursion (J = 127 ... 0), then the remaining ones. Columns past the
-// end of a ragged last block hold z = 0 and all-zero B entries, so their steps change nothing
-// and need no branch.
-template <int J>
-struct Steps {
-  static __device__ __forceinline__ void run(double (&z)[8], const double* __restrict__ bl) {
-    constexpr int a = J >> 4, l = J & 15, off = pack_off(J);
-    const double qb = bcast_row<l>(rint(z[a]));
-#pragma unroll
-    for (int sp = 0; sp <= a; ++sp) z[sp] = fma(-bl[off + 16 * sp], qb, z[sp]);
-    Steps<J - 1>::run(z, bl);
-  }
-};
-template <>
-struct Steps<-1> {
-  static __device__ __forceinline__ void run(double (&)[8], const double*) {}
+// Integer-interference mode: for each of a lane's 8 columns, the bound on the error of the
+// interference it received (int8 limb products: 2^e_j * sum|q| * 2^-P, twice the fixed-point
+// rounding bound, which also covers the fp64 combination) and the interference itself, so that
+// a rounding decision closer to a boundary than the bound can be re-derived exactly.
+struct Guard {
+  float bnd[8];  // the bound, rounded up to float
+  bool hit;      // some decision of this lane fell within its bound
 };
 
-template <bool HAS_G, bool HAS_RESID>
-__global__ __launch_bounds__(256) void k_sic_leaf(int64_t n_out, int64_t j0, int w,
-                                                  const double* __restrict__ Y, int64_t ldy,
-                                                  const double* __restrict__ G, int64_t ldg,
-                                                  const double* __restrict__ Bpk,
-                                                  const double* __restrict__ invd, double c,
-                                                  double invc, int32_t* __restrict__ codes,
-                                                  int64_t ldq, float* __restrict__ resid,
-                                                  int64_t ldr, int* flags) {
+// Step J of the in-block recursion (J = 127 ... 0), then the remaining ones. Columns past the
+// end of a ragged last block hold z = 0 and all-zero B entries, so their steps change nothing
+// and need no branch. With GUARD, the owner of column J records whether its rounding decision
+// is closer to a boundary than the interference error bound.
+template <int J, bool GUARD>
+struct Steps {
+  static __device__ __forceinline__ void run(double (&z)[8], const double* __restrict__ bl,
+                                             Guard& g, int l16) {
+    constexpr int a = J >> 4, l = J & 15, off = pack_off(J);
+    const double qv = rint(z[a]);
+    if (GUARD) g.hit |= (l16 == l) && (0.5 - fabs(z[a] - qv) <= (double)g.bnd[a]);
+    const double qb = bcast_row<l>(qv);
+#pragma unroll
+    for (int sp = 0; sp <= a; ++sp) z[sp] = fma(-bl[off + 16 * sp], qb, z[sp]);
+    Steps<J - 1, GUARD>::run(z, bl, g, l16);
+  }
+};
+template <bool GUARD>
+struct Steps<-1, GUARD> {
+  static __device__ __forceinline__ void run(double (&)[8], const double*, Guard&, int) {}
+};
+
+// I8 = the interference G came from the int8 limb product (k_limb.hip): then the leaf also
+// applies the exact excess of codes beyond +-127 listed by earlier leaves, guards its rounding
+// decisions with the error bound, and emits what the next limb products need: the int8 code
+// plane, the row sums of |q| and its own excess list.
+template <bool HAS_G, bool HAS_RESID, bool I8>
+__global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
   __shared__ __attribute__((aligned(16))) double Bs[PACK];
   const int tid = threadIdx.x;
   {
     // all 18 loads of a thread in flight before its LDS stores
     constexpr int PER = PACK / 2 / 256;
     static_assert(PER * 256 * 2 == PACK, "packed block is a whole number of 16-byte rounds");
-    const uint4* src = reinterpret_cast<const uint4*>(Bpk);
+    const uint4* src = reinterpret_cast<const uint4*>(p.Bpk);
     uint4* dst = reinterpret_cast<uint4*>(Bs);
     uint4 v[PER];
 #pragma unroll
@@ -79,31 +89,83 @@ __global__ __launch_bounds__(256) void k_sic_leaf(int64_t n_out, int64_t j0, int
     for (int e = 0; e < PER; ++e) dst[e * 256 + tid] = v[e];
   }
 
-  const int l16 = tid & 15;
+  const int l16 = tid & 15, lane = tid & 63;
   const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
-  const bool active = row < n_out;
+  const bool active = row < p.n_out;
+  const int64_t j0 = p.j0;
+  const int w = p.w;
 
   double z[8];
+  Guard g;
+  double S = 0.0;  // sum of |q| over the columns right of this block (I8 mode)
+  if (I8 && active) S = p.absq[row];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const int j = l16 + 16 * s;
     double v = 0.0;
     if (active && j < w) {
-      v = Y[row * ldy + j0 + j] * invc;
-      if (HAS_G) v -= G[row * ldg + j0 + j];
+      v = p.Y[row * p.ldy + j0 + j] * p.invc;
+      if (HAS_G) v -= p.G[row * p.ldg + j0 + j];
     }
     z[s] = v;
+    g.bnd[s] = 0.0f;
+  }
+  if (I8 && HAS_G && active) {
+    // exact interference of the excess of large codes to the right (fp64)
+    const int cnt = min(p.ocnt[row], OCAP);
+    for (int o = 0; o < cnt; ++o) {
+      const int2 e = p.olist[row * OCAP + o];
+      const double f = p.invd[e.x] * (double)e.y;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int j = l16 + 16 * s;
+        if (j < w) z[s] -= p.U[(j0 + j) * p.ldu + e.x] * f;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int j = l16 + 16 * s;
+      if (j < w) g.bnd[s] = __double2float_ru(p.bscale[j0 + j] * S * LIMB_EPS * p.guard_scale);
+    }
   }
   __syncthreads();
 
-  Steps<BW - 1>::run(z, Bs + l16);
+  g.hit = false;
+  Steps<BW - 1, I8 && HAS_G>::run(z, Bs + l16, g, l16);
+  if (I8 && HAS_G) {
+    // Rare: a decision inside the error bound. Recompute this workgroup's incoming
+    // interference exactly (fp64, full codes) and redo the block from there.
+    if (__syncthreads_or(g.hit ? 1 : 0)) {
+      const int64_t kbeg = j0 + BW;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) z[s] = 0.0;
+      if (active) {
+        for (int64_t k = kbeg; k < p.n_in; ++k) {
+          const double q = (double)p.codes[row * p.ldq + k] * p.invd[k];
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const int j = l16 + 16 * s;
+            if (j < w) z[s] = fma(p.U[(j0 + j) * p.ldu + k], q, z[s]);
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int j = l16 + 16 * s;
+          z[s] = (j < w) ? p.Y[row * p.ldy + j0 + j] * p.invc - z[s] : 0.0;
+        }
+      }
+      if (lane == 0) atomicAdd(p.flags + 1, 1);  // count of exact re-derivations
+      Steps<BW - 1, false>::run(z, Bs + l16, g, l16);
+    }
+  }
 
-  if (!active) return;
   int bad = 0;
+  double asum = 0.0;
+  int nexc = 0;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const int j = l16 + 16 * s;
-    if (j < w) {
+    if (active && j < w) {
       const double q = rint(z[s]);
       int32_t qi = 0;
       if (q >= -2147483647.0 && q <= 2147483647.0) {
@@ -111,11 +173,55 @@ __global__ __launch_bounds__(256) void k_sic_leaf(int64_t n_out, int64_t j0, int
       } else {
         bad |= (z[s] == z[s]) ? FLAG_RANGE : FLAG_NONFINITE;
       }
-      codes[row * ldq + j0 + j] = qi;
-      if (HAS_RESID) resid[row * ldr + j0 + j] = (float)((z[s] - q) * (c * invd[j0 + j]));
+      p.codes[row * p.ldq + j0 + j] = qi;
+      if (HAS_RESID) p.resid[row * p.ldr + j0 + j] = (float)((z[s] - q) * (p.c * p.invd[j0 + j]));
+      if (I8) {
+        const int q8 = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
+        p.q8[row * p.ldq8 + j0 + j] = (int8_t)q8;
+        asum += fabs(q);
+        nexc += (q8 != qi);
+      }
     }
   }
-  if (bad) atomicOr(flags, bad);
+  if (I8) {
+    // row totals over the 16 lanes; deterministic order of the excess list (lane, then slot)
+    double tot = asum;
+    int ntot = nexc;
+    for (int m = 8; m >= 1; m >>= 1) {
+      tot += __shfl_xor(tot, m, 16);
+      ntot += __shfl_xor(ntot, m, 16);
+    }
+    int pre = nexc;  // inclusive scan of nexc over lanes 0..l16
+    for (int d = 1; d < 16; d <<= 1) {
+      const int t = __shfl_up(pre, d, 16);
+      if (l16 >= d) pre += t;
+    }
+    pre -= nexc;
+    const int base = active ? p.ocnt[row] : 0;
+    if (active && nexc) {
+      int idx = base + pre;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int j = l16 + 16 * s;
+        if (j < w) {
+          const int32_t qi = p.codes[row * p.ldq + j0 + j];
+          const int q8 = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
+          if (q8 != qi) {
+            if (idx < OCAP)
+              p.olist[row * OCAP + idx] = make_int2((int)(j0 + j), qi - q8);
+            else
+              bad |= FLAG_OVERFLOW_LIST;
+            ++idx;
+          }
+        }
+      }
+    }
+    if (active && l16 == 0) {
+      p.absq[row] = S + tot;
+      p.ocnt[row] = base + ntot;
+    }
+  }
+  if (bad) atomicOr(p.flags, bad);
 }
 
 // Packed diagonal blocks of B = U diag(1/U_jj): one block per 128 columns.
@@ -238,32 +344,35 @@ int launch_pack_blocks(const double* U, int64_t ldu, int64_t n, const double* in
   return WSIC_OK;
 }
 
-int launch_sic_leaf(int64_t n_out, int64_t j0, int w, const double* Y, int64_t ldy,
-                    const double* G, int64_t ldg, const double* Bpk, const double* invd, double c,
-                    int32_t* codes, int64_t ldq, float* resid, int64_t ldr, int* flags,
-                    hipStream_t st) {
-  if (w <= 0 || w > BW || j0 % BW != 0) {
-    set_error("internal: leaf at %lld width %d", (long long)j0, w);
+int launch_sic_leaf(const LeafArgs& a, bool i8, hipStream_t st) {
+  if (a.w <= 0 || a.w > BW || a.j0 % BW != 0) {
+    set_error("internal: leaf at %lld width %d", (long long)a.j0, a.w);
     return WSIC_E_INVAL;
   }
-  const double* blk = Bpk + (j0 / BW) * PACK;
-  const unsigned blocks = (unsigned)((n_out + 15) / 16);
-  const double invc = 1.0 / c;
-  // bytes that must stream: Y (+G) in, codes (+resid) out
-  const double work = (double)n_out * w * (8.0 + (G ? 8.0 : 0.0) + 4.0 + (resid ? 4.0 : 0.0));
-#define WSIC_LEAF(HG, HR)                                                                   \
-  WSIC_LAUNCH("sic_leaf", work, st, (k_sic_leaf<HG, HR>), dim3(blocks), dim3(256), 0, n_out, \
-              j0, w, Y, ldy, G, ldg, blk, invd, c, invc, codes, ldq, resid, ldr, flags)
-  if (G) {
-    if (resid)
-      WSIC_LEAF(true, true);
-    else
-      WSIC_LEAF(true, false);
+  if (i8 && (!a.q8 || !a.absq || !a.ocnt || !a.olist || !a.U || !a.bscale)) {
+    set_error("internal: integer-interference leaf without its buffers");
+    return WSIC_E_INVAL;
+  }
+  LeafArgs p = a;
+  p.Bpk = a.Bpk + (a.j0 / BW) * PACK;
+  p.invc = 1.0 / a.c;
+  const unsigned blocks = (unsigned)((a.n_out + 15) / 16);
+  // bytes that must stream: Y (+G) in, codes (+resid, +int8 codes) out
+  const double work = (double)a.n_out * a.w *
+                      (8.0 + (a.G ? 8.0 : 0.0) + 4.0 + (a.resid ? 4.0 : 0.0) + (i8 ? 1.0 : 0.0));
+#define WSIC_LEAF(HG, HR, I8)                                                                      \
+  WSIC_LAUNCH("sic_leaf", work, st, (k_sic_leaf<HG, HR, I8>), dim3(blocks), dim3(256), 0, p)
+  const bool hg = a.G != nullptr, hr = a.resid != nullptr;
+  if (i8) {
+    if (hg && hr) WSIC_LEAF(true, true, true);
+    else if (hg) WSIC_LEAF(true, false, true);
+    else if (hr) WSIC_LEAF(false, true, true);
+    else WSIC_LEAF(false, false, true);
   } else {
-    if (resid)
-      WSIC_LEAF(false, true);
-    else
-      WSIC_LEAF(false, false);
+    if (hg && hr) WSIC_LEAF(true, true, false);
+    else if (hg) WSIC_LEAF(true, false, false);
+    else if (hr) WSIC_LEAF(false, true, false);
+    else WSIC_LEAF(false, false, false);
   }
 #undef WSIC_LEAF
   return WSIC_OK;

@@ -105,12 +105,26 @@ struct Carve {
   }
 };
 
+// int8 operand rows: padded to 64 bytes, padding kept zero
+inline int64_t ld_i8(int64_t n_in) { return (n_in + 63) / 64 * 64; }
+
 struct SicWs {
-  int* flags;
+  int* flags;       // setup checks
   double* invd;
   double* Y;
   double* G;
   double* Bpk;
+  // integer interference product
+  double* escale;   // 2^(e_j - P)
+  double* bscale;   // 2^e_j
+  int8_t* D;        // LIMBS planes n_in x ld_i8
+  int8_t* q8;       // n_out x ld_i8
+  // per-pass state, cleared by one fill: flags word(s), row |q| sums, excess list counts
+  int* pflags;      // [0] flag bits of the pass, [1] exact re-derivations
+  double* absq;
+  int* ocnt;
+  size_t pass_bytes;
+  int2* olist;
 };
 SicWs carve_sic(Carve& cv, int64_t n_out, int64_t n_in) {
   SicWs w;
@@ -119,6 +133,19 @@ SicWs carve_sic(Carve& cv, int64_t n_out, int64_t n_in) {
   w.Y = cv.take<double>((size_t)n_out * n_in);
   w.G = cv.take<double>((size_t)n_out * n_in);
   w.Bpk = cv.take<double>((size_t)sic_pack_doubles(n_in));
+  w.escale = cv.take<double>((size_t)n_in);
+  w.bscale = cv.take<double>((size_t)n_in);
+  w.D = cv.take<int8_t>((size_t)LIMBS * n_in * ld_i8(n_in));
+  w.q8 = cv.take<int8_t>((size_t)n_out * ld_i8(n_in));
+  // contiguous: flags, absq, ocnt (one fill per pass)
+  const size_t off0 = cv.off;
+  w.pflags = cv.take<int>(FLAGS_BYTES / sizeof(int));
+  w.absq = (double*)(cv.base ? cv.base + cv.off : nullptr);
+  cv.off += (size_t)n_out * sizeof(double);
+  w.ocnt = (int*)(cv.base ? cv.base + cv.off : nullptr);
+  cv.off = align_up(cv.off + (size_t)n_out * sizeof(int));
+  w.pass_bytes = cv.off - off0;
+  w.olist = cv.take<int2>((size_t)n_out * OCAP);
   return w;
 }
 
@@ -279,7 +306,20 @@ struct SicCtx {
   int64_t ldu;
   SicWs ws;
   hipStream_t st;
+  bool i8;             // interference by the exact int8 limb product (else fp64 MFMA)
+  double guard_scale;  // multiplies the error bound (testing hook; 1 in normal use)
 };
+
+SicCtx make_ctx(int64_t n_out, int64_t n_in, const void* W, int dtype, int64_t ldw,
+                const double* U, int64_t ldu, const SicWs& ws, hipStream_t st) {
+  SicCtx x{n_out, n_in, W, dtype, ldw, U, ldu, ws, st, true, 1.0};
+  if (const char* e = std::getenv("WSIC_FP64_TRAIL")) x.i8 = (e[0] == '0');
+  if (const char* e = std::getenv("WSIC_GUARD_SCALE")) {
+    const double v = std::atof(e);
+    if (v > 0.0) x.guard_scale = v;
+  }
+  return x;
+}
 
 // invd, Y = W U^T, input checks. Leaves flags on the device (read by the caller).
 int sic_setup(const SicCtx& x) {
@@ -287,6 +327,11 @@ int sic_setup(const SicCtx& x) {
   WSIC_TRY(launch_check_finite(x.W, x.dtype, x.n_out, x.n_in, x.ldw, x.ws.flags, x.st));
   WSIC_TRY(launch_prep(x.U, x.ldu, x.n_in, x.ws.invd, x.ws.flags, x.st));
   WSIC_TRY(launch_pack_blocks(x.U, x.ldu, x.n_in, x.ws.invd, x.ws.Bpk, x.st));
+  if (x.i8) {
+    WSIC_TRY(launch_limb_pack(x.U, x.ldu, x.n_in, x.ws.invd, x.ws.escale, x.ws.bscale, x.ws.D,
+                              ld_i8(x.n_in), x.st));
+    WSIC_TRY(launch_fill_zero(x.ws.q8, (size_t)x.n_out * ld_i8(x.n_in), x.st));
+  }
   GemmArgs g{};
   g.M = x.n_out;
   g.N = x.n_in;
@@ -313,12 +358,45 @@ int sic_range(const SicCtx& x, int64_t lo, int64_t hi, double c, int32_t* codes,
               float* resid, int64_t ldr) {
   const int64_t w = hi - lo;
   const bool has_g = hi < x.n_in;
-  if (w <= BW)
-    return launch_sic_leaf(x.n_out, lo, (int)w, x.ws.Y, x.n_in, has_g ? x.ws.G : nullptr, x.n_in,
-                           x.ws.Bpk, x.ws.invd, c, codes, ldq, resid, ldr, x.ws.flags, x.st);
+  if (w <= BW) {
+    LeafArgs a{};
+    a.n_out = x.n_out;
+    a.n_in = x.n_in;
+    a.j0 = lo;
+    a.w = (int)w;
+    a.Y = x.ws.Y;
+    a.ldy = x.n_in;
+    a.G = has_g ? x.ws.G : nullptr;
+    a.ldg = x.n_in;
+    a.Bpk = x.ws.Bpk;
+    a.invd = x.ws.invd;
+    a.c = c;
+    a.codes = codes;
+    a.ldq = ldq;
+    a.resid = resid;
+    a.ldr = ldr;
+    a.flags = x.ws.pflags;
+    a.U = x.U;
+    a.ldu = x.ldu;
+    a.bscale = x.ws.bscale;
+    a.guard_scale = x.guard_scale;
+    a.q8 = x.ws.q8;
+    a.ldq8 = ld_i8(x.n_in);
+    a.absq = x.ws.absq;
+    a.ocnt = x.ws.ocnt;
+    a.olist = x.ws.olist;
+    return launch_sic_leaf(a, x.i8, x.st);
+  }
   const int64_t nblk = (w + BW - 1) / BW;
   const int64_t mid = lo + BW * ((nblk + 1) / 2);
   WSIC_TRY(sic_range(x, mid, hi, c, codes, ldq, resid, ldr));
+  if (x.i8) {
+    const int64_t ld8 = ld_i8(x.n_in);
+    WSIC_TRY(launch_gemm_i8(x.n_out, mid - lo, hi - mid, x.ws.q8 + mid, ld8, x.ws.D + lo * ld8 + mid,
+                            ld8, x.n_in * ld8, x.ws.escale + lo, x.ws.G + lo, x.n_in,
+                            has_g ? 1.0 : 0.0, x.st));
+    return sic_range(x, lo, mid, c, codes, ldq, resid, ldr);
+  }
   GemmArgs g{};
   g.M = x.n_out;
   g.N = mid - lo;
@@ -337,13 +415,37 @@ int sic_range(const SicCtx& x, int64_t lo, int64_t hi, double c, int32_t* codes,
   return sic_range(x, lo, mid, c, codes, ldq, resid, ldr);
 }
 
-int sic_pass(const SicCtx& x, double c, int32_t* codes, int64_t ldq, float* resid, int64_t ldr) {
+// One pass. With the int8 product, a row whose list of large codes overflows sends the whole
+// pass through the fp64 product instead (the flag is read back with the pass's result).
+int sic_pass_once(const SicCtx& x, double c, int32_t* codes, int64_t ldq, float* resid,
+                  int64_t ldr) {
+  WSIC_TRY(launch_fill_zero(x.ws.pflags, x.ws.pass_bytes, x.st));
   return sic_range(x, 0, x.n_in, c, codes, ldq, resid, ldr);
+}
+
+int sic_pass(const SicCtx& x, double c, int32_t* codes, int64_t ldq, float* resid, int64_t ldr,
+             int* pass_flags) {
+  WSIC_TRY(sic_pass_once(x, c, codes, ldq, resid, ldr));
+  int f[2] = {0, 0};
+  WSIC_HIP_TRY(hipMemcpyAsync(f, x.ws.pflags, sizeof f, hipMemcpyDeviceToHost, x.st));
+  WSIC_HIP_TRY(hipStreamSynchronize(x.st));
+  if (x.i8 && (f[0] & FLAG_OVERFLOW_LIST)) {
+    SicCtx y = x;
+    y.i8 = false;
+    WSIC_TRY(sic_pass_once(y, c, codes, ldq, resid, ldr));
+    WSIC_HIP_TRY(hipMemcpyAsync(f, x.ws.pflags, sizeof f, hipMemcpyDeviceToHost, x.st));
+    WSIC_HIP_TRY(hipStreamSynchronize(x.st));
+  }
+  if (std::getenv("WSIC_TRACE") && f[1])
+    std::fprintf(stderr, "wsic sic pass: %d workgroup(s) re-derived in fp64\n", f[1]);
+  if (pass_flags) *pass_flags = f[0];
+  return flags_status(f[0], "sic pass");
 }
 
 // ============================================================== entropy
 int entropy_of(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq, const HistWs& h,
-               const int* dflags, hipStream_t st, double* H, int64_t* nsym, int* flags_out) {
+               const int* dflags, hipStream_t st, double* H, int64_t* nsym, int* flags_out,
+               int* aux_out = nullptr) {
   WSIC_TRY(launch_fill_zero(h.bins, HIST_CLEAR_BYTES, st));
   WSIC_TRY(launch_hist(codes, n_out, n_in, ldq, h.bins, h.ovf, h.ovf_count, st));
   WSIC_TRY(launch_entropy_reduce(h.bins, h.ovf_count, dflags, h.res, st));
@@ -351,6 +453,7 @@ int entropy_of(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq, c
   WSIC_HIP_TRY(hipMemcpyAsync(&r, h.res, sizeof r, hipMemcpyDeviceToHost, st));
   WSIC_HIP_TRY(hipStreamSynchronize(st));
   if (flags_out) *flags_out = r.flags;
+  if (aux_out) *aux_out = r.aux;
   double s = r.sum_nlogn;
   int64_t ns = (int64_t)r.nsym;
   if (r.ovf_count > 0) {
@@ -500,12 +603,10 @@ int wsic_sic_quantize(const void* W, int dtype, int64_t n_out, int64_t n_in, int
     }
     WSIC_TRY(check_ws(WSIC_OP_SIC, n_out, n_in, ws, ws_bytes));
     Carve cv(ws);
-    SicCtx x{n_out, n_in, W, dtype, ldw, U, ldu, carve_sic(cv, n_out, n_in), (hipStream_t)stream};
+    SicCtx x = make_ctx(n_out, n_in, W, dtype, ldw, U, ldu, carve_sic(cv, n_out, n_in),
+                        (hipStream_t)stream);
     WSIC_TRY(sic_setup(x));
-    WSIC_TRY(sic_pass(x, c, codes, ldq, resid, ldr));
-    int f = 0;
-    WSIC_TRY(read_flags(x.ws.flags, &f, x.st));
-    return flags_status(f, "sic_quantize");
+    return sic_pass(x, c, codes, ldq, resid, ldr, nullptr);
   } catch (...) {
     set_error("sic_quantize: internal exception");
     return WSIC_E_INVAL;
@@ -543,7 +644,7 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
     hipStream_t st = (hipStream_t)stream;
     Carve cv(ws);
     WfWs wf = carve_wf(cv, n_out, n_in);
-    SicCtx x{n_out, n_in, W, dtype, ldw, U, ldu, wf.sic, st};
+    SicCtx x = make_ctx(n_out, n_in, W, dtype, ldw, U, ldu, wf.sic, st);
     WSIC_TRY(sic_setup(x));
 
     const double R = target_bits;
@@ -580,10 +681,19 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
         return WSIC_E_NO_BRACKET;
       }
       ++passes;
-      WSIC_TRY(sic_pass(x, c, cbuf[buf], ldq, rbuf[buf], ldr));
-      int f = 0;
-      WSIC_TRY(entropy_of(cbuf[buf], n_out, n_in, ldq, wf.hist, wf.sic.flags, st, H, nullptr, &f));
-      if (trace) std::fprintf(stderr, "wsic waterfill pass %d: c=%.17g H=%.17g\n", passes, c, *H);
+      WSIC_TRY(sic_pass_once(x, c, cbuf[buf], ldq, rbuf[buf], ldr));
+      int f = 0, nfix = 0;
+      WSIC_TRY(entropy_of(cbuf[buf], n_out, n_in, ldq, wf.hist, x.ws.pflags, st, H, nullptr, &f,
+                          &nfix));
+      if (x.i8 && (f & FLAG_OVERFLOW_LIST)) {  // a row listed too many large codes: fp64 pass
+        SicCtx y = x;
+        y.i8 = false;
+        WSIC_TRY(sic_pass_once(y, c, cbuf[buf], ldq, rbuf[buf], ldr));
+        WSIC_TRY(entropy_of(cbuf[buf], n_out, n_in, ldq, wf.hist, x.ws.pflags, st, H, nullptr, &f));
+      }
+      if (trace)
+        std::fprintf(stderr, "wsic waterfill pass %d: c=%.17g H=%.17g (%d workgroups re-derived)\n",
+                     passes, c, *H, nfix);
       return flags_status(f, "waterfill");
     };
     auto free_buf = [&]() { return hi_buf == 0 ? 1 : 0; };

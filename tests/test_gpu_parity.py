@@ -289,3 +289,37 @@ def test_bad_factor_diagonal_is_reported(device):
     with pytest.raises(lib.WsicError) as ei:
         lib.sic_quantize(w_tensor(layer), U, 0.1)
     assert ei.value.status == lib.E_INVAL
+
+
+# ------------------------------------------------------------------ interference product variants
+@pytest.mark.parametrize("env", [{"WSIC_FP64_TRAIL": "1"}, {"WSIC_GUARD_SCALE": "1e300"}])
+@pytest.mark.parametrize("name", ["spiked_300x333", "blockar1_77x520"])
+def test_sic_parity_product_variants(device, monkeypatch, env, name):
+    """fp64 MFMA interference, and the int8 product with every decision re-derived exactly in
+    fp64 (error bound forced huge): both must give the oracle's codes."""
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    layer = _layer(name)
+    L, U = _oracle_factor_on_device(layer)
+    c = oracle.initial_scale(layer.w, L, 2.5)
+    say(f"[sic-variant] {name} {env}")
+    codes, resid = lib.sic_quantize(w_tensor(layer), U, c, want_resid=True)
+    sic = oracle.sic_quantize(layer.w, L, c)
+    assert_codes_parity(codes.cpu().numpy(), sic, label=f"{name} {env}")
+
+
+@pytest.mark.parametrize("bits", [7.0, 9.0, 12.0])
+def test_sic_parity_large_codes(device, bits):
+    """Codes beyond +-127 (the int8 product keeps their excess in per-row lists) and, at the
+    highest rate, more of them per row than a list holds (the pass falls back to fp64)."""
+    layer = _layer("outliers_130x200")
+    L, U = _oracle_factor_on_device(layer)
+    c = oracle.initial_scale(layer.w, L, bits)
+    codes, _ = lib.sic_quantize(w_tensor(layer), U, c)
+    q = codes.cpu().numpy()
+    big = (np.abs(q) > 127).sum(axis=1)
+    say(f"[sic-large] bits={bits} max|q|={np.abs(q).max()} rows with |q|>127: {(big > 0).sum()}, "
+        f"max per row {big.max()}")
+    sic = oracle.sic_quantize(layer.w, L, c)
+    assert_codes_parity(q, sic, label=f"bits={bits}")
+    assert big.max() > 0
