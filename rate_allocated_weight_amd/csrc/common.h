@@ -104,9 +104,9 @@ int launch_mirror_upper(double* S, int64_t n, int64_t lds, hipStream_t st);
 int launch_diag_check(const double* S, int64_t n, int64_t lds, int* flags, hipStream_t st);
 
 // cholesky
-int launch_potrf_diag(double* A, int64_t lda, int64_t kb, int nbk, int64_t* info, hipStream_t st);
-int launch_trsm_row(double* A, int64_t lda, int64_t kb, int nbk, int64_t n, const int64_t* info,
-                    hipStream_t st);
+// factor the diagonal block at kb and solve the block row to its right, in place
+int launch_potrf_panel(double* A, int64_t lda, int64_t kb, int nbk, int64_t n, int64_t* info,
+                       hipStream_t st);
 int launch_zero_lower(double* A, int64_t n, int64_t lda, hipStream_t st);
 
 // SIC

@@ -2,103 +2,102 @@
 // item 1 factorizes the activation covariance; U here is the transpose of the page's L).
 //
 // Per 64-column step kb (driven from the host):
-//   k_potrf_diag : one workgroup factors the 64 x 64 diagonal block in LDS
-//   k_trsm_row   : the block row to its right, X = U_kk^-T A_k,rest, one thread per column
-//   trailing     : A_rest,rest -= X^T X on upper tiles (fp64 MFMA GEMM, k-major operands)
+//   k_potrf_panel : the block row [kb, kb+64) x [kb, n). Workgroup b > 0 owns a 64-column slab
+//                   of it; every workgroup factors the 64 x 64 diagonal block itself (the same
+//                   instructions on the same data, so every copy of U_kk is bitwise identical)
+//                   and applies each pivot's elimination to its slab as it goes, which is the
+//                   triangular solve X = U_kk^-T A_k,rest. Thread (wave w, lane j) holds rows
+//                   16w .. 16w+15 of column j of the diagonal block and of its slab. At pivot k
+//                   the owning wave publishes row k of both through LDS; every thread reads the
+//                   pivot and the 16 row entries it needs with all loads in flight and scales
+//                   by 1/sqrt(p). Nothing is written to global memory inside the pivot loop.
+//   trailing      : A_rest,rest -= X^T X on upper tiles (fp64 MFMA GEMM, k-major operands)
 // The first failing pivot (1-based, global) is recorded in *info; later steps see it and
-// return immediately, so a failed factorization costs no more launches' worth of work.
+// return immediately.
 #include "common.h"
 
 namespace wsic {
 namespace {
 
 constexpr int NB = 64;
+constexpr int RPW = NB / 4;  // rows per wave
 
-__global__ __launch_bounds__(256) void k_potrf_diag(double* A, int64_t lda, int64_t kb, int nbk,
-                                                    int64_t* info) {
-  __shared__ double a[NB][NB + 1];
-  __shared__ int fail;
-  if (*info != 0) return;
-  const int tid = threadIdx.x;
-  // thread (ty, tx): column tx of the block, rows ty, ty+4, ... (all 16 loads in flight)
-  const int tx = tid & 63, ty = tid >> 6;
-  {
-    double v[NB / 4];
-#pragma unroll
-    for (int s = 0; s < NB / 4; ++s) {
-      const int i = ty + 4 * s;
-      v[s] = (i < nbk && tx < nbk && tx >= i) ? A[(kb + i) * lda + kb + tx] : 0.0;
-    }
-#pragma unroll
-    for (int s = 0; s < NB / 4; ++s) a[ty + 4 * s][tx] = v[s];
-  }
-  (void)fail;
-  for (int k = 0; k < nbk; ++k) {
-    __syncthreads();
-    const double p = a[k][k];  // every thread sees the same pivot: uniform exit
-    if (!(p > 0.0) || !isfinite(p)) {
-      if (tid == 0) *info = kb + k + 1;
-      return;
-    }
-    const double d = sqrt(p);
-    __syncthreads();  // pivot read by all before row k changes
-    if (ty == 0 && tx >= k && tx < nbk) a[k][tx] = (tx == k) ? d : a[k][tx] / d;
-    __syncthreads();
-    if (tx > k && tx < nbk) {
-      // all 32 LDS reads issued before any FMA (rows ty + 4s are in bounds of the tile)
-      const double akj = a[k][tx];
-      double av[NB / 4], ak[NB / 4];
-#pragma unroll
-      for (int s = 0; s < NB / 4; ++s) {
-        av[s] = a[ty + 4 * s][tx];
-        ak[s] = a[k][ty + 4 * s];
-      }
-#pragma unroll
-      for (int s = 0; s < NB / 4; ++s) {
-        const int i = ty + 4 * s;
-        if (i > k && i <= tx) a[i][tx] = fma(-ak[s], akj, av[s]);
-      }
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int s = 0; s < NB / 4; ++s) {
-    const int i = ty + 4 * s;
-    if (i < nbk && tx < nbk) A[(kb + i) * lda + kb + tx] = (tx >= i) ? a[i][tx] : 0.0;
-  }
+// 1/sqrt(p) to ~1 ulp: hardware estimate refined by two Newton steps
+__device__ __forceinline__ double rsqrt_f64(double p) {
+  double y = __builtin_amdgcn_rsq(p);
+  const double h = 0.5 * p;
+  y = y * fma(-h * y, y, 1.5);
+  y = y * fma(-h * y, y, 1.5);
+  return y;
 }
 
-constexpr int TRSM_THREADS = 64;
-
-__global__ __launch_bounds__(TRSM_THREADS) void k_trsm_row(double* A, int64_t lda, int64_t kb,
-                                                           int64_t n, const int64_t* info) {
-  __shared__ __attribute__((aligned(16))) double u[NB][NB];  // U_kk, row-major
+__global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int64_t kb, int nbk,
+                                                     int64_t n, int64_t* info) {
+  __shared__ double row[NB];   // raw row k of the diagonal block
+  __shared__ double srow[NB];  // raw row k of this workgroup's slab
   if (*info != 0) return;
-  const int tid = threadIdx.x;
-  // thread tid fills column tid of U_kk: 64 loads in flight, then the LDS stores
-  {
-    double v[NB];
+  const int j = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  const int64_t c = kb + (int64_t)b * NB + j;  // slab column (b > 0)
+  const bool has_slab = b > 0;
+  const bool cin = has_slab && c < n;
+
+  double a[RPW], sl[RPW];  // rows 16 w + s of column j: diagonal block, slab
 #pragma unroll
-    for (int t = 0; t < NB; ++t) v[t] = (tid >= t) ? A[(kb + t) * lda + kb + tid] : 0.0;
-#pragma unroll
-    for (int t = 0; t < NB; ++t) u[t][tid] = v[t];
-  }
-  __syncthreads();
-  const int64_t c = kb + NB + (int64_t)blockIdx.x * TRSM_THREADS + tid;
-  if (c >= n) return;
-  double x[NB];
-#pragma unroll
-  for (int t = 0; t < NB; ++t) x[t] = A[(kb + t) * lda + c];
-  // U_kk^T x' = x  (U_kk^T lower): forward substitution, column-oriented so that the updates
-  // of different rows are independent (x_s still accumulates its terms in increasing t)
-#pragma unroll
-  for (int t = 0; t < NB; ++t) {
-    x[t] = x[t] / u[t][t];
-#pragma unroll
-    for (int s = t + 1; s < NB; ++s) x[s] = fma(-u[t][s], x[t], x[s]);
+  for (int s = 0; s < RPW; ++s) {
+    const int i = RPW * w + s;
+    a[s] = (i <= j && j < nbk) ? A[(kb + i) * lda + kb + j] : (i == j ? 1.0 : 0.0);
+    sl[s] = (cin && i < nbk) ? A[(kb + i) * lda + c] : 0.0;
   }
 #pragma unroll
-  for (int t = 0; t < NB; ++t) A[(kb + t) * lda + c] = x[t];
+  for (int k = 0; k < NB; ++k) {
+    if (k < nbk) {  // uniform
+      const int wk = k / RPW, sk = k % RPW;
+      if (w == wk) {
+        row[j] = a[sk];
+        srow[j] = sl[sk];
+      }
+      __syncthreads();
+      const double p = row[k];
+      double rr[RPW];
+#pragma unroll
+      for (int s = 0; s < RPW; ++s) rr[s] = row[RPW * w + s];
+      const double rj = row[j];
+      const double xs = srow[j];
+      if (!(p > 0.0) || !isfinite(p)) {  // uniform: every thread sees the same pivot
+        if (b == 0 && threadIdx.x == 0) *info = kb + k + 1;
+        return;
+      }
+      const double inv = rsqrt_f64(p);
+      const double sj = rj * inv;  // U(k, j)
+      const double xk = xs * inv;  // X(k, c)
+      if (w == wk) {
+        a[sk] = (j == k) ? p * inv : sj;
+        sl[sk] = xk;
+      }
+#pragma unroll
+      for (int s = 0; s < RPW; ++s) {
+        const int i = RPW * w + s;
+        if (i > k) {
+          const double uki = rr[s] * inv;  // U(k, i)
+          a[s] = fma(-uki, sj, a[s]);
+          sl[s] = fma(-uki, xk, sl[s]);
+        }
+      }
+      __syncthreads();  // row k read by all before the next pivot overwrites it
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < RPW; ++s) {
+    const int i = RPW * w + s;
+    if (i < nbk) {
+      if (b == 0) {
+        if (j < nbk) A[(kb + i) * lda + kb + j] = (i <= j) ? a[s] : 0.0;
+      } else if (cin) {
+        A[(kb + i) * lda + c] = sl[s];
+      }
+    }
+  }
 }
 
 __global__ void k_zero_lower(double* A, int64_t n, int64_t lda) {
@@ -112,27 +111,17 @@ __global__ void k_zero_lower(double* A, int64_t n, int64_t lda) {
 
 }  // namespace
 
-int launch_potrf_diag(double* A, int64_t lda, int64_t kb, int nbk, int64_t* info, hipStream_t st) {
+int launch_potrf_panel(double* A, int64_t lda, int64_t kb, int nbk, int64_t n, int64_t* info,
+                       hipStream_t st) {
   if (nbk <= 0 || nbk > NB) {
     set_error("internal: potrf block %d", nbk);
     return WSIC_E_INVAL;
   }
-  WSIC_LAUNCH("potrf_diag", (double)nbk * nbk * nbk / 3.0, st, k_potrf_diag, dim3(1), dim3(256), 0,
-              A, lda, kb, nbk, info);
-  return WSIC_OK;
-}
-
-int launch_trsm_row(double* A, int64_t lda, int64_t kb, int nbk, int64_t n, const int64_t* info,
-                    hipStream_t st) {
-  if (nbk != NB) {
-    set_error("internal: trsm block %d", nbk);
-    return WSIC_E_INVAL;
-  }
-  const int64_t m = n - kb - NB;
-  if (m <= 0) return WSIC_OK;
-  WSIC_LAUNCH("trsm_row", (double)NB * NB * m, st, k_trsm_row,
-              dim3((unsigned)((m + TRSM_THREADS - 1) / TRSM_THREADS)), dim3(TRSM_THREADS), 0, A, lda,
-              kb, n, info);
+  const int64_t m = n - kb - nbk;  // columns right of the diagonal block
+  const unsigned blocks = 1 + (unsigned)((m + NB - 1) / NB);
+  const double work = (double)nbk * nbk * nbk / 3.0 + (double)nbk * nbk * m;
+  WSIC_LAUNCH("potrf_panel", work, st, k_potrf_panel, dim3(blocks), dim3(256), 0, A, lda, kb, nbk, n,
+              info);
   return WSIC_OK;
 }
 

@@ -211,6 +211,8 @@ size_t ws_bytes_for(int op, int64_t n_out, int64_t n_in) {
   Carve cv(nullptr);
   switch (op) {
     case WSIC_OP_COVARIANCE:
+      cv.take<int>(FLAGS_BYTES / sizeof(int));
+      break;
     case WSIC_OP_CHOLESKY:
       cv.take<int>(FLAGS_BYTES / sizeof(int));
       break;
@@ -556,10 +558,9 @@ int wsic_cholesky(double* A, int64_t n, int64_t lda, int64_t* info, void* ws, si
     constexpr int NBK = 64;
     for (int64_t kb = 0; kb < n; kb += NBK) {
       const int nbk = (int)std::min<int64_t>(NBK, n - kb);
-      WSIC_TRY(launch_potrf_diag(A, lda, kb, nbk, dinfo, st));
+      WSIC_TRY(launch_potrf_panel(A, lda, kb, nbk, n, dinfo, st));
       const int64_t m = n - kb - nbk;
       if (m <= 0) break;
-      WSIC_TRY(launch_trsm_row(A, lda, kb, nbk, n, dinfo, st));
       GemmArgs g{};
       g.M = m;
       g.N = m;
