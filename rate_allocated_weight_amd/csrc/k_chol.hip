@@ -10,7 +10,9 @@
 //                   16w .. 16w+15 of column j of the diagonal block and of its slab. At pivot k
 //                   the owning wave publishes row k of both through LDS; every thread reads the
 //                   pivot and the 16 row entries it needs with all loads in flight and scales
-//                   by 1/sqrt(p). Nothing is written to global memory inside the pivot loop.
+//                   by 1/sqrt(p). Waves whose rows are all above the pivot skip the update; the
+//                   pivot row buffers alternate with the parity of k, so one barrier per pivot
+//                   suffices. Nothing is written to global memory inside the pivot loop.
 //   trailing      : A_rest,rest -= X^T X on upper tiles (fp64 MFMA GEMM, k-major operands)
 // The first failing pivot (1-based, global) is recorded in *info; later steps see it and
 // return immediately.
@@ -33,8 +35,10 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
 
 __global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int64_t kb, int nbk,
                                                      int64_t n, int64_t* info) {
-  __shared__ double row[NB];   // raw row k of the diagonal block
-  __shared__ double srow[NB];  // raw row k of this workgroup's slab
+  // raw row k of the diagonal block and of this workgroup's slab, double-buffered by the parity
+  // of k so that one barrier per pivot separates its writes from the previous pivot's reads
+  __shared__ double row[2][NB];
+  __shared__ double srow[2][NB];
   if (*info != 0) return;
   const int j = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = blockIdx.x;
@@ -52,18 +56,15 @@ __global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
     if (k < nbk) {  // uniform
-      const int wk = k / RPW, sk = k % RPW;
+      const int wk = k / RPW, sk = k % RPW, pb = k & 1;
       if (w == wk) {
-        row[j] = a[sk];
-        srow[j] = sl[sk];
+        row[pb][j] = a[sk];
+        srow[pb][j] = sl[sk];
       }
       __syncthreads();
-      const double p = row[k];
-      double rr[RPW];
-#pragma unroll
-      for (int s = 0; s < RPW; ++s) rr[s] = row[RPW * w + s];
-      const double rj = row[j];
-      const double xs = srow[j];
+      const double p = row[pb][k];
+      const double rj = row[pb][j];
+      const double xs = srow[pb][j];
       if (!(p > 0.0) || !isfinite(p)) {  // uniform: every thread sees the same pivot
         if (b == 0 && threadIdx.x == 0) *info = kb + k + 1;
         return;
@@ -71,20 +72,29 @@ __global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int
       const double inv = rsqrt_f64(p);
       const double sj = rj * inv;  // U(k, j)
       const double xk = xs * inv;  // X(k, c)
-      if (w == wk) {
-        a[sk] = (j == k) ? p * inv : sj;
-        sl[sk] = xk;
-      }
+      if (w > wk) {
+        // every row of this wave is below the pivot
+        double rr[RPW];
 #pragma unroll
-      for (int s = 0; s < RPW; ++s) {
-        const int i = RPW * w + s;
-        if (i > k) {
+        for (int s = 0; s < RPW; ++s) rr[s] = row[pb][RPW * w + s];
+#pragma unroll
+        for (int s = 0; s < RPW; ++s) {
           const double uki = rr[s] * inv;  // U(k, i)
           a[s] = fma(-uki, sj, a[s]);
           sl[s] = fma(-uki, xk, sl[s]);
         }
+      } else if (w == wk) {
+        // the pivot's own wave: row k is finished, rows below it are updated
+        a[sk] = (j == k) ? p * inv : sj;
+        sl[sk] = xk;
+#pragma unroll
+        for (int s = sk + 1; s < RPW; ++s) {
+          const double uki = row[pb][RPW * wk + s] * inv;
+          a[s] = fma(-uki, sj, a[s]);
+          sl[s] = fma(-uki, xk, sl[s]);
+        }
       }
-      __syncthreads();  // row k read by all before the next pivot overwrites it
+      // waves above the pivot hold finished rows only
     }
   }
 #pragma unroll

@@ -75,11 +75,45 @@ __global__ void k_limb_digits(const double* __restrict__ U, int64_t ldu, int64_t
 }
 
 // C[M x N] (+)= F, F(m, n) = escale[n] * sum_l 256^(NL-1-l) sum_k A8(m,k) D_l(n,k).
+//
 // Tile 128 x 64, K-step 64; 4 waves in 2 x 2, each 64 x 32 = two 32x32 fragments, every
-// fragment with NL int32 accumulators. A8 rows and D rows are 16-byte aligned with zero
-// padding past the layer, so every load is a whole 16-byte vector.
+// fragment with NL int32 accumulators. Operands go from global memory straight into LDS
+// (global_load_lds_dwordx4: each instruction of a wave fills 1 KiB, lane l at byte 16 l) through
+// a ring of STAGES buffers, so STAGES - 1 K-steps are in flight while one is multiplied, and no
+// registers are spent on staging. Each 64-byte LDS row holds four 16-byte chunks; chunk c of
+// row r sits in slot c ^ swz(r), which spreads the 32 rows one MFMA operand read touches over
+// all LDS banks. When beta != 0 the C tile is loaded into registers before the first operand
+// load, so its latency hides behind the whole K loop.
+//
+// Reads are whole 64-byte K-steps: A8 and D must hold zeros in columns [K, roundup(K, 64)).
+// Rows past M or N load a clamped (valid) row whose results are never stored.
 constexpr int TM = 128, TN = 64, TKB = 64;
-constexpr int LROW = TKB + 16;  // LDS row length in bytes (keeps 16-byte alignment)
+constexpr int STAGES = 3;
+constexpr int A_BYTES = TM * TKB;          // 8 KiB
+constexpr int B_BYTES = NL * TN * TKB;     // 20 KiB
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int A_INSTR = A_BYTES / 1024 / 4;  // DMA instructions per wave per stage
+constexpr int B_INSTR = B_BYTES / 1024 / 4;
+constexpr int DMA_PER_STAGE = A_INSTR + B_INSTR;
+static_assert(A_INSTR * 4096 == A_BYTES && B_INSTR * 4096 == B_BYTES, "whole DMA rounds");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+// Workgroup barrier without the memory fence of __syncthreads(): that fence would also wait
+// for every operand load still in flight. LDS traffic of this wave is drained first; the DMA
+// writes a wave depends on are ordered by wait_vm before it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K,
                                                  const int8_t* __restrict__ A8, int64_t lda,
@@ -87,37 +121,58 @@ __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K
                                                  int64_t plane, const double* __restrict__ escale,
                                                  double* __restrict__ C, int64_t ldc, double beta,
                                                  int tiles_n) {
-  __shared__ __attribute__((aligned(16))) int8_t As[TM][LROW];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[NL][TN][LROW];
+  __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * STAGE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   const int64_t m0 = tm * TM, n0 = tn * TN;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // loaders: A 128 rows x 64 bytes = two 16-byte vectors per thread; each D plane 64 rows x
-  // 64 bytes = one vector per thread
-  const int ar = tid >> 1, ac = (tid & 1) * 32;
-  const int br = tid >> 2, bc = (tid & 3) * 16;
-  uint4 pa[2], pb[NL];
-  auto fetch = [&](int64_t k0) {
-    const int64_t m = m0 + ar;
+  // C tile of this lane (result layout of the 32x32 fragments), loaded first when accumulating
+  const int64_t ncol = n0 + wn * 32 + (lane & 31);
+  const bool ncol_ok = ncol < N;
+  double cold[2][16];
+  if (beta != 0.0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      pa[h] = (m < M && k0 + ac + 16 * h < K)
-                  ? *reinterpret_cast<const uint4*>(A8 + m * lda + k0 + ac + 16 * h)
-                  : make_uint4(0, 0, 0, 0);
-    const int64_t nn = n0 + br;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int l = 0; l < NL; ++l)
-      pb[l] = (nn < N && k0 + bc < K)
-                  ? *reinterpret_cast<const uint4*>(D + l * plane + nn * ldd + k0 + bc)
-                  : make_uint4(0, 0, 0, 0);
-  };
-  auto stash = [&]() {
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        cold[i][r] = (m < M && ncol_ok) ? C[m * ldc + ncol] : 0.0;
+      }
+  }
+
+  // DMA sources of this lane: A instruction h of this wave covers rows 16 (A_INSTR w + h) + l/4,
+  // B instruction h covers limb / row (B_INSTR w + h) as 4 instructions per limb plane.
+  const int8_t* asrc[A_INSTR];
+  const int8_t* bsrc[B_INSTR];
+  int aoff[A_INSTR], boff[B_INSTR];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) *reinterpret_cast<uint4*>(&As[ar][ac + 16 * h]) = pa[h];
+  for (int h = 0; h < A_INSTR; ++h) {
+    const int ins = A_INSTR * wave + h;
+    const int r = 16 * ins + (lane >> 2);
+    const int c = (lane & 3) ^ swz(r);
+    const int64_t m = (m0 + r < M) ? m0 + r : M - 1;
+    asrc[h] = A8 + m * lda + 16 * c;
+    aoff[h] = 1024 * ins;
+  }
 #pragma unroll
-    for (int l = 0; l < NL; ++l) *reinterpret_cast<uint4*>(&Bs[l][br][bc]) = pb[l];
+  for (int h = 0; h < B_INSTR; ++h) {
+    const int ins = B_INSTR * wave + h;
+    const int l = ins >> 2, r = 16 * (ins & 3) + (lane >> 2);
+    const int c = (lane & 3) ^ swz(r);
+    const int64_t n = (n0 + r < N) ? n0 + r : N - 1;
+    bsrc[h] = D + l * plane + n * ldd + 16 * c;
+    boff[h] = A_BYTES + 1024 * ins;
+  }
+  auto issue = [&](int64_t kstep, int buf) {
+    int8_t* base = smem + buf * STAGE_BYTES;
+    const int64_t k0 = kstep * TKB;
+#pragma unroll
+    for (int h = 0; h < A_INSTR; ++h)
+      __builtin_amdgcn_global_load_lds((const void*)(asrc[h] + k0), (lds_void*)(base + aoff[h]), 16, 0, 0);
+#pragma unroll
+    for (int h = 0; h < B_INSTR; ++h)
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[h] + k0), (lds_void*)(base + boff[h]), 16, 0, 0);
   };
 
   v16i acc[2][NL];
@@ -126,22 +181,36 @@ __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K
 #pragma unroll
     for (int l = 0; l < NL; ++l) acc[i][l] = (v16i){};
 
-  fetch(0);
-  for (int64_t k0 = 0; k0 < K; k0 += TKB) {
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (k0 + TKB < K) fetch(k0 + TKB);
+  // LDS byte offsets of this lane's operand reads (K half ks adds 32 bytes before swizzling)
+  const int ar0 = wm * 64 + (lane & 31), br0 = wn * 32 + (lane & 31);
+  const int hs = lane >> 5;
+
+  const int nk = (int)((K + TKB - 1) / TKB);
+  static_assert(STAGES == 3, "wait counts below assume three buffers");
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  int cur = 0, nxt = 2;  // buffer of step t, buffer of step t + 2
+  for (int t = 0; t < nk; ++t) {
+    if (t + 1 < nk) wait_vm<DMA_PER_STAGE>();
+    else wait_vm<0>();
+    barrier_lds();  // step t is in LDS for every wave; every wave is done with step t - 1
+    if (t + 2 < nk) issue(t + 2, nxt);
+    const int8_t* As = smem + cur * STAGE_BYTES;
+    cur = (cur == STAGES - 1) ? 0 : cur + 1;
+    nxt = (nxt == STAGES - 1) ? 0 : nxt + 1;
+    const int8_t* Bs = As + A_BYTES;
 #pragma unroll
     for (int ks = 0; ks < TKB / 32; ++ks) {
-      const int kb = ks * 32 + 16 * (lane >> 5);
+      const int c = 2 * ks + hs;
       v4i a[2], b[NL];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const v4i*>(&As[wm * 64 + i * 32 + (lane & 31)][kb]);
+      for (int i = 0; i < 2; ++i) {
+        const int r = ar0 + 32 * i;
+        a[i] = *reinterpret_cast<const v4i*>(As + r * TKB + 16 * (c ^ swz(r)));
+      }
 #pragma unroll
       for (int l = 0; l < NL; ++l)
-        b[l] = *reinterpret_cast<const v4i*>(&Bs[l][wn * 32 + (lane & 31)][kb]);
+        b[l] = *reinterpret_cast<const v4i*>(Bs + l * TN * TKB + br0 * TKB + 16 * (c ^ swz(br0)));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -150,9 +219,8 @@ __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K
     }
   }
 
-  const int64_t n = n0 + wn * 32 + (lane & 31);
-  if (n >= N) return;
-  const double es = escale[n];
+  if (!ncol_ok) return;
+  const double es = escale[ncol];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -163,8 +231,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K
 #pragma unroll
         for (int l = 0; l < NL; ++l) f = fma((double)acc[i][l][r], ldexp(1.0, 8 * (NL - 1 - l)), f);
         f *= es;
-        double* p = C + m * ldc + n;
-        *p = (beta != 0.0) ? fma(beta, *p, f) : f;
+        C[m * ldc + ncol] = (beta != 0.0) ? fma(beta, cold[i][r], f) : f;
       }
     }
 }
@@ -187,6 +254,11 @@ int launch_gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t* A8, int64_t ld
   if (M <= 0 || N <= 0) return WSIC_OK;
   if ((lda % 16) || (ldd % 16) || (((uintptr_t)A8) & 15) || (((uintptr_t)D) & 15)) {
     set_error("internal: int8 operands must be 16-byte aligned");
+    return WSIC_E_INVAL;
+  }
+  // whole 64-column K-steps are read: the caller's buffers must extend (zero) that far
+  if (K % TKB != 0 && (lda < K + (TKB - K % TKB) || ldd < K + (TKB - K % TKB))) {
+    set_error("internal: int8 operands shorter than whole K-steps");
     return WSIC_E_INVAL;
   }
   const int64_t tiles_n = (N + TN - 1) / TN, tiles = ((M + TM - 1) / TM) * tiles_n;

@@ -32,8 +32,8 @@ static_assert(pack_off(BW) == PACK, "packed block size");
 template <int L>
 __device__ __forceinline__ double bcast_row(double v) {
   // row_newbcast:L -- lane L of each 16-lane DPP row to every lane of that row
-  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), 0x150 + L, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), 0x150 + L, 0xf, 0xf, false);
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), 0x150 + L, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), 0x150 + L, 0xf, 0xf, false);
   return __hiloint2double(hi, lo);
 }
 
@@ -43,30 +43,53 @@ __device__ __forceinline__ double bcast_row(double v) {
 // a rounding decision closer to a boundary than the bound can be re-derived exactly.
 struct Guard {
   float bnd[8];  // the bound, rounded up to float
-  bool hit;      // some decision of this lane fell within its bound
 };
 
 // Step J of the in-block recursion (J = 127 ... 0), then the remaining ones. Columns past the
 // end of a ragged last block hold z = 0 and all-zero B entries, so their steps change nothing
-// and need no branch. With GUARD, the owner of column J records whether its rounding decision
-// is closer to a boundary than the interference error bound.
-template <int J, bool GUARD>
+// and need no branch. A column's target is final once its own step has run (later steps only
+// touch columns left of it), so rounding decisions can be checked after the block.
+//
+// The B entries of a step are read from LDS two steps ahead (b0: this step, b1: the next one),
+// and the target the next step rounds is updated first, so the sequential chain per column is
+// round -> broadcast -> one FMA.
+template <int J>
+__device__ __forceinline__ void load_b(double (&b)[8], const double* __restrict__ bl) {
+  if constexpr (J >= 0) {
+    constexpr int a = J >> 4, off = pack_off(J);
+#pragma unroll
+    for (int sp = 0; sp <= a; ++sp) b[sp] = bl[off + 16 * sp];
+  }
+}
+
+template <int J>
 struct Steps {
   static __device__ __forceinline__ void run(double (&z)[8], const double* __restrict__ bl,
-                                             Guard& g, int l16) {
-    constexpr int a = J >> 4, l = J & 15, off = pack_off(J);
-    const double qv = rint(z[a]);
-    if (GUARD) g.hit |= (l16 == l) && (0.5 - fabs(z[a] - qv) <= (double)g.bnd[a]);
-    const double qb = bcast_row<l>(qv);
+                                             const double (&b0)[8], const double (&b1)[8]) {
+    constexpr int a = J >> 4, l = J & 15;
+    constexpr int an = (J - 1) >> 4;  // group of the next step's target (a or a - 1)
+    double b2[8];
+    load_b<J - 2>(b2, bl);
+    const double qb = bcast_row<l>(rint(z[a]));
+    if constexpr (J > 0) z[an] = fma(-b0[an], qb, z[an]);
 #pragma unroll
-    for (int sp = 0; sp <= a; ++sp) z[sp] = fma(-bl[off + 16 * sp], qb, z[sp]);
-    Steps<J - 1, GUARD>::run(z, bl, g, l16);
+    for (int sp = 0; sp <= a; ++sp)
+      if (J == 0 || sp != an) z[sp] = fma(-b0[sp], qb, z[sp]);
+    Steps<J - 1>::run(z, bl, b1, b2);
   }
 };
-template <bool GUARD>
-struct Steps<-1, GUARD> {
-  static __device__ __forceinline__ void run(double (&)[8], const double*, Guard&, int) {}
+template <>
+struct Steps<-1> {
+  static __device__ __forceinline__ void run(double (&)[8], const double*, const double (&)[8],
+                                             const double (&)[8]) {}
 };
+
+__device__ __forceinline__ void run_block(double (&z)[8], const double* __restrict__ bl) {
+  double b0[8], b1[8];
+  load_b<BW - 1>(b0, bl);
+  load_b<BW - 2>(b1, bl);
+  Steps<BW - 1>::run(z, bl, b0, b1);
+}
 
 // I8 = the interference G came from the int8 limb product (k_limb.hip): then the leaf also
 // applies the exact excess of codes beyond +-127 listed by earlier leaves, guards its rounding
@@ -76,8 +99,32 @@ template <bool HAS_G, bool HAS_RESID, bool I8>
 __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
   __shared__ __attribute__((aligned(16))) double Bs[PACK];
   const int tid = threadIdx.x;
+  const int l16 = tid & 15, lane = tid & 63;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
+  const bool active = row < p.n_out;
+  const int64_t j0 = p.j0;
+  const int w = p.w;
+
+  // Every global load of the prologue is issued before the first is used: the per-row and
+  // per-column operands, then the packed B block (all 18 16-byte loads of a thread in flight
+  // before its LDS stores).
+  double S = 0.0;  // sum of |q| over the columns right of this block (I8 mode)
+  int cnt0 = 0;    // entries in this row's excess list so far (I8 mode)
+  if (I8 && active) {
+    S = p.absq[row];
+    cnt0 = p.ocnt[row];
+  }
+  double yv[8], gv[8], bsc[8], dsc[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int j = l16 + 16 * s;
+    const bool in = active && j < w;
+    yv[s] = in ? p.Y[row * p.ldy + j0 + j] : 0.0;
+    gv[s] = (HAS_G && in) ? p.G[row * p.ldg + j0 + j] : 0.0;
+    bsc[s] = (I8 && HAS_G && in) ? p.bscale[j0 + j] : 0.0;
+    dsc[s] = (HAS_RESID && in) ? p.invd[j0 + j] : 0.0;
+  }
   {
-    // all 18 loads of a thread in flight before its LDS stores
     constexpr int PER = PACK / 2 / 256;
     static_assert(PER * 256 * 2 == PACK, "packed block is a whole number of 16-byte rounds");
     const uint4* src = reinterpret_cast<const uint4*>(p.Bpk);
@@ -89,30 +136,16 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
     for (int e = 0; e < PER; ++e) dst[e * 256 + tid] = v[e];
   }
 
-  const int l16 = tid & 15, lane = tid & 63;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
-  const bool active = row < p.n_out;
-  const int64_t j0 = p.j0;
-  const int w = p.w;
-
   double z[8];
   Guard g;
-  double S = 0.0;  // sum of |q| over the columns right of this block (I8 mode)
-  if (I8 && active) S = p.absq[row];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const int j = l16 + 16 * s;
-    double v = 0.0;
-    if (active && j < w) {
-      v = p.Y[row * p.ldy + j0 + j] * p.invc;
-      if (HAS_G) v -= p.G[row * p.ldg + j0 + j];
-    }
-    z[s] = v;
-    g.bnd[s] = 0.0f;
+    z[s] = yv[s] * p.invc - gv[s];
+    g.bnd[s] = (I8 && HAS_G) ? __double2float_ru(bsc[s] * S * LIMB_EPS * p.guard_scale) : 0.0f;
   }
   if (I8 && HAS_G && active) {
     // exact interference of the excess of large codes to the right (fp64)
-    const int cnt = min(p.ocnt[row], OCAP);
+    const int cnt = min(cnt0, OCAP);
     for (int o = 0; o < cnt; ++o) {
       const int2 e = p.olist[row * OCAP + o];
       const double f = p.invd[e.x] * (double)e.y;
@@ -122,20 +155,17 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
         if (j < w) z[s] -= p.U[(j0 + j) * p.ldu + e.x] * f;
       }
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int j = l16 + 16 * s;
-      if (j < w) g.bnd[s] = __double2float_ru(p.bscale[j0 + j] * S * LIMB_EPS * p.guard_scale);
-    }
   }
   __syncthreads();
 
-  g.hit = false;
-  Steps<BW - 1, I8 && HAS_G>::run(z, Bs + l16, g, l16);
+  run_block(z, Bs + l16);
   if (I8 && HAS_G) {
     // Rare: a decision inside the error bound. Recompute this workgroup's incoming
     // interference exactly (fp64, full codes) and redo the block from there.
-    if (__syncthreads_or(g.hit ? 1 : 0)) {
+    bool hit = false;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) hit |= 0.5 - fabs(z[s] - rint(z[s])) <= (double)g.bnd[s];
+    if (__syncthreads_or(hit ? 1 : 0)) {
       const int64_t kbeg = j0 + BW;
 #pragma unroll
       for (int s = 0; s < 8; ++s) z[s] = 0.0;
@@ -155,7 +185,7 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
         }
       }
       if (lane == 0) atomicAdd(p.flags + 1, 1);  // count of exact re-derivations
-      Steps<BW - 1, false>::run(z, Bs + l16, g, l16);
+      run_block(z, Bs + l16);
     }
   }
 
@@ -174,7 +204,7 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
         bad |= (z[s] == z[s]) ? FLAG_RANGE : FLAG_NONFINITE;
       }
       p.codes[row * p.ldq + j0 + j] = qi;
-      if (HAS_RESID) p.resid[row * p.ldr + j0 + j] = (float)((z[s] - q) * (p.c * p.invd[j0 + j]));
+      if (HAS_RESID) p.resid[row * p.ldr + j0 + j] = (float)((z[s] - q) * (p.c * dsc[s]));
       if (I8) {
         const int q8 = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
         p.q8[row * p.ldq8 + j0 + j] = (int8_t)q8;
@@ -197,7 +227,7 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
       if (l16 >= d) pre += t;
     }
     pre -= nexc;
-    const int base = active ? p.ocnt[row] : 0;
+    const int base = cnt0;
     if (active && nexc) {
       int idx = base + pre;
 #pragma unroll
