@@ -10,9 +10,10 @@
 //                   16w .. 16w+15 of column j of the diagonal block and of its slab. At pivot k
 //                   the owning wave publishes row k of both through LDS; every thread reads the
 //                   pivot and the 16 row entries it needs with all loads in flight and scales
-//                   by 1/sqrt(p). Waves whose rows are all above the pivot skip the update; the
-//                   pivot row buffers alternate with the parity of k, so one barrier per pivot
-//                   suffices. Nothing is written to global memory inside the pivot loop.
+//                   by 1/sqrt(p). The update has no branches (rows above the pivot meet a zero
+//                   multiplier); the pivot row buffers alternate with the parity of k, so one
+//                   barrier per pivot suffices. Nothing is written to global memory inside the
+//                   pivot loop.
 //   trailing      : A_rest,rest -= X^T X on upper tiles (fp64 MFMA GEMM, k-major operands)
 // The first failing pivot (1-based, global) is recorded in *info; later steps see it and
 // return immediately.
@@ -40,7 +41,9 @@ __global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int
   __shared__ double row[2][NB];
   __shared__ double srow[2][NB];
   if (*info != 0) return;
-  const int j = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = threadIdx.x & 63;
+  // the wave index, known to the compiler as wave-uniform
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x;
   const int64_t c = kb + (int64_t)b * NB + j;  // slab column (b > 0)
   const bool has_slab = b > 0;
@@ -58,7 +61,9 @@ __global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int
     if (k < nbk) {  // uniform
       const int wk = k / RPW, sk = k % RPW, pb = k & 1;
       if (w == wk) {
-        row[pb][j] = a[sk];
+        // row k of the block is published with zeros left of the diagonal (the lower-triangle
+        // entries a thread holds are scratch, never stored)
+        row[pb][j] = (j >= k) ? a[sk] : 0.0;
         srow[pb][j] = sl[sk];
       }
       __syncthreads();
@@ -72,29 +77,22 @@ __global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int
       const double inv = rsqrt_f64(p);
       const double sj = rj * inv;  // U(k, j)
       const double xk = xs * inv;  // X(k, c)
-      if (w > wk) {
-        // every row of this wave is below the pivot
-        double rr[RPW];
+      // Branch-free elimination: the published row k is zero left of the diagonal, so rows above
+      // the pivot get a zero multiplier and keep their values, and no upper entry is touched by
+      // a column left of the pivot; the pivot row itself is then overwritten with its scaled
+      // entries.
+      double rr[RPW];
 #pragma unroll
-        for (int s = 0; s < RPW; ++s) rr[s] = row[pb][RPW * w + s];
+      for (int s = 0; s < RPW; ++s) rr[s] = row[pb][RPW * w + s];
 #pragma unroll
-        for (int s = 0; s < RPW; ++s) {
-          const double uki = rr[s] * inv;  // U(k, i)
-          a[s] = fma(-uki, sj, a[s]);
-          sl[s] = fma(-uki, xk, sl[s]);
-        }
-      } else if (w == wk) {
-        // the pivot's own wave: row k is finished, rows below it are updated
-        a[sk] = (j == k) ? p * inv : sj;
-        sl[sk] = xk;
-#pragma unroll
-        for (int s = sk + 1; s < RPW; ++s) {
-          const double uki = row[pb][RPW * wk + s] * inv;
-          a[s] = fma(-uki, sj, a[s]);
-          sl[s] = fma(-uki, xk, sl[s]);
-        }
+      for (int s = 0; s < RPW; ++s) {
+        const double uki = rr[s] * inv;  // U(k, i) for i > k
+        a[s] = fma(-uki, sj, a[s]);
+        sl[s] = fma(-uki, xk, sl[s]);
       }
-      // waves above the pivot hold finished rows only
+      const bool own = (w == wk);
+      a[sk] = own ? ((j == k) ? p * inv : sj) : a[sk];
+      sl[sk] = own ? xk : sl[sk];
     }
   }
 #pragma unroll

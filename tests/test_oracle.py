@@ -70,6 +70,18 @@ def test_covariance_chunking_and_orthogonal_rows():
     np.testing.assert_allclose(oracle.covariance([4.0 * q]), np.eye(16), atol=1e-14)
 
 
+def test_covariance_entries_match_the_whole_matrix():
+    rng = np.random.default_rng(11)
+    chunks = [rng.standard_normal((r, 24)).astype(np.float32) for r in (7, 1, 30)]
+    whole = oracle.covariance(chunks)
+    I = rng.integers(0, 24, 50)
+    J = rng.integers(0, 24, 50)
+    np.testing.assert_allclose(oracle.covariance_entries(chunks, I, J), whole[I, J], rtol=1e-13, atol=1e-15)
+    # a single calibration row: x_i x_j exactly
+    x = np.array([[0.5, -2.0, 3.0]], dtype=np.float32)
+    assert oracle.covariance_entries([x], np.array([0, 1, 2]), np.array([2, 1, 0])).tolist() == [1.5, 4.0, 1.5]
+
+
 def test_covariance_matches_population_ar1():
     # AR(1) rows from the workload generator: Sigma_ij -> rho^|i-j| as N grows
     lay = workloads.make_layer("ar1", 4, 24, 200000, dtype="f32", rho=0.9, seed=3)
