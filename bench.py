@@ -7,8 +7,11 @@ Default workload: the attention-projection layer (W 4096 x 4096 bf16, X 8192 x 4
 2 bits per weight). Metric: quantized weights per second (Gparams/s).
 
 Prints one JSON line. `roofline` is taken for the kernel family with the largest share of the
-timed region, from HIP events around its launches on the library's stream; `cpu_baseline` times
-the fp64 oracle on a bounded sample of the same workload.
+step (found in the warm-up), from HIP events around its launches on the library's stream in the
+timed region (no other launch carries events); `phases_ms` splits the step at the call
+boundaries and `value_from_U` is the rate of the part that starts from U in HBM (waterfill +
+entropy + distortion). `cpu_baseline` times the fp64 oracle on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -173,42 +176,81 @@ def main():
     ws_ent = L.workspace(L.OP_ENTROPY, n_out, n_in, dev)
     ws_dist = L.workspace(L.OP_DISTORTION, n_out, n_in, dev)
 
-    def step():
+    # phase boundaries on the library's stream (the current torch stream)
+    phase_names = ("covariance", "cholesky", "waterfill", "entropy+distortion")
+    phase_ms = {k: 0.0 for k in phase_names}
+    phase_events = []
+
+    def step(record=False):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        if record:
+            ev[0].record()
         for i, c in enumerate(X):
             L.covariance(c, sigma, alpha=1.0 / n_rows, beta=0.0 if i == 0 else 1.0, ws=ws_cov)
+        if record:
+            ev[1].record()
         U, _ = L.cholesky(sigma, ws=ws_chol)
+        if record:
+            ev[2].record()
         wf = L.waterfill(W, U, args.target, mode=args.mode, codes=codes, resid=resid, ws=ws_wf)
+        if record:
+            ev[3].record()
         h, _ = L.entropy(codes, ws=ws_ent)
         D, _ = L.distortion(W, codes, U, wf["c"], resid=resid, ws=ws_dist)
+        if record:
+            ev[4].record()
+            phase_events.append(ev)
         return wf, h, D
 
+    # warm-up; with profiling on, it also finds the kernel family with the largest share, the
+    # only one whose launches carry events in the timed region
+    dom = None
+    if not args.no_profile:
+        L.profile_select(None)
+        L.profile_reset()
+        L.profile_enable(True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    def dominant():
+        cand = [(k, L.profile_read(k)["ms"]) for k in L.profile_names() if k in FAMILIES]
+        return max(cand, key=lambda kv: kv[1])[0] if cand else None
+
     if not args.no_profile:
+        L.profile_enable(False)
+        if args.warmup > 0:
+            dom = dominant()
         L.profile_reset()
+        L.profile_select([dom] if dom else None)  # no warm-up: every family is timed
         L.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    results = [step() for _ in range(args.steps)]
+    results = [step(record=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if not args.no_profile:
         L.profile_enable(False)
+        L.profile_select(None)
     elapsed = t1 - t0
     ms_per_step = 1e3 * elapsed / args.steps
     wf, h, D = results[-1]
+    for ev in phase_events:
+        for k, name in enumerate(phase_names):
+            phase_ms[name] += ev[k].elapsed_time(ev[k + 1]) / args.steps
+    ms_from_u = phase_ms["waterfill"] + phase_ms["entropy+distortion"]
 
     kernels = {}
     roofline = None
     if not args.no_profile:
+        if dom is None:
+            dom = dominant()
         for name in L.profile_names():
             p = L.profile_read(name)
             kernels[name] = {"launches": p["launches"], "ms": round(p["ms"], 4),
                              "avg_us": round(1e3 * p["ms"] / max(1, p["launches"]), 3), "work": p["work"]}
-        cand = [(k, v) for k, v in kernels.items() if k in FAMILIES]
-        if cand:
-            dom, v = max(cand, key=lambda kv: kv[1]["ms"])
+        if dom in kernels:
+            v = kernels[dom]
             bound, peak_key, scale = FAMILIES[dom]
             peak, unit = PEAKS[peak_key]
             achieved = v["work"] * scale / (v["ms"] * 1e-3)
@@ -238,6 +280,8 @@ def main():
                    "w_dtype": layer.dtype, "target_bits": args.target, "controller": args.mode,
                    "step": "covariance+cholesky+waterfill+entropy+distortion"},
         "result": {"c": wf["c"], "rate": wf["rate"], "entropy": h, "passes": wf["passes"], "D": D},
+        "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
+        "value_from_U": round(n_out * n_in / (ms_from_u * 1e-3) / 1e9, 6),
         "roofline": roofline,
         "kernels": kernels,
     }

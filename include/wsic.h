@@ -183,9 +183,12 @@ int wsic_distortion(const void* W, int dtype, int64_t n_out, int64_t n_in, int64
  * stream; wsic_profile_read synchronizes and returns, for the kernel family `name`, the
  * launch count, the summed event time in ms and the summed algorithmic work (flops for the
  * MFMA kernels, bytes for the streaming kernels). wsic_profile_names writes a
- * comma-separated list of the families seen into buf. Not thread-safe.
+ * comma-separated list of the families seen into buf. wsic_profile_select restricts the timing
+ * to the families in a comma-separated list (NULL or "" = every family), so that the events
+ * disturb nothing else. Not thread-safe.
  */
 int wsic_profile_enable(int on);
+int wsic_profile_select(const char* families);
 int wsic_profile_reset(void);
 int wsic_profile_read(const char* name, int64_t* launches, double* total_ms, double* total_work);
 int wsic_profile_names(char* buf, size_t buf_bytes);

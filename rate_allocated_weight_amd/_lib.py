@@ -59,6 +59,7 @@ _SIGS = {
                                        ctypes.c_int, ctypes.POINTER(_d), _p, ctypes.c_int, _i64, _p, _sz, _p]),
     "wsic_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "wsic_profile_reset": (ctypes.c_int, []),
+    "wsic_profile_select": (ctypes.c_int, [ctypes.c_char_p]),
     "wsic_profile_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(_i64), ctypes.POINTER(_d),
                                          ctypes.POINTER(_d)]),
     "wsic_profile_names": (ctypes.c_int, [ctypes.c_char_p, _sz]),
@@ -269,6 +270,12 @@ def distortion(W: torch.Tensor, codes: torch.Tensor, U: torch.Tensor, c: float,
 # ------------------------------------------------------------------------------ kernel timing
 def profile_enable(on: bool = True) -> None:
     _check(lib().wsic_profile_enable(1 if on else 0))
+
+
+def profile_select(families: Optional[Sequence[str]] = None) -> None:
+    """Time only these kernel families (None: all)."""
+    arg = None if not families else ",".join(families).encode()
+    _check(lib().wsic_profile_select(arg))
 
 
 def profile_reset() -> None:

@@ -1,6 +1,7 @@
 // Internal declarations shared by the libwsic translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -25,18 +26,25 @@ const char* last_error();
   } while (0)
 
 // ---------------------------------------------------------------- launch timing
-// A launch bracketed by HIP events on its own stream when profiling is on.
+// While timing is on, a launch of a selected family carries a start and a stop event that the
+// dispatch itself timestamps (hipExtLaunchKernelGGL), so the interval is the kernel's own
+// execution, without marker packets around it.
 struct ProfToken {
   int slot;
+  hipEvent_t a, b;
 };
-ProfToken prof_begin(const char* family, hipStream_t st);
-void prof_end(ProfToken t, hipStream_t st, double work);
+ProfToken prof_begin(const char* family);
+void prof_end(ProfToken t, double work);
 
 #define WSIC_LAUNCH(family, work, stream, kernel, grid, block, shmem, ...)      \
   do {                                                                          \
-    ::wsic::ProfToken _tok = ::wsic::prof_begin(family, stream);                \
-    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);        \
-    ::wsic::prof_end(_tok, stream, (double)(work));                             \
+    ::wsic::ProfToken _tok = ::wsic::prof_begin(family);                        \
+    if (_tok.slot >= 0)                                                         \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, _tok.a, _tok.b, \
+                            0, __VA_ARGS__);                                    \
+    else                                                                        \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);      \
+    ::wsic::prof_end(_tok, (double)(work));                                     \
     hipError_t _le = hipGetLastError();                                         \
     if (_le != hipSuccess) {                                                    \
       ::wsic::set_error("launch of %s failed: %s", #kernel,                     \

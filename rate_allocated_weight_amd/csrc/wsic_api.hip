@@ -39,6 +39,7 @@ struct ProfAcc {
   double ms = 0.0, work = 0.0;
 };
 bool g_prof = false;
+std::vector<std::string> g_prof_only;  // families to time; empty = all
 std::vector<PendingEvent> g_pending;
 std::map<std::string, ProfAcc> g_acc;
 std::vector<hipEvent_t> g_event_pool;
@@ -72,19 +73,22 @@ int prof_collect() {
 }
 }  // namespace
 
-ProfToken prof_begin(const char* family, hipStream_t st) {
-  if (!g_prof) return ProfToken{-1};
+ProfToken prof_begin(const char* family) {
+  if (!g_prof) return ProfToken{-1, nullptr, nullptr};
+  if (!g_prof_only.empty()) {
+    bool sel = false;
+    for (const auto& f : g_prof_only) sel = sel || f == family;
+    if (!sel) return ProfToken{-1, nullptr, nullptr};
+  }
   PendingEvent p{family, pool_event(), pool_event(), 0.0};
-  if (p.a) (void)hipEventRecord(p.a, st);
+  if (!p.a || !p.b) return ProfToken{-1, nullptr, nullptr};
   g_pending.push_back(p);
-  return ProfToken{(int)g_pending.size() - 1};
+  return ProfToken{(int)g_pending.size() - 1, p.a, p.b};
 }
 
-void prof_end(ProfToken t, hipStream_t st, double work) {
+void prof_end(ProfToken t, double work) {
   if (t.slot < 0 || t.slot >= (int)g_pending.size()) return;
-  PendingEvent& p = g_pending[t.slot];
-  if (p.b) (void)hipEventRecord(p.b, st);
-  p.work = work;
+  g_pending[t.slot].work = work;
 }
 
 // ============================================================== workspace layouts
@@ -918,6 +922,22 @@ int wsic_distortion(const void* W, int dtype, int64_t n_out, int64_t n_in, int64
 
 int wsic_profile_enable(int on) {
   g_prof = on != 0;
+  return WSIC_OK;
+}
+
+int wsic_profile_select(const char* families) {
+  g_prof_only.clear();
+  if (!families) return WSIC_OK;
+  std::string cur;
+  for (const char* p = families;; ++p) {
+    if (*p == ',' || *p == 0) {
+      if (!cur.empty()) g_prof_only.push_back(cur);
+      cur.clear();
+      if (*p == 0) break;
+    } else {
+      cur += *p;
+    }
+  }
   return WSIC_OK;
 }
 
