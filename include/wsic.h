@@ -109,7 +109,8 @@ int wsic_cholesky(double* A, int64_t n, int64_t lda, int64_t* info,
  * One SIC pass at grid scale c [WaterSIC §2 items 1-2]: steps Delta_j = c / U_jj, columns
  * visited j = n_in-1 ... 0, each rounded (ties to even) after cancelling the interference of
  * the columns already quantized. Computed in fp64.
- * W: n_out x n_in (dtype), ldw >= n_in. U: upper factor from wsic_cholesky, ldu >= n_in.
+ * W: n_out x n_in (dtype), ldw >= n_in. U: upper factor from wsic_cholesky, ldu >= n_in; its
+ * strict lower triangle is never read (here and in wsic_waterfill / wsic_distortion).
  * codes (out): n_out x n_in int32, ldq >= n_in.
  * resid (out, nullable): n_out x n_in float, ldr >= n_in, r_j = t_j - Delta_j q_j in the
  * units of W (|r_j| <= Delta_j / 2); sum_j U_jj^2 ||r_:,j||^2 is the layer distortion.

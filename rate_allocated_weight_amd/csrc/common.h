@@ -105,6 +105,11 @@ int gemm_tiles(const GemmArgs& g);  // number of tiles (size of `partial`)
 int launch_gemm(int amode, int epi, const GemmArgs& g, const char* family, double work,
                 hipStream_t st);
 
+// Y = W U^T (setup of the SIC): W (dtype) M x K row-major, U fp64 with U[n][k] = 0 for k < n
+// (the strict lower triangle is never read)
+int launch_gemm_y(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                  const double* B, int64_t ldb, double* C, int64_t ldc, double work, hipStream_t st);
+
 // covariance
 int launch_syrk(const void* X, int dtype, int64_t rows, int64_t n, int64_t ldx, double alpha,
                 double beta, double* S, int64_t lds, hipStream_t st);

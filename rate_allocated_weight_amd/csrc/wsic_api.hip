@@ -338,21 +338,9 @@ int sic_setup(const SicCtx& x) {
                               ld_i8(x.n_in), x.st));
     WSIC_TRY(launch_fill_zero(x.ws.q8, (size_t)x.n_out * ld_i8(x.n_in), x.st));
   }
-  GemmArgs g{};
-  g.M = x.n_out;
-  g.N = x.n_in;
-  g.K = x.n_in;
-  g.A = x.W;
-  g.lda = x.ldw;
-  g.B = x.U;
-  g.ldb = x.ldu;
-  g.C = x.ws.Y;
-  g.ldc = x.n_in;
-  g.alpha = 1.0;
-  g.beta = 0.0;
-  g.tri = 1;
   const double work = (double)x.n_out * (double)x.n_in * (double)(x.n_in + 1);
-  WSIC_TRY(launch_gemm(x.dtype == WSIC_BF16 ? A_BF16 : A_F32, EPI_STORE, g, "gemm_y", work, x.st));
+  WSIC_TRY(launch_gemm_y(x.dtype, x.n_out, x.n_in, x.n_in, x.W, x.ldw, x.U, x.ldu, x.ws.Y, x.n_in,
+                         work, x.st));
   int f = 0;
   WSIC_TRY(read_flags(x.ws.flags, &f, x.st));
   return flags_status(f, "sic");

@@ -20,6 +20,8 @@ LAYERS = {
     "blockar1_77x520": ("blockar1", 77, 520, 1100, dict(dtype="bf16", block=96, chunk_rows=400)),
     "outliers_130x200": ("ar1", 130, 200, 600, dict(dtype="bf16", rho=0.95, scale_sigma=0.5,
                                                    outlier_cols=3)),
+    # n_in a multiple of 16 but not of 128, n_out ragged: the pipelined Y product with partial tiles
+    "spiked_200x272": ("spiked", 200, 272, 700, dict(dtype="bf16", rank=16)),
 }
 
 
@@ -153,6 +155,28 @@ def test_sic_strided_inputs(device):
     sic = oracle.sic_quantize(layer.w, L, c)
     assert_codes_parity(codes_big[:, :n_in].cpu().numpy(), sic, label="strided")
     assert torch.all(codes_big[:, n_in:] == -99)
+
+
+@pytest.mark.parametrize("name", ["spiked_200x272", "blockar1_77x520"])
+def test_u_lower_triangle_is_not_read(device, name):
+    """U's strict lower triangle may hold anything: codes, residuals, the search and both
+    distortion modes are unchanged when it is NaN."""
+    layer = _layer(name)
+    L, U = _oracle_factor_on_device(layer)
+    Wt = w_tensor(layer)
+    c = oracle.initial_scale(layer.w, L, 2.0)
+    Un = U.clone()
+    Un[torch.tril(torch.ones_like(Un, dtype=torch.bool), -1)] = float("nan")
+    q0, r0 = lib.sic_quantize(Wt, U, c, want_resid=True)
+    q1, r1 = lib.sic_quantize(Wt, Un, c, want_resid=True)
+    assert torch.equal(q0, q1) and torch.equal(r0, r1)
+    wf0 = lib.waterfill(Wt, U, 2.0)
+    wf1 = lib.waterfill(Wt, Un, 2.0)
+    assert wf0["c"] == wf1["c"] and torch.equal(wf0["codes"], wf1["codes"])
+    for mode in ("resid", "direct"):
+        D0, _ = lib.distortion(Wt, q0, U, c, resid=r0 if mode == "resid" else None, mode=mode)
+        D1, _ = lib.distortion(Wt, q0, Un, c, resid=r0 if mode == "resid" else None, mode=mode)
+        assert D0 == D1 and math.isfinite(D1)
 
 
 # ------------------------------------------------------------------ controller
