@@ -56,10 +56,15 @@ __global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int
     a[s] = (i <= j && j < nbk) ? A[(kb + i) * lda + kb + j] : (i == j ? 1.0 : 0.0);
     sl[s] = (cin && i < nbk) ? A[(kb + i) * lda + c] : 0.0;
   }
+  // pivots in four groups of RPW: the group loop stays a loop (code size: the instruction cache
+  // holds one group), the RPW pivots of a group are unrolled so register indices are constants
+#pragma unroll 1
+  for (int wk = 0; wk < NB / RPW; ++wk) {
 #pragma unroll
-  for (int k = 0; k < NB; ++k) {
+  for (int sk = 0; sk < RPW; ++sk) {
+    const int k = RPW * wk + sk;
     if (k < nbk) {  // uniform
-      const int wk = k / RPW, sk = k % RPW, pb = k & 1;
+      const int pb = sk & 1;
       if (w == wk) {
         // row k of the block is published with zeros left of the diagonal (the lower-triangle
         // entries a thread holds are scratch, never stored)
@@ -95,6 +100,7 @@ __global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int
       sl[sk] = own ? xk : sl[sk];
     }
   }
+  }
 #pragma unroll
   for (int s = 0; s < RPW; ++s) {
     const int i = RPW * w + s;
@@ -106,6 +112,107 @@ __global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int
       }
     }
   }
+}
+
+// Trailing update A22 -= X^T X after a block row: X = rows r0 .. r0+KR-1 of A at columns
+// c0 .. c0+m-1 (the solved block row), A22 = A[c0.., c0..] (m x m), upper tiles only.
+// One 256-thread workgroup per 64 x 64 upper tile (tiles enumerated triangularly): the C tile is
+// loaded into registers first, then the KR x 64 column strips of X for the tile's rows and
+// columns go global -> LDS directly (global_load_lds_dwordx4, lane l of an instruction at byte
+// 16 l) in their natural layout, [k][col], which is already the conflict-free layout of the
+// v_mfma_f64_16x16x4 operands (16 lanes read 16 consecutive doubles of one k row). Diagonal
+// tiles load one strip. 4 waves in 2 x 2, each 32 x 32 = 2 x 2 fragments.
+// Requirements (checked by the launcher): A 16-byte aligned, lda even, c0 even.
+namespace cupd {
+constexpr int T = 64;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef double d4 __attribute__((ext_vector_type(4)));
+}  // namespace cupd
+
+template <int KR>
+__global__ __launch_bounds__(256) void k_chol_update(double* A, int64_t lda, int64_t r0, int64_t c0,
+                                                     int64_t m, const int64_t* info) {
+  using namespace cupd;
+  __shared__ __attribute__((aligned(1024))) double Xs[2][KR][T];
+  if (*info != 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // triangular tile index: bid -> (tm <= tn)
+  const int64_t bid = blockIdx.x;
+  int64_t tn = (int64_t)((sqrt(8.0 * (double)bid + 1.0) - 1.0) * 0.5);
+  while ((tn + 1) * (tn + 2) / 2 <= bid) ++tn;
+  while (tn * (tn + 1) / 2 > bid) --tn;
+  const int64_t tm = bid - tn * (tn + 1) / 2;
+  const int64_t i0 = tm * T, j0 = tn * T;
+  const bool diag = (tm == tn);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, lk = lane >> 4;
+
+  // C tile of this lane (result layout), loaded first
+  double cold[2][2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t ii = i0 + wm * 32 + i * 16 + lk + 4 * r;
+        const int64_t jj = j0 + wn * 32 + j * 16 + lr;
+        cold[i][j][r] = (ii < m && jj < m) ? A[(c0 + ii) * lda + c0 + jj] : 0.0;
+      }
+
+  // strips: KR rows x 64 columns = KR * 32 chunks of 16 bytes, KR / 2 instructions per strip
+  constexpr int INS = KR / 2 / 4;  // per wave per strip
+  const int64_t clast = (m - 1) & ~(int64_t)1;  // last chunk start inside the row
+#pragma unroll
+  for (int sidx = 0; sidx < 2; ++sidx) {
+    if (sidx == 1 && diag) break;  // uniform
+    const int64_t col0 = (sidx == 0) ? i0 : j0;
+#pragma unroll
+    for (int h = 0; h < INS; ++h) {
+      const int ins = INS * wave + h;
+      const int p = 64 * ins + lane;
+      const int t = p >> 5, ch = p & 31;
+      int64_t cc = col0 + 2 * ch;
+      cc = cc < clast ? cc : clast;
+      __builtin_amdgcn_global_load_lds((const void*)(A + (r0 + t) * lda + c0 + cc),
+                                       (lds_void*)(&Xs[sidx][0][0] + 128 * ins), 16, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const double(*Xa)[T] = Xs[0];
+  const double(*Xb)[T] = diag ? Xs[0] : Xs[1];
+  d4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (d4){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int k4 = 0; k4 < KR / 4; ++k4) {
+    const int k = 4 * k4 + lk;
+    double a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = Xa[k][wm * 32 + i * 16 + lr];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = Xb[k][wn * 32 + j * 16 + lr];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t ii = i0 + wm * 32 + i * 16 + lk + 4 * r;
+        const int64_t jj = j0 + wn * 32 + j * 16 + lr;
+        if (ii < m && jj < m) A[(c0 + ii) * lda + c0 + jj] = cold[i][j][r] - acc[i][j][r];
+      }
 }
 
 __global__ void k_zero_lower(double* A, int64_t n, int64_t lda) {
@@ -130,6 +237,25 @@ int launch_potrf_panel(double* A, int64_t lda, int64_t kb, int nbk, int64_t n, i
   const double work = (double)nbk * nbk * nbk / 3.0 + (double)nbk * nbk * m;
   WSIC_LAUNCH("potrf_panel", work, st, k_potrf_panel, dim3(blocks), dim3(256), 0, A, lda, kb, nbk, n,
               info);
+  return WSIC_OK;
+}
+
+bool chol_update_ok(const double* A, int64_t lda, int64_t c0, int kr) {
+  return kr == NB && (((uintptr_t)A) & 15) == 0 && (lda % 2) == 0 && (c0 % 2) == 0;
+}
+
+int launch_chol_update(double* A, int64_t lda, int64_t r0, int64_t c0, int64_t m, int kr,
+                       const int64_t* info, hipStream_t st) {
+  if (m <= 0) return WSIC_OK;
+  if (!chol_update_ok(A, lda, c0, kr)) {
+    set_error("internal: chol update preconditions");
+    return WSIC_E_INVAL;
+  }
+  const int64_t t = (m + cupd::T - 1) / cupd::T;
+  const int64_t tiles = t * (t + 1) / 2;
+  const double work = (double)m * (double)(m + 1) * (double)kr;
+  WSIC_LAUNCH("chol_update", work, st, k_chol_update<NB>, dim3((unsigned)tiles), dim3(256), 0, A,
+              lda, r0, c0, m, info);
   return WSIC_OK;
 }
 

@@ -553,6 +553,10 @@ int wsic_cholesky(double* A, int64_t n, int64_t lda, int64_t* info, void* ws, si
       WSIC_TRY(launch_potrf_panel(A, lda, kb, nbk, n, dinfo, st));
       const int64_t m = n - kb - nbk;
       if (m <= 0) break;
+      if (nbk == NBK && chol_update_ok(A, lda, kb + nbk, nbk)) {
+        WSIC_TRY(launch_chol_update(A, lda, kb, kb + nbk, m, nbk, dinfo, st));
+        continue;
+      }
       GemmArgs g{};
       g.M = m;
       g.N = m;
