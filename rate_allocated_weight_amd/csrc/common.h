@@ -192,6 +192,7 @@ struct EntropyResult {
   unsigned int ovf_count;      // codes outside the window
   int flags;                   // flags word of the pass (when given)
   int aux;                     // its second word: workgroups re-derived in fp64
+  int aux2;                    // its third word: decisions re-checked one by one
 };
 int launch_hist(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
                 unsigned long long* bins, int32_t* ovf, unsigned int* ovf_count, hipStream_t st);

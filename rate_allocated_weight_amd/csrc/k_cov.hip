@@ -126,6 +126,177 @@ __global__ __launch_bounds__(256) void k_syrk_bf16(const uint16_t* __restrict__ 
   }
 }
 
+// bf16 X, pipelined: Sigma tile 128 x 128 per 256-thread workgroup (upper tiles only, enumerated
+// triangularly); 4 waves in 2 x 2, each 64 x 64 = 2 x 2 fragments of v_mfma_f32_32x32x16_bf16.
+// Per K-step of 32 calibration rows the two 32 x 128 row strips of X (the tile's rows and its
+// columns of Sigma) go global -> LDS directly (global_load_lds_dwordx4) through a ring of 3
+// buffers, in X's own row-major layout with the 16-byte chunks of row r XOR-swizzled by 2 (r & 3).
+// The MFMA wants 8 consecutive rows of X per lane; ds_read_b64_tr_b16 delivers them: within each
+// 16-lane group, lane i receives element i % 4 of the 8-byte rows addressed by lanes 4v + i / 4
+// (v = 0..3, checked on gfx950), so lanes pointing at [k0 + j/4][c0 + 4 (j%4)] hand lane i the
+// values X[k0 .. k0+3][c0 + i]. fp32 sums over 256 rows are folded into fp64 accumulators.
+// Rows and columns past the matrix read a zero chunk. Requirements (checked by the launcher):
+// n % 8 == 0, ldx % 8 == 0, X 16-byte aligned.
+namespace sdma {
+constexpr int T = 128, TKR = 32, STAGES = 3, FOLD_STEPS = 256 / TKR;
+constexpr int STRIP = TKR * T * 2;  // 8 KiB
+constexpr int STAGE = 2 * STRIP;
+constexpr int INS = STRIP / 4096;   // DMA instructions per wave per strip
+constexpr int DMA = 2 * INS;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// byte offset of bf16 column c of row r inside a strip
+__device__ __forceinline__ int strip_off(int r, int c) {
+  return r * (T * 2) + (((c >> 3) ^ (2 * (r & 3))) << 4) + ((c & 7) << 1);
+}
+}  // namespace sdma
+
+__device__ __align__(16) uint4 g_zero16 = {0u, 0u, 0u, 0u};
+
+__global__ __launch_bounds__(256) void k_syrk_bf16_dma(const uint16_t* __restrict__ X, int64_t rows,
+                                                       int64_t n, int64_t ldx, double alpha,
+                                                       double beta, double* __restrict__ S,
+                                                       int64_t lds) {
+  constexpr int T = sdma::T, TKR = sdma::TKR, STAGES = sdma::STAGES, FOLD_STEPS = sdma::FOLD_STEPS;
+  constexpr int STRIP = sdma::STRIP, STAGE = sdma::STAGE, INS = sdma::INS, DMA = sdma::DMA;
+  using sdma::lds_void;
+  using sdma::lds_v4s;
+  using sdma::v4s;
+  using sdma::strip_off;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t bid = blockIdx.x;
+  int64_t tn = (int64_t)((sqrt(8.0 * (double)bid + 1.0) - 1.0) * 0.5);
+  while ((tn + 1) * (tn + 2) / 2 <= bid) ++tn;
+  while (tn * (tn + 1) / 2 > bid) --tn;
+  const int64_t tm = bid - tn * (tn + 1) / 2;
+  const int64_t i0 = tm * T, j0 = tn * T;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // this lane's DMA chunks: strip s, instruction h -> row r, global chunk column col
+  int drow[2][INS];
+  int64_t dcol[2][INS];
+  bool dcol_ok[2][INS];
+#pragma unroll
+  for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+    for (int h = 0; h < INS; ++h) {
+      const int p = 64 * (INS * wave + h) + lane;
+      const int r = p >> 4, slot = p & 15;
+      const int c = slot ^ (2 * (r & 3));
+      drow[sidx][h] = r;
+      dcol[sidx][h] = (sidx == 0 ? i0 : j0) + 8 * c;
+      dcol_ok[sidx][h] = dcol[sidx][h] < n;
+    }
+  auto issue = [&](int64_t k0, int buf) {
+    char* base = smem + buf * STAGE;
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+      for (int h = 0; h < INS; ++h) {
+        const int64_t r = k0 + drow[sidx][h];
+        const void* src = (r < rows && dcol_ok[sidx][h])
+                              ? (const void*)(X + r * ldx + dcol[sidx][h])
+                              : (const void*)&g_zero16;
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + sidx * STRIP + 1024 * (INS * wave + h)),
+                                         16, 0, 0);
+      }
+  };
+
+  f16v acc32[2][2];
+  double acc64[2][2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      acc32[i][j] = (f16v){};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc64[i][j][r] = 0.0;
+    }
+
+  // operand read coordinates of this lane (16-lane group g, lane j in the group)
+  const int g = lane >> 4, jl = lane & 15;
+  const int m_off = 16 * (g & 1), k_off = 8 * (g >> 1);
+  const int rsub = jl >> 2, csub = 4 * (jl & 3);
+
+  const int nk = (int)((rows + TKR - 1) / TKR);
+  if (nk > 0) issue(0, 0);
+  if (nk > 1) issue(TKR, 1);
+  int cur = 0, nxt = 2;
+  for (int t = 0; t < nk; ++t) {
+    if (t + 1 < nk) sdma::wait_vm<DMA>();
+    else sdma::wait_vm<0>();
+    sdma::barrier_lds();
+    if (t + 2 < nk) issue((int64_t)(t + 2) * TKR, nxt);
+    const char* As = smem + cur * STAGE;
+    const char* Bs = As + STRIP;
+    cur = (cur == STAGES - 1) ? 0 : cur + 1;
+    nxt = (nxt == STAGES - 1) ? 0 : nxt + 1;
+#pragma unroll
+    for (int ks = 0; ks < TKR / 16; ++ks) {
+      bf8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int cbase = wm * 64 + i * 32 + m_off + csub;
+        v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4s*)(As + strip_off(ks * 16 + k_off + rsub, cbase)));
+        v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4s*)(As + strip_off(ks * 16 + k_off + 4 + rsub, cbase)));
+        short e8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        __builtin_memcpy(&a[i], e8, 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int cbase = wn * 64 + j * 32 + m_off + csub;
+        v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4s*)(Bs + strip_off(ks * 16 + k_off + rsub, cbase)));
+        v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4s*)(Bs + strip_off(ks * 16 + k_off + 4 + rsub, cbase)));
+        short e8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        __builtin_memcpy(&b[j], e8, 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc32[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc32[i][j], 0, 0, 0);
+    }
+    if ((t + 1) % FOLD_STEPS == 0 || t + 1 == nk) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc64[i][j][r] += (double)acc32[i][j][r];
+          acc32[i][j] = (f16v){};
+        }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t ii = i0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t jj = j0 + wn * 64 + j * 32 + (lane & 31);
+        if (ii < n && jj < n && jj >= ii) {
+          double* p = S + ii * lds + jj;
+          *p = (beta != 0.0) ? fma(alpha, acc64[i][j][r], beta * *p) : alpha * acc64[i][j][r];
+        }
+      }
+}
+
 __global__ __launch_bounds__(256) void k_syrk_f32(const float* __restrict__ X, int64_t rows,
                                                   int64_t n, int64_t ldx, double alpha, double beta,
                                                   double* __restrict__ S, int64_t lds, int tiles) {
@@ -205,7 +376,12 @@ int launch_syrk(const void* X, int dtype, int64_t rows, int64_t n, int64_t ldx, 
   const int tiles = (int)((n + T - 1) / T);
   const unsigned grid = (unsigned)((int64_t)tiles * tiles);
   const double work = (double)rows * (double)n * (double)(n + 1);  // flops of the upper triangle
-  if (dtype == WSIC_BF16)
+  const bool dma_ok = n % 8 == 0 && ldx % 8 == 0 && (((uintptr_t)X) & 15) == 0;
+  if (dtype == WSIC_BF16 && dma_ok) {
+    const int64_t t = (n + sdma::T - 1) / sdma::T;
+    WSIC_LAUNCH("syrk_bf16", work, st, k_syrk_bf16_dma, dim3((unsigned)(t * (t + 1) / 2)), dim3(256),
+                0, (const uint16_t*)X, rows, n, ldx, alpha, beta, S, lds);
+  } else if (dtype == WSIC_BF16)
     WSIC_LAUNCH("syrk_bf16", work, st, k_syrk_bf16, dim3(grid), dim3(256), 0, (const uint16_t*)X,
                 rows, n, ldx, alpha, beta, S, lds, tiles);
   else

@@ -103,6 +103,7 @@ __global__ __launch_bounds__(256) void k_entropy_reduce(const unsigned long long
     res->ovf_count = *ovf_count;
     res->flags = flags ? flags[0] : 0;
     res->aux = flags ? flags[1] : 0;
+    res->aux2 = flags ? flags[2] : 0;
   }
 }
 

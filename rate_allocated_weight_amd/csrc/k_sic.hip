@@ -25,6 +25,7 @@ namespace wsic {
 namespace {
 
 constexpr int BW = 128;                  // block width
+constexpr int HIT_CAP = 32;              // decisions re-checked one by one before a full redo
 constexpr int PACK = 9216;               // doubles per packed block
 constexpr int pack_off(int j) { return 16 * ((j >> 4) + 1) * (8 * (j >> 4) + (j & 15)); }
 static_assert(pack_off(BW) == PACK, "packed block size");
@@ -156,35 +157,109 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
       }
     }
   }
+  // incoming interference as received (int8 product + exact excess terms), for the check below
+  double gin[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) gin[s] = yv[s] * p.invc - z[s];
   __syncthreads();
 
   run_block(z, Bs + l16);
   if (I8 && HAS_G) {
-    // Rare: a decision inside the error bound. Recompute this workgroup's incoming
-    // interference exactly (fp64, full codes) and redo the block from there.
-    bool hit = false;
+    // A rounding decision closer to a boundary than the error bound of the int8 product is
+    // first re-checked on its own: the workgroup forms that decision's exact fp64 interference
+    // (one dot product over the finished columns, split over all 256 threads) and compares the
+    // rounding. Only when some decision would change (or there are too many to check) is the
+    // whole block re-derived from exact interference.
+    __shared__ int n_hit, must_redo;
+    __shared__ int hit_j[HIT_CAP];
+    __shared__ int hit_r[HIT_CAP];
+    __shared__ double hit_z[HIT_CAP], hit_g[HIT_CAP];
+    __shared__ double red[4];
+    if (tid == 0) {
+      n_hit = 0;
+      must_redo = 0;
+    }
+    __syncthreads();
 #pragma unroll
-    for (int s = 0; s < 8; ++s) hit |= 0.5 - fabs(z[s] - rint(z[s])) <= (double)g.bnd[s];
-    if (__syncthreads_or(hit ? 1 : 0)) {
+    for (int s = 0; s < 8; ++s) {
+      if (0.5 - fabs(z[s] - rint(z[s])) <= (double)g.bnd[s]) {
+        const int h = atomicAdd(&n_hit, 1);
+        if (h < HIT_CAP) {
+          hit_j[h] = l16 + 16 * s;
+          hit_r[h] = tid >> 4;
+          hit_z[h] = z[s];
+          hit_g[h] = gin[s];
+        }
+      }
+    }
+    __syncthreads();
+    const int nh = n_hit;
+    if (tid == 0 && nh > 0) atomicAdd(p.flags + 2, nh);  // count of re-checked decisions
+    if (nh > HIT_CAP) {
+      if (tid == 0) must_redo = 1;
+    } else {
       const int64_t kbeg = j0 + BW;
+      for (int h = 0; h < nh; ++h) {
+        const int64_t rr = (int64_t)blockIdx.x * 16 + hit_r[h];
+        const double* ur = p.U + (j0 + hit_j[h]) * p.ldu;
+        const int32_t* qr = p.codes + rr * p.ldq;
+        double part = 0.0;
+#pragma unroll 4
+        for (int64_t k = kbeg + tid; k < p.n_in; k += 256)
+          part = fma(ur[k], (double)qr[k] * p.invd[k], part);
+        for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+        if (lane == 0) red[tid >> 6] = part;
+        __syncthreads();
+        if (tid == 0) {
+          const double dot = (red[0] + red[1]) + (red[2] + red[3]);
+          const double zx = hit_z[h] + (hit_g[h] - dot);
+          if (rint(zx) != rint(hit_z[h])) must_redo = 1;
+        }
+        __syncthreads();
+      }
+    }
+    __syncthreads();
+    if (must_redo) {
+      // each lane streams its own 8 rows of U along k in 4-column chunks (contiguous loads),
+      // against its row's codes scaled by 1/U_kk
+      const int64_t kbeg = j0 + BW;
+      double acc[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) z[s] = 0.0;
+      for (int s = 0; s < 8; ++s) acc[s] = 0.0;
       if (active) {
-        for (int64_t k = kbeg; k < p.n_in; ++k) {
-          const double q = (double)p.codes[row * p.ldq + k] * p.invd[k];
+        const int32_t* qrow = p.codes + row * p.ldq;
+        constexpr int CH = 4;
+        const int64_t kfull = kbeg + ((p.n_in - kbeg) / CH) * CH;
+#pragma unroll 1
+        for (int64_t k = kbeg; k < kfull; k += CH) {
+          double qk[CH];
+#pragma unroll
+          for (int e = 0; e < CH; ++e) qk[e] = (double)qrow[k + e] * p.invd[k + e];
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
             const int j = l16 + 16 * s;
-            if (j < w) z[s] = fma(p.U[(j0 + j) * p.ldu + k], q, z[s]);
+            if (j < w) {
+              const double* ur = p.U + (j0 + j) * p.ldu + k;
+#pragma unroll
+              for (int e = 0; e < CH; ++e) acc[s] = fma(ur[e], qk[e], acc[s]);
+            }
           }
         }
+        for (int64_t k = kfull; k < p.n_in; ++k) {
+          const double q = (double)qrow[k] * p.invd[k];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int j = l16 + 16 * s;
-          z[s] = (j < w) ? p.Y[row * p.ldy + j0 + j] * p.invc - z[s] : 0.0;
+          for (int s = 0; s < 8; ++s) {
+            const int j = l16 + 16 * s;
+            if (j < w) acc[s] = fma(p.U[(j0 + j) * p.ldu + k], q, acc[s]);
+          }
         }
       }
-      if (lane == 0) atomicAdd(p.flags + 1, 1);  // count of exact re-derivations
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int j = l16 + 16 * s;
+        z[s] = (active && j < w) ? yv[s] * p.invc - acc[s] : 0.0;
+      }
+      if (tid == 0) atomicAdd(p.flags + 1, 1);  // count of exact re-derivations
       run_block(z, Bs + l16);
     }
   }

@@ -124,7 +124,7 @@ struct SicWs {
   int8_t* D;        // LIMBS planes n_in x ld_i8
   int8_t* q8;       // n_out x ld_i8
   // per-pass state, cleared by one fill: flags word(s), row |q| sums, excess list counts
-  int* pflags;      // [0] flag bits of the pass, [1] exact re-derivations
+  int* pflags;      // [0] flag bits of the pass, [1] exact re-derivations, [2] re-checked decisions
   double* absq;
   int* ocnt;
   size_t pass_bytes;
@@ -420,7 +420,7 @@ int sic_pass_once(const SicCtx& x, double c, int32_t* codes, int64_t ldq, float*
 int sic_pass(const SicCtx& x, double c, int32_t* codes, int64_t ldq, float* resid, int64_t ldr,
              int* pass_flags) {
   WSIC_TRY(sic_pass_once(x, c, codes, ldq, resid, ldr));
-  int f[2] = {0, 0};
+  int f[3] = {0, 0, 0};
   WSIC_HIP_TRY(hipMemcpyAsync(f, x.ws.pflags, sizeof f, hipMemcpyDeviceToHost, x.st));
   WSIC_HIP_TRY(hipStreamSynchronize(x.st));
   if (x.i8 && (f[0] & FLAG_OVERFLOW_LIST)) {
@@ -430,8 +430,9 @@ int sic_pass(const SicCtx& x, double c, int32_t* codes, int64_t ldq, float* resi
     WSIC_HIP_TRY(hipMemcpyAsync(f, x.ws.pflags, sizeof f, hipMemcpyDeviceToHost, x.st));
     WSIC_HIP_TRY(hipStreamSynchronize(x.st));
   }
-  if (std::getenv("WSIC_TRACE") && f[1])
-    std::fprintf(stderr, "wsic sic pass: %d workgroup(s) re-derived in fp64\n", f[1]);
+  if (std::getenv("WSIC_TRACE") && (f[1] || f[2]))
+    std::fprintf(stderr, "wsic sic pass: %d decision(s) re-checked, %d workgroup(s) re-derived\n",
+                 f[2], f[1]);
   if (pass_flags) *pass_flags = f[0];
   return flags_status(f[0], "sic pass");
 }
@@ -439,7 +440,7 @@ int sic_pass(const SicCtx& x, double c, int32_t* codes, int64_t ldq, float* resi
 // ============================================================== entropy
 int entropy_of(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq, const HistWs& h,
                const int* dflags, hipStream_t st, double* H, int64_t* nsym, int* flags_out,
-               int* aux_out = nullptr) {
+               int* aux_out = nullptr, int* aux2_out = nullptr) {
   WSIC_TRY(launch_fill_zero(h.bins, HIST_CLEAR_BYTES, st));
   WSIC_TRY(launch_hist(codes, n_out, n_in, ldq, h.bins, h.ovf, h.ovf_count, st));
   WSIC_TRY(launch_entropy_reduce(h.bins, h.ovf_count, dflags, h.res, st));
@@ -448,6 +449,7 @@ int entropy_of(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq, c
   WSIC_HIP_TRY(hipStreamSynchronize(st));
   if (flags_out) *flags_out = r.flags;
   if (aux_out) *aux_out = r.aux;
+  if (aux2_out) *aux2_out = r.aux2;
   double s = r.sum_nlogn;
   int64_t ns = (int64_t)r.nsym;
   if (r.ovf_count > 0) {
@@ -679,9 +681,9 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
       }
       ++passes;
       WSIC_TRY(sic_pass_once(x, c, cbuf[buf], ldq, rbuf[buf], ldr));
-      int f = 0, nfix = 0;
+      int f = 0, nfix = 0, nchk = 0;
       WSIC_TRY(entropy_of(cbuf[buf], n_out, n_in, ldq, wf.hist, x.ws.pflags, st, H, nullptr, &f,
-                          &nfix));
+                          &nfix, &nchk));
       if (x.i8 && (f & FLAG_OVERFLOW_LIST)) {  // a row listed too many large codes: fp64 pass
         SicCtx y = x;
         y.i8 = false;
@@ -689,8 +691,10 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
         WSIC_TRY(entropy_of(cbuf[buf], n_out, n_in, ldq, wf.hist, x.ws.pflags, st, H, nullptr, &f));
       }
       if (trace)
-        std::fprintf(stderr, "wsic waterfill pass %d: c=%.17g H=%.17g (%d workgroups re-derived)\n",
-                     passes, c, *H, nfix);
+        std::fprintf(stderr,
+                     "wsic waterfill pass %d: c=%.17g H=%.17g (%d decisions re-checked, %d "
+                     "workgroups re-derived)\n",
+                     passes, c, *H, nchk, nfix);
       return flags_status(f, "waterfill");
     };
     auto free_buf = [&]() { return hi_buf == 0 ? 1 : 0; };
