@@ -16,6 +16,7 @@
 // A[l%32][8*(l/32) + e], B operand B[8*(l/32) + e][l%32], result register r of lane l is
 // D[8*(r/4) + 4*(l/32) + r%4][l%32].
 #include "common.h"
+#include "pipe.h"
 
 namespace wsic {
 namespace {
@@ -128,39 +129,29 @@ __global__ __launch_bounds__(256) void k_syrk_bf16(const uint16_t* __restrict__ 
 
 // bf16 X, pipelined: Sigma tile 128 x 128 per 256-thread workgroup (upper tiles only, enumerated
 // triangularly); 4 waves in 2 x 2, each 64 x 64 = 2 x 2 fragments of v_mfma_f32_32x32x16_bf16.
-// Per K-step of 32 calibration rows the two 32 x 128 row strips of X (the tile's rows and its
-// columns of Sigma) go global -> LDS directly (global_load_lds_dwordx4) through a ring of 3
+// Per K-step of 64 calibration rows the two 64 x 128 row strips of X (the tile's rows and its
+// columns of Sigma) go global -> LDS directly (global_load_lds_dwordx4) through a ring of 4
 // buffers, in X's own row-major layout with the 16-byte chunks of row r XOR-swizzled by 2 (r & 3).
 // The MFMA wants 8 consecutive rows of X per lane; ds_read_b64_tr_b16 delivers them: within each
 // 16-lane group, lane i receives element i % 4 of the 8-byte rows addressed by lanes 4v + i / 4
 // (v = 0..3, checked on gfx950), so lanes pointing at [k0 + j/4][c0 + 4 (j%4)] hand lane i the
 // values X[k0 .. k0+3][c0 + i]. fp32 sums over 256 rows are folded into fp64 accumulators.
-// Rows and columns past the matrix read a zero chunk. Requirements (checked by the launcher):
-// n % 8 == 0, ldx % 8 == 0, X 16-byte aligned.
+// Operands are read through a buffer resource over X, so rows and columns past the matrix read
+// zeros. Requirements (checked by the launcher): n % 8 == 0, ldx % 8 == 0, X 16-byte aligned,
+// X's span below 2 GiB.
 namespace sdma {
-constexpr int T = 128, TKR = 32, STAGES = 3, FOLD_STEPS = 256 / TKR;
-constexpr int STRIP = TKR * T * 2;  // 8 KiB
+constexpr int T = 128, TKR = 128, STAGES = 2, FOLD_STEPS = 256 / TKR;
+constexpr int STRIP = TKR * T * 2;  // 16 KiB
 constexpr int STAGE = 2 * STRIP;
 constexpr int INS = STRIP / 4096;   // DMA instructions per wave per strip
 constexpr int DMA = 2 * INS;
-typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 // byte offset of bf16 column c of row r inside a strip
 __device__ __forceinline__ int strip_off(int r, int c) {
   return r * (T * 2) + (((c >> 3) ^ (2 * (r & 3))) << 4) + ((c & 7) << 1);
 }
 }  // namespace sdma
-
-__device__ __align__(16) uint4 g_zero16 = {0u, 0u, 0u, 0u};
 
 __global__ __launch_bounds__(256) void k_syrk_bf16_dma(const uint16_t* __restrict__ X, int64_t rows,
                                                        int64_t n, int64_t ldx, double alpha,
@@ -168,7 +159,6 @@ __global__ __launch_bounds__(256) void k_syrk_bf16_dma(const uint16_t* __restric
                                                        int64_t lds) {
   constexpr int T = sdma::T, TKR = sdma::TKR, STAGES = sdma::STAGES, FOLD_STEPS = sdma::FOLD_STEPS;
   constexpr int STRIP = sdma::STRIP, STAGE = sdma::STAGE, INS = sdma::INS, DMA = sdma::DMA;
-  using sdma::lds_void;
   using sdma::lds_v4s;
   using sdma::v4s;
   using sdma::strip_off;
@@ -197,6 +187,7 @@ __global__ __launch_bounds__(256) void k_syrk_bf16_dma(const uint16_t* __restric
       dcol[sidx][h] = (sidx == 0 ? i0 : j0) + 8 * c;
       dcol_ok[sidx][h] = dcol[sidx][h] < n;
     }
+  const __amdgpu_buffer_rsrc_t xr = pipe::make_rsrc(X, (unsigned)(rows * ldx * 2));
   auto issue = [&](int64_t k0, int buf) {
     char* base = smem + buf * STAGE;
 #pragma unroll
@@ -204,11 +195,10 @@ __global__ __launch_bounds__(256) void k_syrk_bf16_dma(const uint16_t* __restric
 #pragma unroll
       for (int h = 0; h < INS; ++h) {
         const int64_t r = k0 + drow[sidx][h];
-        const void* src = (r < rows && dcol_ok[sidx][h])
-                              ? (const void*)(X + r * ldx + dcol[sidx][h])
-                              : (const void*)&g_zero16;
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + sidx * STRIP + 1024 * (INS * wave + h)),
-                                         16, 0, 0);
+        const unsigned voff = (r < rows && dcol_ok[sidx][h])
+                                  ? (unsigned)((r * ldx + dcol[sidx][h]) * 2)
+                                  : pipe::OUT_OF_RANGE;
+        pipe::dma16_buf(xr, voff, base + sidx * STRIP + 1024 * (INS * wave + h));
       }
   };
 
@@ -229,18 +219,17 @@ __global__ __launch_bounds__(256) void k_syrk_bf16_dma(const uint16_t* __restric
   const int rsub = jl >> 2, csub = 4 * (jl & 3);
 
   const int nk = (int)((rows + TKR - 1) / TKR);
-  if (nk > 0) issue(0, 0);
-  if (nk > 1) issue(TKR, 1);
-  int cur = 0, nxt = 2;
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue((int64_t)st * TKR, st);
+  int cur = 0;
   for (int t = 0; t < nk; ++t) {
-    if (t + 1 < nk) sdma::wait_vm<DMA>();
-    else sdma::wait_vm<0>();
-    sdma::barrier_lds();
-    if (t + 2 < nk) issue((int64_t)(t + 2) * TKR, nxt);
+    pipe::wait_ahead<DMA, STAGES - 2>(min(STAGES - 2, nk - 1 - t));
+    pipe::barrier_lds();
+    if (t + STAGES - 1 < nk) issue((int64_t)(t + STAGES - 1) * TKR, cur == 0 ? STAGES - 1 : cur - 1);
     const char* As = smem + cur * STAGE;
     const char* Bs = As + STRIP;
     cur = (cur == STAGES - 1) ? 0 : cur + 1;
-    nxt = (nxt == STAGES - 1) ? 0 : nxt + 1;
 #pragma unroll
     for (int ks = 0; ks < TKR / 16; ++ks) {
       bf8 a[2], b[2];
@@ -376,7 +365,8 @@ int launch_syrk(const void* X, int dtype, int64_t rows, int64_t n, int64_t ldx, 
   const int tiles = (int)((n + T - 1) / T);
   const unsigned grid = (unsigned)((int64_t)tiles * tiles);
   const double work = (double)rows * (double)n * (double)(n + 1);  // flops of the upper triangle
-  const bool dma_ok = n % 8 == 0 && ldx % 8 == 0 && (((uintptr_t)X) & 15) == 0;
+  const bool dma_ok = n % 8 == 0 && ldx % 8 == 0 && (((uintptr_t)X) & 15) == 0 &&
+                      rows * ldx * 2 < (int64_t)pipe::OUT_OF_RANGE;
   if (dtype == WSIC_BF16 && dma_ok) {
     const int64_t t = (n + sdma::T - 1) / sdma::T;
     WSIC_LAUNCH("syrk_bf16", work, st, k_syrk_bf16_dma, dim3((unsigned)(t * (t + 1) / 2)), dim3(256),

@@ -18,6 +18,7 @@
 // MFMA f64 16x16x4 lane layout (checked on gfx950): A operand lane l = A[l%16][l/16],
 // B operand lane l = B[l/16][l%16], result register r of lane l = D[l/16 + 4r][l%16].
 #include "common.h"
+#include "pipe.h"
 
 namespace wsic {
 namespace {
@@ -182,16 +183,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, int tiles_n) {
 namespace ydma {
 constexpr int TM = 128, TN = 128, TKY = 16, STAGES = 3;
 constexpr int B_BYTES = TN * TKY * 8;  // 16 KiB
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 template <typename TA>
 __device__ __forceinline__ double widen(TA v);
 template <>
@@ -247,10 +238,10 @@ __global__ __launch_bounds__(256) void k_gemm_y(int64_t M, int64_t N, int64_t K,
     char* base = smem + buf * STAGE;
 #pragma unroll
     for (int h = 0; h < A_INS; ++h)
-      __builtin_amdgcn_global_load_lds((const void*)(asrc[h] + k0), (lds_void*)(base + aoff[h]), 16, 0, 0);
+      pipe::dma16(asrc[h] + k0, base + aoff[h]);
 #pragma unroll
     for (int h = 0; h < B_INS; ++h)
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[h] + k0), (lds_void*)(base + boff[h]), 16, 0, 0);
+      pipe::dma16(bsrc[h] + k0, base + boff[h]);
   };
 
   d4 acc[4][4];
@@ -266,9 +257,8 @@ __global__ __launch_bounds__(256) void k_gemm_y(int64_t M, int64_t N, int64_t K,
   if (nk > 1) issue(kbeg + TKY, 1);
   int cur = 0, nxt = 2;
   for (int t = 0; t < nk; ++t) {
-    if (t + 1 < nk) wait_vm<DMA>();
-    else wait_vm<0>();
-    barrier_lds();
+    pipe::wait_ahead<DMA, STAGES - 2>(min(STAGES - 2, nk - 1 - t));
+    pipe::barrier_lds();
     if (t + 2 < nk) issue(kbeg + (int64_t)(t + 2) * TKY, nxt);
     const char* As = smem + cur * STAGE;
     const char* Bs = As + A_BYTES;

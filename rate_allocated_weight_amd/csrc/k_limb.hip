@@ -17,6 +17,7 @@
 // A[l%32][16*(l/32) + e], B operand B[16*(l/32) + e][l%32], result register r of lane l is
 // D[8*(r/4) + 4*(l/32) + r%4][l%32].
 #include "common.h"
+#include "pipe.h"
 
 namespace wsic {
 namespace {
@@ -97,24 +98,9 @@ constexpr int B_INSTR = B_BYTES / 1024 / 4;
 constexpr int DMA_PER_STAGE = A_INSTR + B_INSTR;
 static_assert(A_INSTR * 4096 == A_BYTES && B_INSTR * 4096 == B_BYTES, "whole DMA rounds");
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
-// Workgroup barrier without the memory fence of __syncthreads(): that fence would also wait
-// for every operand load still in flight. LDS traffic of this wave is drained first; the DMA
-// writes a wave depends on are ordered by wait_vm before it.
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K,
                                                  const int8_t* __restrict__ A8, int64_t lda,
                                                  const int8_t* __restrict__ D, int64_t ldd,
@@ -169,10 +155,10 @@ __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K
     const int64_t k0 = kstep * TKB;
 #pragma unroll
     for (int h = 0; h < A_INSTR; ++h)
-      __builtin_amdgcn_global_load_lds((const void*)(asrc[h] + k0), (lds_void*)(base + aoff[h]), 16, 0, 0);
+      pipe::dma16(asrc[h] + k0, base + aoff[h]);
 #pragma unroll
     for (int h = 0; h < B_INSTR; ++h)
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[h] + k0), (lds_void*)(base + boff[h]), 16, 0, 0);
+      pipe::dma16(bsrc[h] + k0, base + boff[h]);
   };
 
   v16i acc[2][NL];
@@ -186,18 +172,16 @@ __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K
   const int hs = lane >> 5;
 
   const int nk = (int)((K + TKB - 1) / TKB);
-  static_assert(STAGES == 3, "wait counts below assume three buffers");
-  issue(0, 0);
-  if (nk > 1) issue(1, 1);
-  int cur = 0, nxt = 2;  // buffer of step t, buffer of step t + 2
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue(st, st);
+  int cur = 0;  // buffer of step t; step t + STAGES - 1 goes into the one before it
   for (int t = 0; t < nk; ++t) {
-    if (t + 1 < nk) wait_vm<DMA_PER_STAGE>();
-    else wait_vm<0>();
-    barrier_lds();  // step t is in LDS for every wave; every wave is done with step t - 1
-    if (t + 2 < nk) issue(t + 2, nxt);
+    pipe::wait_ahead<DMA_PER_STAGE, STAGES - 2>(min(STAGES - 2, nk - 1 - t));
+    pipe::barrier_lds();  // step t is in LDS for every wave; every wave is done with step t - 1
+    if (t + STAGES - 1 < nk) issue(t + STAGES - 1, cur == 0 ? STAGES - 1 : cur - 1);
     const int8_t* As = smem + cur * STAGE_BYTES;
     cur = (cur == STAGES - 1) ? 0 : cur + 1;
-    nxt = (nxt == STAGES - 1) ? 0 : nxt + 1;
     const int8_t* Bs = As + A_BYTES;
 #pragma unroll
     for (int ks = 0; ks < TKB / 32; ++ks) {
