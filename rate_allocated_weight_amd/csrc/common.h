@@ -170,6 +170,13 @@ struct LeafArgs {
   double* absq;  // per row: sum |q| over the columns done so far in this pass
   int* ocnt;     // per row: entries in the excess list
   int2* olist;   // per row: OCAP (column, q - clamp(q)) pairs
+  // interference of the finished columns [kf0, kf0 + kf) formed inside the leaf from the int8
+  // digit planes (kf = 0: none)
+  const int8_t* D;        // digit plane 0 (row j, column k at D[j * ldd + k])
+  int64_t ldd, plane;
+  const double* escale;   // 2^(e_j - P)
+  int64_t kf0;
+  int kf;
 };
 int launch_sic_leaf(const LeafArgs& p, bool i8, hipStream_t st);
 

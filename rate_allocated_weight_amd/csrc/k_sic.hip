@@ -96,8 +96,10 @@ __device__ __forceinline__ void run_block(double (&z)[8], const double* __restri
 // applies the exact excess of codes beyond +-127 listed by earlier leaves, guards its rounding
 // decisions with the error bound, and emits what the next limb products need: the int8 code
 // plane, the row sums of |q| and its own excess list.
-template <bool HAS_G, bool HAS_RESID, bool I8>
+template <bool HAS_G, bool HAS_RESID, bool I8, bool FUSE>
 __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
+  static_assert(!FUSE || I8, "the fused product is the int8 one");
+  constexpr bool GIN = HAS_G || FUSE;  // the block receives interference from finished columns
   __shared__ __attribute__((aligned(16))) double Bs[PACK];
   const int tid = threadIdx.x;
   const int l16 = tid & 15, lane = tid & 63;
@@ -122,8 +124,64 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
     const bool in = active && j < w;
     yv[s] = in ? p.Y[row * p.ldy + j0 + j] : 0.0;
     gv[s] = (HAS_G && in) ? p.G[row * p.ldg + j0 + j] : 0.0;
-    bsc[s] = (I8 && HAS_G && in) ? p.bscale[j0 + j] : 0.0;
+    bsc[s] = (I8 && GIN && in) ? p.bscale[j0 + j] : 0.0;
     dsc[s] = (HAS_RESID && in) ? p.invd[j0 + j] : 0.0;
+  }
+  // Interference of the finished columns [kf0, kf0 + kf) next to the block, formed here on the
+  // int8 matrix cores (the same digit planes and error bound as the separate product): wave v
+  // takes block columns 32 v .. 32 v + 31 against the workgroup's 16 rows (a 32-row fragment with
+  // the upper half zero), 5 digit accumulators, combined in fp64 and staged through LDS (the
+  // B-block area, loaded afterwards) into the target layout.
+  double fz[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) fz[s] = 0.0;
+  if constexpr (FUSE) {
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    typedef int v16i __attribute__((ext_vector_type(16)));
+    const int wv = tid >> 6, mrow = lane & 31, kh = lane >> 5;
+    const int64_t arow = (int64_t)blockIdx.x * 16 + mrow;
+    const bool a_ok = mrow < 16 && arow < p.n_out;
+    const int jn = 32 * wv + (lane & 31);
+    const bool b_ok = jn < w;
+    const int8_t* ap = p.q8 + (a_ok ? arow : 0) * p.ldq8 + p.kf0 + 16 * kh;
+    const int8_t* bp = p.D + (j0 + (b_ok ? jn : 0)) * p.ldd + p.kf0 + 16 * kh;
+    const int nks = (p.kf + 31) / 32;
+    v16i acc[LIMBS];
+#pragma unroll
+    for (int l = 0; l < LIMBS; ++l) acc[l] = (v16i){};
+    // k-steps in groups of GK: every operand load of a group is in flight before its products
+    constexpr int GK = 4;
+    for (int k0 = 0; k0 < nks; k0 += GK) {
+      v4i a[GK], b[GK][LIMBS];
+#pragma unroll
+      for (int g4 = 0; g4 < GK; ++g4) {
+        const bool in = k0 + g4 < nks;
+        a[g4] = (a_ok && in) ? *reinterpret_cast<const v4i*>(ap + 32 * (k0 + g4)) : (v4i){0, 0, 0, 0};
+#pragma unroll
+        for (int l = 0; l < LIMBS; ++l)
+          b[g4][l] = (b_ok && in) ? *reinterpret_cast<const v4i*>(bp + l * p.plane + 32 * (k0 + g4))
+                                  : (v4i){0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int g4 = 0; g4 < GK; ++g4)
+#pragma unroll
+        for (int l = 0; l < LIMBS; ++l)
+          acc[l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[g4], b[g4][l], acc[l], 0, 0, 0);
+    }
+    const double es = b_ok ? p.escale[j0 + jn] : 0.0;
+    double* Fs = Bs;  // [16][BW]
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {  // result rows 8 (r/4) + 4 kh + r%4 < 16
+      double f = 0.0;
+#pragma unroll
+      for (int l = 0; l < LIMBS; ++l)
+        f = fma((double)acc[l][r], ldexp(1.0, 8 * (LIMBS - 1 - l)), f);
+      Fs[(8 * (r >> 2) + 4 * kh + (r & 3)) * BW + jn] = f * es;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) fz[s] = Fs[(tid >> 4) * BW + l16 + 16 * s];
+    __syncthreads();  // before the B block overwrites the staging area
   }
   {
     constexpr int PER = PACK / 2 / 256;
@@ -141,10 +199,10 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
   Guard g;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    z[s] = yv[s] * p.invc - gv[s];
-    g.bnd[s] = (I8 && HAS_G) ? __double2float_ru(bsc[s] * S * LIMB_EPS * p.guard_scale) : 0.0f;
+    z[s] = yv[s] * p.invc - gv[s] - fz[s];
+    g.bnd[s] = (I8 && GIN) ? __double2float_ru(bsc[s] * S * LIMB_EPS * p.guard_scale) : 0.0f;
   }
-  if (I8 && HAS_G && active) {
+  if (I8 && GIN && active) {
     // exact interference of the excess of large codes to the right (fp64)
     const int cnt = min(cnt0, OCAP);
     for (int o = 0; o < cnt; ++o) {
@@ -164,7 +222,7 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
   __syncthreads();
 
   run_block(z, Bs + l16);
-  if (I8 && HAS_G) {
+  if (I8 && GIN) {
     // A rounding decision closer to a boundary than the error bound of the int8 product is
     // first re-checked on its own: the workgroup forms that decision's exact fp64 interference
     // (one dot product over the finished columns, split over all 256 threads) and compares the
@@ -458,6 +516,11 @@ int launch_sic_leaf(const LeafArgs& a, bool i8, hipStream_t st) {
     set_error("internal: integer-interference leaf without its buffers");
     return WSIC_E_INVAL;
   }
+  if (a.kf > 0 && (!i8 || !a.D || !a.escale || a.kf0 != a.j0 + BW || (a.ldd % 16) != 0 ||
+                   (a.ldq8 % 16) != 0 || (a.kf0 % 16) != 0)) {
+    set_error("internal: fused leaf product preconditions");
+    return WSIC_E_INVAL;
+  }
   LeafArgs p = a;
   p.Bpk = a.Bpk + (a.j0 / BW) * PACK;
   p.invc = 1.0 / a.c;
@@ -465,19 +528,24 @@ int launch_sic_leaf(const LeafArgs& a, bool i8, hipStream_t st) {
   // bytes that must stream: Y (+G) in, codes (+resid, +int8 codes) out
   const double work = (double)a.n_out * a.w *
                       (8.0 + (a.G ? 8.0 : 0.0) + 4.0 + (a.resid ? 4.0 : 0.0) + (i8 ? 1.0 : 0.0));
-#define WSIC_LEAF(HG, HR, I8)                                                                      \
-  WSIC_LAUNCH("sic_leaf", work, st, (k_sic_leaf<HG, HR, I8>), dim3(blocks), dim3(256), 0, p)
-  const bool hg = a.G != nullptr, hr = a.resid != nullptr;
-  if (i8) {
-    if (hg && hr) WSIC_LEAF(true, true, true);
-    else if (hg) WSIC_LEAF(true, false, true);
-    else if (hr) WSIC_LEAF(false, true, true);
-    else WSIC_LEAF(false, false, true);
+#define WSIC_LEAF(HG, HR, I8, FU)                                                                  \
+  WSIC_LAUNCH("sic_leaf", work, st, (k_sic_leaf<HG, HR, I8, FU>), dim3(blocks), dim3(256), 0, p)
+  const bool hg = a.G != nullptr, hr = a.resid != nullptr, fu = a.kf > 0;
+  if (i8 && fu) {
+    if (hg && hr) WSIC_LEAF(true, true, true, true);
+    else if (hg) WSIC_LEAF(true, false, true, true);
+    else if (hr) WSIC_LEAF(false, true, true, true);
+    else WSIC_LEAF(false, false, true, true);
+  } else if (i8) {
+    if (hg && hr) WSIC_LEAF(true, true, true, false);
+    else if (hg) WSIC_LEAF(true, false, true, false);
+    else if (hr) WSIC_LEAF(false, true, true, false);
+    else WSIC_LEAF(false, false, true, false);
   } else {
-    if (hg && hr) WSIC_LEAF(true, true, false);
-    else if (hg) WSIC_LEAF(true, false, false);
-    else if (hr) WSIC_LEAF(false, true, false);
-    else WSIC_LEAF(false, false, false);
+    if (hg && hr) WSIC_LEAF(true, true, false, false);
+    else if (hg) WSIC_LEAF(true, false, false, false);
+    else if (hr) WSIC_LEAF(false, true, false, false);
+    else WSIC_LEAF(false, false, false, false);
   }
 #undef WSIC_LEAF
   return WSIC_OK;

@@ -348,10 +348,63 @@ int sic_setup(const SicCtx& x) {
 
 // Columns [lo, hi): G[:, lo:hi] holds the interference of every column >= hi (none when
 // hi == n_in). Right half first, then its interference on the left half, then the left half.
+// With the int8 product, a range of at most SUPER blocks is finished leaf by leaf, right to left,
+// each leaf forming the interference of the columns between it and hi itself.
+constexpr int64_t SUPER = 4;
+
+int sic_leaf_at(const SicCtx& x, int64_t j0, int64_t wb, int64_t hi, double c, int32_t* codes,
+                int64_t ldq, float* resid, int64_t ldr, bool fuse) {
+  const bool has_g = hi < x.n_in;
+  LeafArgs a{};
+  a.n_out = x.n_out;
+  a.n_in = x.n_in;
+  a.j0 = j0;
+  a.w = (int)wb;
+  a.Y = x.ws.Y;
+  a.ldy = x.n_in;
+  a.G = has_g ? x.ws.G : nullptr;
+  a.ldg = x.n_in;
+  a.Bpk = x.ws.Bpk;
+  a.invd = x.ws.invd;
+  a.c = c;
+  a.codes = codes;
+  a.ldq = ldq;
+  a.resid = resid;
+  a.ldr = ldr;
+  a.flags = x.ws.pflags;
+  a.U = x.U;
+  a.ldu = x.ldu;
+  a.bscale = x.ws.bscale;
+  a.guard_scale = x.guard_scale;
+  a.q8 = x.ws.q8;
+  a.ldq8 = ld_i8(x.n_in);
+  a.absq = x.ws.absq;
+  a.ocnt = x.ws.ocnt;
+  a.olist = x.ws.olist;
+  if (fuse && j0 + BW < hi) {
+    a.D = x.ws.D;
+    a.ldd = ld_i8(x.n_in);
+    a.plane = x.n_in * a.ldd;
+    a.escale = x.ws.escale;
+    a.kf0 = j0 + BW;
+    a.kf = (int)(hi - (j0 + BW));
+  }
+  return launch_sic_leaf(a, x.i8, x.st);
+}
+
 int sic_range(const SicCtx& x, int64_t lo, int64_t hi, double c, int32_t* codes, int64_t ldq,
               float* resid, int64_t ldr) {
   const int64_t w = hi - lo;
   const bool has_g = hi < x.n_in;
+  if (x.i8 && w <= SUPER * BW) {
+    const int64_t nb = (w + BW - 1) / BW;
+    for (int64_t b = nb - 1; b >= 0; --b) {
+      const int64_t j0 = lo + b * BW;
+      WSIC_TRY(sic_leaf_at(x, j0, std::min<int64_t>(BW, hi - j0), hi, c, codes, ldq, resid, ldr,
+                           true));
+    }
+    return WSIC_OK;
+  }
   if (w <= BW) {
     LeafArgs a{};
     a.n_out = x.n_out;
