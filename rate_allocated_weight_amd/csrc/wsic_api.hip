@@ -280,10 +280,60 @@ int check_layer(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t l
     if (_rc != WSIC_OK) return _rc; \
   } while (0)
 
-int read_flags(const int* dflags, int* out, hipStream_t st) {
-  WSIC_HIP_TRY(hipMemcpyAsync(out, dflags, sizeof(int), hipMemcpyDeviceToHost, st));
-  WSIC_HIP_TRY(hipStreamSynchronize(st));
+// Device -> host reads at the synchronization points of the API. The pieces land in a pinned
+// per-thread staging buffer (a direct DMA target, unlike pageable memory) and completion is
+// polled on an event, which returns sooner than a blocking stream synchronization; after a
+// short spin the wait blocks on the event instead.
+struct ReadPiece {
+  void* host;
+  const void* dev;
+  size_t bytes;
+};
+
+struct HostStage {
+  char* buf = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+};
+thread_local HostStage t_stage;  // never freed: one small pinned buffer per calling thread
+
+int read_back(const ReadPiece* p, int n, hipStream_t st) {
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) total += align_up(p[i].bytes, 16);
+  HostStage& hs = t_stage;
+  if (!hs.ev) WSIC_HIP_TRY(hipEventCreateWithFlags(&hs.ev, hipEventDisableTiming));
+  if (total > hs.cap) {
+    const size_t cap = std::max<size_t>(total, 4096);
+    char* nb = nullptr;
+    WSIC_HIP_TRY(hipHostMalloc((void**)&nb, cap, hipHostMallocDefault));
+    if (hs.buf) (void)hipHostFree(hs.buf);
+    hs.buf = nb;
+    hs.cap = cap;
+  }
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    WSIC_HIP_TRY(hipMemcpyAsync(hs.buf + off, p[i].dev, p[i].bytes, hipMemcpyDeviceToHost, st));
+    off += align_up(p[i].bytes, 16);
+  }
+  WSIC_HIP_TRY(hipEventRecord(hs.ev, st));
+  hipError_t e = hipErrorNotReady;
+  for (int spin = 0; spin < (1 << 22) && e == hipErrorNotReady; ++spin) e = hipEventQuery(hs.ev);
+  if (e == hipErrorNotReady) e = hipEventSynchronize(hs.ev);
+  if (e != hipSuccess) {
+    set_error("device read-back failed: %s", hipGetErrorString(e));
+    return WSIC_E_HIP;
+  }
+  off = 0;
+  for (int i = 0; i < n; ++i) {
+    std::memcpy(p[i].host, hs.buf + off, p[i].bytes);
+    off += align_up(p[i].bytes, 16);
+  }
   return WSIC_OK;
+}
+
+int read_flags(const int* dflags, int* out, hipStream_t st) {
+  const ReadPiece pc{out, dflags, sizeof(int)};
+  return read_back(&pc, 1, st);
 }
 
 int flags_status(int f, const char* what) {
@@ -328,7 +378,8 @@ SicCtx make_ctx(int64_t n_out, int64_t n_in, const void* W, int dtype, int64_t l
 }
 
 // invd, Y = W U^T, input checks. Leaves flags on the device (read by the caller).
-int sic_setup(const SicCtx& x) {
+// With read_now false the flags stay on the device for the caller to read with its next read-back.
+int sic_setup(const SicCtx& x, bool read_now = true) {
   WSIC_TRY(launch_fill_zero(x.ws.flags, FLAGS_BYTES, x.st));
   WSIC_TRY(launch_check_finite(x.W, x.dtype, x.n_out, x.n_in, x.ldw, x.ws.flags, x.st));
   WSIC_TRY(launch_prep(x.U, x.ldu, x.n_in, x.ws.invd, x.ws.flags, x.st));
@@ -341,6 +392,7 @@ int sic_setup(const SicCtx& x) {
   const double work = (double)x.n_out * (double)x.n_in * (double)(x.n_in + 1);
   WSIC_TRY(launch_gemm_y(x.dtype, x.n_out, x.n_in, x.n_in, x.W, x.ldw, x.U, x.ldu, x.ws.Y, x.n_in,
                          work, x.st));
+  if (!read_now) return WSIC_OK;
   int f = 0;
   WSIC_TRY(read_flags(x.ws.flags, &f, x.st));
   return flags_status(f, "sic");
@@ -474,14 +526,13 @@ int sic_pass(const SicCtx& x, double c, int32_t* codes, int64_t ldq, float* resi
              int* pass_flags) {
   WSIC_TRY(sic_pass_once(x, c, codes, ldq, resid, ldr));
   int f[3] = {0, 0, 0};
-  WSIC_HIP_TRY(hipMemcpyAsync(f, x.ws.pflags, sizeof f, hipMemcpyDeviceToHost, x.st));
-  WSIC_HIP_TRY(hipStreamSynchronize(x.st));
+  const ReadPiece pc{f, x.ws.pflags, sizeof f};
+  WSIC_TRY(read_back(&pc, 1, x.st));
   if (x.i8 && (f[0] & FLAG_OVERFLOW_LIST)) {
     SicCtx y = x;
     y.i8 = false;
     WSIC_TRY(sic_pass_once(y, c, codes, ldq, resid, ldr));
-    WSIC_HIP_TRY(hipMemcpyAsync(f, x.ws.pflags, sizeof f, hipMemcpyDeviceToHost, x.st));
-    WSIC_HIP_TRY(hipStreamSynchronize(x.st));
+    WSIC_TRY(read_back(&pc, 1, x.st));
   }
   if (std::getenv("WSIC_TRACE") && (f[1] || f[2]))
     std::fprintf(stderr, "wsic sic pass: %d decision(s) re-checked, %d workgroup(s) re-derived\n",
@@ -498,8 +549,8 @@ int entropy_of(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq, c
   WSIC_TRY(launch_hist(codes, n_out, n_in, ldq, h.bins, h.ovf, h.ovf_count, st));
   WSIC_TRY(launch_entropy_reduce(h.bins, h.ovf_count, dflags, h.res, st));
   EntropyResult r;
-  WSIC_HIP_TRY(hipMemcpyAsync(&r, h.res, sizeof r, hipMemcpyDeviceToHost, st));
-  WSIC_HIP_TRY(hipStreamSynchronize(st));
+  const ReadPiece pr{&r, h.res, sizeof r};
+  WSIC_TRY(read_back(&pr, 1, st));
   if (flags_out) *flags_out = r.flags;
   if (aux_out) *aux_out = r.aux;
   if (aux2_out) *aux2_out = r.aux2;
@@ -512,9 +563,8 @@ int entropy_of(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq, c
       return WSIC_E_RANGE;
     }
     std::vector<int32_t> v(r.ovf_count);
-    WSIC_HIP_TRY(hipMemcpyAsync(v.data(), h.ovf, v.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
-                                st));
-    WSIC_HIP_TRY(hipStreamSynchronize(st));
+    const ReadPiece po{v.data(), h.ovf, v.size() * sizeof(int32_t)};
+    WSIC_TRY(read_back(&po, 1, st));
     std::sort(v.begin(), v.end());
     size_t i = 0;
     while (i < v.size()) {
@@ -629,8 +679,8 @@ int wsic_cholesky(double* A, int64_t n, int64_t lda, int64_t* info, void* ws, si
       WSIC_TRY(launch_gemm(A_F64_T, EPI_STORE, g, "gemm_chol", work, st));
     }
     WSIC_TRY(launch_zero_lower(A, n, lda, st));
-    WSIC_HIP_TRY(hipMemcpyAsync(info, dinfo, sizeof(int64_t), hipMemcpyDeviceToHost, st));
-    WSIC_HIP_TRY(hipStreamSynchronize(st));
+    const ReadPiece pi{info, dinfo, sizeof(int64_t)};
+    WSIC_TRY(read_back(&pi, 1, st));
     if (*info != 0) {
       set_error("cholesky: leading minor %lld is not positive definite", (long long)*info);
       return WSIC_E_NOT_PD;
@@ -697,25 +747,29 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
     Carve cv(ws);
     WfWs wf = carve_wf(cv, n_out, n_in);
     SicCtx x = make_ctx(n_out, n_in, W, dtype, ldw, U, ldu, wf.sic, st);
-    WSIC_TRY(sic_setup(x));
+    WSIC_TRY(sic_setup(x, false));
 
     const double R = target_bits;
-    // starting grid scale
+    // starting grid scale (the setup's flags are read with it, or alone)
     double c0 = o.c_init;
+    int setup_flags = 0;
     if (!(c0 > 0.0)) {
       WSIC_TRY(launch_colstats(W, dtype, n_out, n_in, ldw, wf.colvar + n_in, wf.colvar, st));
       WSIC_TRY(launch_delta(U, ldu, n_in, 1.0, nullptr, wf.diag, st));
       std::vector<double> var(n_in), diag(n_in);
-      WSIC_HIP_TRY(hipMemcpyAsync(var.data(), wf.colvar, n_in * sizeof(double),
-                                  hipMemcpyDeviceToHost, st));
-      WSIC_HIP_TRY(hipMemcpyAsync(diag.data(), wf.diag, n_in * sizeof(double),
-                                  hipMemcpyDeviceToHost, st));
-      WSIC_HIP_TRY(hipStreamSynchronize(st));
+      const ReadPiece pv[3] = {{var.data(), wf.colvar, n_in * sizeof(double)},
+                               {diag.data(), wf.diag, n_in * sizeof(double)},
+                               {&setup_flags, x.ws.flags, sizeof(int)}};
+      WSIC_TRY(read_back(pv, 3, st));
+      WSIC_TRY(flags_status(setup_flags, "sic"));
       double m = 0.0;
       for (int64_t j = 0; j < n_in; ++j) m += var[j] * diag[j] * diag[j];
       m /= (double)n_in;
       if (!(m > 0.0)) m = 1.0;
       c0 = std::sqrt(2.0 * M_PI * M_E * m) * std::pow(2.0, -R);
+    } else {
+      WSIC_TRY(read_flags(x.ws.flags, &setup_flags, st));
+      WSIC_TRY(flags_status(setup_flags, "sic"));
     }
 
     // two code buffers: the caller's and one in the workspace; `hi_buf` holds the codes of
@@ -959,9 +1013,9 @@ int wsic_distortion(const void* W, int dtype, int64_t n_out, int64_t n_in, int64
                            work, st));
     }
     WSIC_TRY(launch_sum_partials(d.partial, np, d.out, st));
-    WSIC_HIP_TRY(hipMemcpyAsync(D_out, d.out, sizeof(double), hipMemcpyDeviceToHost, st));
     int f = 0;
-    WSIC_TRY(read_flags(d.flags, &f, st));
+    const ReadPiece pd[2] = {{D_out, d.out, sizeof(double)}, {&f, d.flags, sizeof(int)}};
+    WSIC_TRY(read_back(pd, 2, st));
     return flags_status(f, "distortion");
   } catch (...) {
     set_error("distortion: internal exception");
