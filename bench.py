@@ -33,6 +33,7 @@ PEAKS = {
     "mfma_f32": (157.3, "TFLOP/s"),
     "mfma_bf16": (2500.0, "TFLOP/s"),
     "mfma_i8": (5000.0, "TOP/s"),
+    "valu_f64": (78.6, "TFLOP/s"),
 }
 # kernel family -> (bound, peak key, work unit scale to the peak's unit)
 FAMILIES = {
@@ -40,6 +41,8 @@ FAMILIES = {
     "gemm_trail": ("mfma", "mfma_f64", 1e-12),
     "gemm_y": ("mfma", "mfma_f64", 1e-12),
     "gemm_chol": ("mfma", "mfma_f64", 1e-12),
+    "chol_update": ("mfma", "mfma_f64", 1e-12),
+    "potrf_panel": ("alu", "valu_f64", 1e-12),
     "gemm_dist": ("mfma", "mfma_f64", 1e-12),
     "syrk_bf16": ("mfma", "mfma_bf16", 1e-12),
     "sic_leaf": ("hbm", "hbm", 1e-9),
