@@ -179,6 +179,9 @@ struct LeafArgs {
   int kf;
 };
 int launch_sic_leaf(const LeafArgs& p, bool i8, hipStream_t st);
+// int8 mode: up to 4 blocks [j0, j0 + w) in one launch (w <= 512), interference of the range's
+// finished columns formed inside; G (nullable) holds the interference of the columns >= j0 + w
+int launch_sic_super(const LeafArgs& p, hipStream_t st);
 
 int launch_limb_pack(const double* U, int64_t ldu, int64_t n, const double* invd, double* escale,
                      double* bscale, int8_t* D, int64_t ldd, hipStream_t st);

@@ -20,6 +20,7 @@
 // its entries unconditionally (a zero leaves finished targets unchanged). Column j = 16a + r
 // starts at 16 (a+1)(8a + r); a block holds 9216 doubles (72 KiB, two workgroups per CU).
 #include "common.h"
+#include "pipe.h"
 
 namespace wsic {
 namespace {
@@ -387,6 +388,350 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
   if (bad) atomicOr(p.flags, bad);
 }
 
+// ------------------------------------------------------------------ super-block kernel
+// With the int8 product, up to SUP_BLOCKS blocks of 128 columns [lo, hi) are finished by one
+// launch: each workgroup walks its 16 rows through the blocks right to left. For every block it
+// forms the interference of the super-block's finished columns on the int8 matrix cores from its
+// own codes (kept in LDS) and the digit planes, runs the 128 sequential steps as the leaf does,
+// checks its rounding decisions against the error bound, and writes codes, residuals, int8 codes
+// and excess entries. While a block's steps run, the next block's packed B (global -> LDS,
+// second buffer) and its Y / G / scale operands (registers) are already on the way. Row sums
+// and list counts stay in registers across the blocks.
+constexpr int SUP_BLOCKS = 4;  // matches the recursion's super-block width
+constexpr int SUP_W = SUP_BLOCKS * BW;
+constexpr int PACK_DMA = PACK * 8 / 1024 / 4;  // 16-byte direct LDS loads per wave per block
+static_assert(PACK_DMA * 4 * 1024 == PACK * 8, "packed block is a whole number of 1 KiB rounds");
+
+template <bool HAS_G, bool HAS_RESID>
+__global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  typedef int v16i __attribute__((ext_vector_type(16)));
+  // two packed-B buffers as separate objects, so that the compiler can tell the prefetch into
+  // one from the reads of the other (the loop below is unrolled by two for that)
+  __shared__ __attribute__((aligned(1024))) double BsA[PACK];
+  __shared__ __attribute__((aligned(1024))) double BsB[PACK];
+  __shared__ __attribute__((aligned(16))) int8_t q8s[16][SUP_W];
+  __shared__ int n_hit, must_redo;
+  __shared__ int hit_j[HIT_CAP];
+  __shared__ int hit_r[HIT_CAP];
+  __shared__ double hit_z[HIT_CAP], hit_g[HIT_CAP];
+  __shared__ double red[4];
+
+  const int tid = threadIdx.x;
+  const int l16 = tid & 15, lane = tid & 63, wave = tid >> 6;
+  const int rloc = tid >> 4;
+  const int64_t row = (int64_t)blockIdx.x * 16 + rloc;
+  const bool active = row < p.n_out;
+  const int64_t rowc = active ? row : 0;  // clamped row for unconditional loads
+  const int64_t lo = p.j0, hi = p.j0 + p.w;
+  const int nb = (p.w + BW - 1) / BW;
+
+  // this workgroup's int8 codes of the range (zero past hi)
+  for (int e = tid; e < 16 * SUP_W / 16; e += 256) reinterpret_cast<uint4*>(&q8s[0][0])[e] = make_uint4(0, 0, 0, 0);
+
+  double S = 0.0;  // sum of |q| over the finished columns of this row
+  int cnt = 0;     // entries in this row's excess list
+  if (active) {
+    S = p.absq[row];
+    cnt = p.ocnt[row];
+  }
+  int bad = 0;
+
+  // block b's packed B into LDS buffer `buf`; its per-row / per-column operands into registers
+  auto issue_pack = [&](int b, double* buf) {
+    const char* src = reinterpret_cast<const char*>(p.Bpk + (lo / BW + b) * PACK);
+    char* dst = reinterpret_cast<char*>(buf);
+#pragma unroll
+    for (int i = 0; i < PACK_DMA; ++i) {
+      const int ins = PACK_DMA * wave + i;
+      pipe::dma16(src + 1024 * ins + 16 * lane, dst + 1024 * ins);
+    }
+  };
+  auto load_ops = [&](int b, double (&yv)[8], double (&gv)[8], double (&bsc)[8]) {
+    const int64_t j0 = lo + (int64_t)b * BW;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int64_t jc = j0 + l16 + 16 * s < hi ? j0 + l16 + 16 * s : hi - 1;  // clamped column
+      yv[s] = p.Y[rowc * p.ldy + jc];
+      gv[s] = HAS_G ? p.G[rowc * p.ldg + jc] : 0.0;
+      bsc[s] = p.bscale[jc];
+    }
+  };
+
+  // Y, G and the bound's column scale (rounded up to float) of the current block
+  double yv[8], gv[8];
+  float bsf[8];
+  {
+    double b0[8];
+    issue_pack(nb - 1, BsA);
+    load_ops(nb - 1, yv, gv, b0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) bsf[s] = __double2float_ru(b0[s]);
+  }
+
+  auto do_block = [&](int b, double* Bcur, double* Bidle) {
+    const int64_t j0 = lo + (int64_t)b * BW;
+    const int w = (int)(hi - j0 < BW ? hi - j0 : BW);
+    const int64_t kf0 = j0 + BW;
+    const int kf = (int)(hi - kf0);  // finished columns of the range right of this block
+    const bool gin = HAS_G || kf > 0;
+
+    // interference of the range's finished columns [kf0, hi) (int8 product, as in the leaf)
+    double fz[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) fz[s] = 0.0;
+    if (kf > 0) {  // uniform
+      const int mrow = lane & 31, kh = lane >> 5;
+      const int jn = 32 * wave + (lane & 31);
+      const bool b_ok = jn < w;
+      const int8_t* bp = p.D + (j0 + (b_ok ? jn : 0)) * p.ldd + kf0 + 16 * kh;
+      const int8_t* as = &q8s[mrow & 15][(int)(kf0 - lo) + 16 * kh];
+      const int nks = (kf + 31) / 32;
+      v16i acc[LIMBS];
+#pragma unroll
+      for (int l = 0; l < LIMBS; ++l) acc[l] = (v16i){};
+      constexpr int GK = 2;
+      for (int k0 = 0; k0 < nks; k0 += GK) {
+        v4i a[GK], bb[GK][LIMBS];
+#pragma unroll
+        for (int g4 = 0; g4 < GK; ++g4) {
+          const bool in = k0 + g4 < nks;
+          a[g4] = (mrow < 16 && in) ? *reinterpret_cast<const v4i*>(as + 32 * (k0 + g4)) : (v4i){0, 0, 0, 0};
+#pragma unroll
+          for (int l = 0; l < LIMBS; ++l)
+            bb[g4][l] = (b_ok && in) ? *reinterpret_cast<const v4i*>(bp + l * p.plane + 32 * (k0 + g4))
+                                     : (v4i){0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < GK; ++g4)
+#pragma unroll
+          for (int l = 0; l < LIMBS; ++l)
+            acc[l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[g4], bb[g4][l], acc[l], 0, 0, 0);
+      }
+      const double es = b_ok ? p.escale[j0 + jn] : 0.0;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {  // result rows 8 (r/4) + 4 kh + r%4 < 16
+        double f = 0.0;
+#pragma unroll
+        for (int l = 0; l < LIMBS; ++l)
+          f = fma((double)acc[l][r], ldexp(1.0, 8 * (LIMBS - 1 - l)), f);
+        Bidle[(8 * (r >> 2) + 4 * kh + (r & 3)) * BW + jn] = f * es;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) fz[s] = Bidle[rloc * BW + l16 + 16 * s];
+    }
+    // this block's packed B has landed (issued during the previous block); the idle buffer is
+    // free once every wave has read the staging
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    double z[8], gin_v[8];
+    Guard g;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int j = l16 + 16 * s;
+      const bool in = active && j < w;
+      z[s] = in ? yv[s] * p.invc - gv[s] - fz[s] : 0.0;
+      g.bnd[s] = (in && gin) ? __double2float_ru((double)bsf[s] * S * LIMB_EPS * p.guard_scale) : 0.0f;
+    }
+    if (active && cnt > 0) {
+      // exact interference of the excess of large codes to the right (fp64); the list may have
+      // grown in this launch, so its entries are read past the L1 cache
+      const int cn = min(cnt, OCAP);
+      const long long* ol = reinterpret_cast<const long long*>(p.olist + row * OCAP);
+      for (int o = 0; o < cn; ++o) {
+        const long long raw = __hip_atomic_load(ol + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int ex = (int)(raw & 0xffffffffll), ey = (int)(raw >> 32);
+        const double f = p.invd[ex] * (double)ey;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int j = l16 + 16 * s;
+          if (j < w) z[s] -= p.U[(j0 + j) * p.ldu + ex] * f;
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) gin_v[s] = yv[s] * p.invc - z[s];
+    // the next block's operands are on the way while this block's steps run (issued after the
+    // loads above: the memory counter completes in order)
+    double yn[8], gn[8], bn[8];
+    if (b > 0) {
+      issue_pack(b - 1, Bidle);
+      load_ops(b - 1, yn, gn, bn);
+    }
+
+    // the lane's offset is made opaque here so that the block's LDS addresses are formed inside
+    // the loop (immediate offsets) instead of being hoisted into hundreds of live registers
+    int lb = l16;
+    asm volatile("" : "+v"(lb));
+    run_block(z, Bcur + lb);
+
+    if (gin) {  // uniform
+      // decisions inside the error bound: re-check one by one, re-derive the block if needed
+      if (tid == 0) {
+        n_hit = 0;
+        must_redo = 0;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (0.5 - fabs(z[s] - rint(z[s])) <= (double)g.bnd[s]) {
+          const int h = atomicAdd(&n_hit, 1);
+          if (h < HIT_CAP) {
+            hit_j[h] = l16 + 16 * s;
+            hit_r[h] = rloc;
+            hit_z[h] = z[s];
+            hit_g[h] = gin_v[s];
+          }
+        }
+      }
+      __syncthreads();
+      const int nh = n_hit;
+      if (tid == 0 && nh > 0) atomicAdd(p.flags + 2, nh);
+      if (nh > HIT_CAP) {
+        if (tid == 0) must_redo = 1;
+      } else {
+        for (int h = 0; h < nh; ++h) {
+          const int64_t rr = (int64_t)blockIdx.x * 16 + hit_r[h];
+          const double* ur = p.U + (j0 + hit_j[h]) * p.ldu;
+          const int32_t* qr = p.codes + rr * p.ldq;
+          double part = 0.0;
+#pragma unroll 4
+          for (int64_t k = kf0 + tid; k < p.n_in; k += 256)
+            part = fma(ur[k], (double)qr[k] * p.invd[k], part);
+          for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+          if (lane == 0) red[wave] = part;
+          __syncthreads();
+          if (tid == 0) {
+            const double dot = (red[0] + red[1]) + (red[2] + red[3]);
+            const double zx = hit_z[h] + (hit_g[h] - dot);
+            if (rint(zx) != rint(hit_z[h])) must_redo = 1;
+          }
+          __syncthreads();
+        }
+      }
+      __syncthreads();
+      if (must_redo) {
+        double acc[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc[s] = 0.0;
+        if (active) {
+          const int32_t* qrow = p.codes + row * p.ldq;
+          constexpr int CH = 4;
+          const int64_t kfull = kf0 + ((p.n_in - kf0) / CH) * CH;
+#pragma unroll 1
+          for (int64_t k = kf0; k < kfull; k += CH) {
+            double qk[CH];
+#pragma unroll
+            for (int e = 0; e < CH; ++e) qk[e] = (double)qrow[k + e] * p.invd[k + e];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+              const int j = l16 + 16 * s;
+              if (j < w) {
+                const double* ur = p.U + (j0 + j) * p.ldu + k;
+#pragma unroll
+                for (int e = 0; e < CH; ++e) acc[s] = fma(ur[e], qk[e], acc[s]);
+              }
+            }
+          }
+          for (int64_t k = kfull; k < p.n_in; ++k) {
+            const double q = (double)qrow[k] * p.invd[k];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+              const int j = l16 + 16 * s;
+              if (j < w) acc[s] = fma(p.U[(j0 + j) * p.ldu + k], q, acc[s]);
+            }
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int j = l16 + 16 * s;
+          z[s] = (active && j < w) ? yv[s] * p.invc - acc[s] : 0.0;
+        }
+        if (tid == 0) atomicAdd(p.flags + 1, 1);
+        run_block(z, Bcur + lb);
+      }
+    }
+
+    // outputs of the block
+    double asum = 0.0;
+    int nexc = 0;
+    int32_t qv[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int j = l16 + 16 * s;
+      qv[s] = 0;
+      if (active && j < w) {
+        const double q = rint(z[s]);
+        int32_t qi = 0;
+        if (q >= -2147483647.0 && q <= 2147483647.0) {
+          qi = (int32_t)q;
+        } else {
+          bad |= (z[s] == z[s]) ? FLAG_RANGE : FLAG_NONFINITE;
+        }
+        qv[s] = qi;
+        p.codes[row * p.ldq + j0 + j] = qi;
+        if (HAS_RESID) p.resid[row * p.ldr + j0 + j] = (float)((z[s] - q) * (p.c * p.invd[j0 + j]));
+        const int q8 = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
+        p.q8[row * p.ldq8 + j0 + j] = (int8_t)q8;
+        q8s[rloc][(int)(j0 - lo) + j] = (int8_t)q8;
+        asum += fabs(q);
+        nexc += (q8 != qi);
+      }
+    }
+    double tot = asum;
+    int ntot = nexc;
+    for (int m = 8; m >= 1; m >>= 1) {
+      tot += __shfl_xor(tot, m, 16);
+      ntot += __shfl_xor(ntot, m, 16);
+    }
+    int pre = nexc;
+    for (int d = 1; d < 16; d <<= 1) {
+      const int t = __shfl_up(pre, d, 16);
+      if (l16 >= d) pre += t;
+    }
+    pre -= nexc;
+    if (active && nexc) {
+      int idx = cnt + pre;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int j = l16 + 16 * s;
+        if (j < w) {
+          const int q8 = qv[s] > 127 ? 127 : (qv[s] < -127 ? -127 : qv[s]);
+          if (q8 != qv[s]) {
+            if (idx < OCAP)
+              p.olist[row * OCAP + idx] = make_int2((int)(j0 + j), qv[s] - q8);
+            else
+              bad |= FLAG_OVERFLOW_LIST;
+            ++idx;
+          }
+        }
+      }
+    }
+    S += tot;
+    cnt += ntot;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      yv[s] = yn[s];
+      gv[s] = gn[s];
+      bsf[s] = __double2float_ru(bn[s]);
+    }
+    // int8 codes in LDS and list entries visible to every wave; every wave done with this
+    // block's packed B before it becomes the idle buffer
+    __syncthreads();
+  };
+  for (int b = nb - 1; b >= 0; b -= 2) {
+    do_block(b, BsA, BsB);
+    if (b >= 1) do_block(b - 1, BsB, BsA);
+  }
+  if (active && l16 == 0) {
+    p.absq[row] = S;
+    p.ocnt[row] = cnt;
+  }
+  if (bad) atomicOr(p.flags, bad);
+}
+
 // Packed diagonal blocks of B = U diag(1/U_jj): one block per 128 columns.
 __global__ void k_pack_blocks(const double* __restrict__ U, int64_t ldu, int64_t n,
                               const double* __restrict__ invd, double* __restrict__ Bpk) {
@@ -548,6 +893,29 @@ int launch_sic_leaf(const LeafArgs& a, bool i8, hipStream_t st) {
     else WSIC_LEAF(false, false, false, false);
   }
 #undef WSIC_LEAF
+  return WSIC_OK;
+}
+
+int launch_sic_super(const LeafArgs& a, hipStream_t st) {
+  if (a.w <= 0 || a.w > SUP_W || a.j0 % BW != 0 || !a.q8 || !a.absq || !a.ocnt || !a.olist || !a.U ||
+      !a.bscale || !a.D || !a.escale || (a.ldd % 16) != 0 || (a.ldq8 % 16) != 0) {
+    set_error("internal: super-block launch at %lld width %d", (long long)a.j0, a.w);
+    return WSIC_E_INVAL;
+  }
+  LeafArgs p = a;
+  p.invc = 1.0 / a.c;
+  const unsigned blocks = (unsigned)((a.n_out + 15) / 16);
+  const double work = (double)a.n_out * a.w *
+                      (8.0 + (a.G ? 8.0 : 0.0) + 4.0 + (a.resid ? 4.0 : 0.0) + 1.0);
+  const bool hg = a.G != nullptr, hr = a.resid != nullptr;
+  if (hg && hr)
+    WSIC_LAUNCH("sic_leaf", work, st, (k_sic_super<true, true>), dim3(blocks), dim3(256), 0, p);
+  else if (hg)
+    WSIC_LAUNCH("sic_leaf", work, st, (k_sic_super<true, false>), dim3(blocks), dim3(256), 0, p);
+  else if (hr)
+    WSIC_LAUNCH("sic_leaf", work, st, (k_sic_super<false, true>), dim3(blocks), dim3(256), 0, p);
+  else
+    WSIC_LAUNCH("sic_leaf", work, st, (k_sic_super<false, false>), dim3(blocks), dim3(256), 0, p);
   return WSIC_OK;
 }
 

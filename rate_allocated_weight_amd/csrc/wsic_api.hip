@@ -364,12 +364,14 @@ struct SicCtx {
   hipStream_t st;
   bool i8;             // interference by the exact int8 limb product (else fp64 MFMA)
   double guard_scale;  // multiplies the error bound (testing hook; 1 in normal use)
+  bool super_launch;   // int8 mode: a range of up to SUPER blocks in one launch (else per block)
 };
 
 SicCtx make_ctx(int64_t n_out, int64_t n_in, const void* W, int dtype, int64_t ldw,
                 const double* U, int64_t ldu, const SicWs& ws, hipStream_t st) {
-  SicCtx x{n_out, n_in, W, dtype, ldw, U, ldu, ws, st, true, 1.0};
+  SicCtx x{n_out, n_in, W, dtype, ldw, U, ldu, ws, st, true, 1.0, true};
   if (const char* e = std::getenv("WSIC_FP64_TRAIL")) x.i8 = (e[0] == '0');
+  if (const char* e = std::getenv("WSIC_SUPER_BLOCKS")) x.super_launch = (e[0] != '0');
   if (const char* e = std::getenv("WSIC_GUARD_SCALE")) {
     const double v = std::atof(e);
     if (v > 0.0) x.guard_scale = v;
@@ -400,8 +402,9 @@ int sic_setup(const SicCtx& x, bool read_now = true) {
 
 // Columns [lo, hi): G[:, lo:hi] holds the interference of every column >= hi (none when
 // hi == n_in). Right half first, then its interference on the left half, then the left half.
-// With the int8 product, a range of at most SUPER blocks is finished leaf by leaf, right to left,
-// each leaf forming the interference of the columns between it and hi itself.
+// With the int8 product, a range of at most SUPER blocks is finished right to left by one
+// launch that forms the interference of the range's finished columns itself (or, per block,
+// by one leaf launch each when super_launch is off).
 constexpr int64_t SUPER = 4;
 
 int sic_leaf_at(const SicCtx& x, int64_t j0, int64_t wb, int64_t hi, double c, int32_t* codes,
@@ -448,6 +451,39 @@ int sic_range(const SicCtx& x, int64_t lo, int64_t hi, double c, int32_t* codes,
               float* resid, int64_t ldr) {
   const int64_t w = hi - lo;
   const bool has_g = hi < x.n_in;
+  if (x.i8 && w <= SUPER * BW && x.super_launch) {
+    LeafArgs a{};
+    a.n_out = x.n_out;
+    a.n_in = x.n_in;
+    a.j0 = lo;
+    a.w = (int)w;
+    a.Y = x.ws.Y;
+    a.ldy = x.n_in;
+    a.G = has_g ? x.ws.G : nullptr;
+    a.ldg = x.n_in;
+    a.Bpk = x.ws.Bpk;
+    a.invd = x.ws.invd;
+    a.c = c;
+    a.codes = codes;
+    a.ldq = ldq;
+    a.resid = resid;
+    a.ldr = ldr;
+    a.flags = x.ws.pflags;
+    a.U = x.U;
+    a.ldu = x.ldu;
+    a.bscale = x.ws.bscale;
+    a.guard_scale = x.guard_scale;
+    a.q8 = x.ws.q8;
+    a.ldq8 = ld_i8(x.n_in);
+    a.absq = x.ws.absq;
+    a.ocnt = x.ws.ocnt;
+    a.olist = x.ws.olist;
+    a.D = x.ws.D;
+    a.ldd = ld_i8(x.n_in);
+    a.plane = x.n_in * a.ldd;
+    a.escale = x.ws.escale;
+    return launch_sic_super(a, x.st);
+  }
   if (x.i8 && w <= SUPER * BW) {
     const int64_t nb = (w + BW - 1) / BW;
     for (int64_t b = nb - 1; b >= 0; --b) {

@@ -317,7 +317,8 @@ def test_bad_factor_diagonal_is_reported(device):
 
 # ------------------------------------------------------------------ interference product variants
 @pytest.mark.parametrize("env", [{"WSIC_FP64_TRAIL": "1"}, {"WSIC_GUARD_SCALE": "1e300"},
-                                 {"WSIC_GUARD_SCALE": "3e4"}])
+                                 {"WSIC_GUARD_SCALE": "3e4"}, {"WSIC_SUPER_BLOCKS": "0"},
+                                 {"WSIC_SUPER_BLOCKS": "0", "WSIC_GUARD_SCALE": "3e4"}])
 @pytest.mark.parametrize("name", ["spiked_300x333", "blockar1_77x520"])
 def test_sic_parity_product_variants(device, monkeypatch, env, name):
     """fp64 MFMA interference, and the int8 product with every decision re-derived exactly in
