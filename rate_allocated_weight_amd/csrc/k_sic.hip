@@ -399,6 +399,8 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
 // and list counts stay in registers across the blocks.
 constexpr int SUP_BLOCKS = 4;  // matches the recursion's super-block width
 constexpr int SUP_W = SUP_BLOCKS * BW;
+constexpr int SUP_RING = 4;  // 4 KiB units of the fused product in flight per wave
+static_assert(4 * SUP_RING * 4096 <= PACK * 8, "product rings fit the idle buffer");
 constexpr int PACK_DMA = PACK * 8 / 1024 / 4;  // 16-byte direct LDS loads per wave per block
 static_assert(PACK_DMA * 4 * 1024 == PACK * 8, "packed block is a whole number of 1 KiB rounds");
 
@@ -484,30 +486,79 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
       const int mrow = lane & 31, kh = lane >> 5;
       const int jn = 32 * wave + (lane & 31);
       const bool b_ok = jn < w;
-      const int8_t* bp = p.D + (j0 + (b_ok ? jn : 0)) * p.ldd + kf0 + 16 * kh;
       const int8_t* as = &q8s[mrow & 15][(int)(kf0 - lo) + 16 * kh];
-      const int nks = (kf + 31) / 32;
+      // The digit planes stream through a per-wave ring of SUP_RING units in the idle buffer; a
+      // unit is one plane over 4 k-steps: 32 rows x 128 bytes, fetched as whole cache lines (8
+      // lanes per row) by 4 direct loads. Chunk c of row r sits at 16-byte slot 8 r + (c ^ r%8),
+      // so an MFMA operand read (32 rows, one chunk) touches every LDS bank once.
+      const int nq = (kf + 127) / 128;  // k-quads (rows are zero-padded to whole lines)
+      const int nu = nq * LIMBS;
+      char* ring = reinterpret_cast<char*>(Bidle) + wave * (SUP_RING * 4096);
+      // (a block with finished columns to its right in the range is a whole 128 columns wide)
+      const int8_t* brow = p.D + (j0 + 32 * wave) * p.ldd + kf0;
+      auto issue_u = [&](int u) {
+        const int q = u / LIMBS, l = u - q * LIMBS;
+        char* slot = ring + (u % SUP_RING) * 4096;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 8 * i + (lane >> 3);
+          const int c = (lane & 7) ^ (r & 7);
+          pipe::dma16(brow + l * p.plane + r * p.ldd + 128 * q + 16 * c, slot + 1024 * i);
+        }
+      };
+      // this lane's operand slots for the 4 k-steps of a unit (row mrow, chunk 2 t + kh)
+      unsigned ro[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ro[t] = 16u * (8 * mrow + ((2 * t + kh) ^ (mrow & 7)));
       v16i acc[LIMBS];
 #pragma unroll
       for (int l = 0; l < LIMBS; ++l) acc[l] = (v16i){};
-      constexpr int GK = 2;
-      for (int k0 = 0; k0 < nks; k0 += GK) {
-        v4i a[GK], bb[GK][LIMBS];
 #pragma unroll
-        for (int g4 = 0; g4 < GK; ++g4) {
-          const bool in = k0 + g4 < nks;
-          a[g4] = (mrow < 16 && in) ? *reinterpret_cast<const v4i*>(as + 32 * (k0 + g4)) : (v4i){0, 0, 0, 0};
+      for (int u = 0; u < SUP_RING; ++u)
+        if (u < nu) issue_u(u);
+#pragma unroll 1
+      for (int q = 0; q < nq; ++q) {
+        // this quad's A operands (the workgroup's codes; rows 16-31 of the fragment are zero),
+        // read in assembly for the same reason as the ring below
+        v4i a[4];
+        const unsigned sa = (unsigned)reinterpret_cast<uintptr_t>((const pipe::lds_char*)(as + 128 * q));
+        asm volatile(
+            "ds_read_b128 %0, %4\n\t"
+            "ds_read_b128 %1, %4 offset:32\n\t"
+            "ds_read_b128 %2, %4 offset:64\n\t"
+            "ds_read_b128 %3, %4 offset:96\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+            : "v"(sa)
+            : "memory");
 #pragma unroll
-          for (int l = 0; l < LIMBS; ++l)
-            bb[g4][l] = (b_ok && in) ? *reinterpret_cast<const v4i*>(bp + l * p.plane + 32 * (k0 + g4))
-                                     : (v4i){0, 0, 0, 0};
+        for (int t = 0; t < 4; ++t)
+          if (mrow >= 16) a[t] = (v4i){0, 0, 0, 0};
+#pragma unroll
+        for (int l = 0; l < LIMBS; ++l) {
+          const int u = q * LIMBS + l;
+          pipe::wait_ahead<4, SUP_RING - 1>(min(nu - 1 - u, SUP_RING - 1));
+          // read in assembly with its wait inside: the compiler would otherwise order every
+          // read of this buffer behind all direct loads in flight
+          const unsigned sb =
+              (unsigned)reinterpret_cast<uintptr_t>((const pipe::lds_char*)(ring + (u % SUP_RING) * 4096));
+          v4i bb[4];
+          asm volatile(
+              "ds_read_b128 %0, %4\n\t"
+              "ds_read_b128 %1, %5\n\t"
+              "ds_read_b128 %2, %6\n\t"
+              "ds_read_b128 %3, %7\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(bb[0]), "=&v"(bb[1]), "=&v"(bb[2]), "=&v"(bb[3])
+              : "v"(sb + ro[0]), "v"(sb + ro[1]), "v"(sb + ro[2]), "v"(sb + ro[3])
+              : "memory");
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc[l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t], bb[t], acc[l], 0, 0, 0);
+          if (u + SUP_RING < nu) issue_u(u + SUP_RING);  // the slot's operands are in registers
         }
-#pragma unroll
-        for (int g4 = 0; g4 < GK; ++g4)
-#pragma unroll
-          for (int l = 0; l < LIMBS; ++l)
-            acc[l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[g4], bb[g4][l], acc[l], 0, 0, 0);
       }
+      pipe::barrier_lds();  // every wave done with its ring before the staging overwrites it
       const double es = b_ok ? p.escale[j0 + jn] : 0.0;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {  // result rows 8 (r/4) + 4 kh + r%4 < 16
@@ -717,9 +768,11 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
       gv[s] = gn[s];
       bsf[s] = __double2float_ru(bn[s]);
     }
-    // int8 codes in LDS and list entries visible to every wave; every wave done with this
-    // block's packed B before it becomes the idle buffer
-    __syncthreads();
+    // int8 codes in LDS visible to every wave; every wave done with this block's packed B
+    // before it becomes the idle buffer. (Global stores are not waited for here: the next
+    // block's reads of codes by other waves come after a fenced barrier, and a wave's own
+    // excess entries are read after its wait for the packed B.)
+    pipe::barrier_lds();
   };
   for (int b = nb - 1; b >= 0; b -= 2) {
     do_block(b, BsA, BsB);

@@ -11,6 +11,7 @@ namespace wsic {
 namespace pipe {
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const char lds_char;
 
 // Workgroup barrier without the memory fence of __syncthreads(): that fence would also wait
 // for every operand load still in flight. This wave's LDS traffic is drained first; the DMA

@@ -110,7 +110,9 @@ struct Carve {
 };
 
 // int8 operand rows: padded to 64 bytes, padding kept zero
-inline int64_t ld_i8(int64_t n_in) { return (n_in + 63) / 64 * 64; }
+// int8 rows are padded to whole 128-byte lines (zeros): the products read whole K-steps, and the
+// super-block product fetches whole lines
+inline int64_t ld_i8(int64_t n_in) { return (n_in + 127) / 128 * 128; }
 
 struct SicWs {
   int* flags;       // setup checks
