@@ -85,15 +85,15 @@ __global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int
       // Branch-free elimination: the published row k is zero left of the diagonal, so rows above
       // the pivot get a zero multiplier and keep their values, and no upper entry is touched by
       // a column left of the pivot; the pivot row itself is then overwritten with its scaled
-      // entries.
+      // entries. U(k,i) U(k,j) = row_k(i) * (U(k,j) / sqrt(p)): one multiplier per column.
+      const double mj = sj * inv, mx = xk * inv;
       double rr[RPW];
 #pragma unroll
       for (int s = 0; s < RPW; ++s) rr[s] = row[pb][RPW * w + s];
 #pragma unroll
       for (int s = 0; s < RPW; ++s) {
-        const double uki = rr[s] * inv;  // U(k, i) for i > k
-        a[s] = fma(-uki, sj, a[s]);
-        sl[s] = fma(-uki, xk, sl[s]);
+        a[s] = fma(-rr[s], mj, a[s]);
+        sl[s] = fma(-rr[s], mx, sl[s]);
       }
       const bool own = (w == wk);
       a[sk] = own ? ((j == k) ? p * inv : sj) : a[sk];

@@ -607,7 +607,19 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
     // the next block's operands are on the way while this block's steps run (issued after the
     // loads above: the memory counter completes in order)
     double yn[8], gn[8], bn[8];
+    int pf = 0;  // touched digit-plane words (consumed below, never used)
     if (b > 0) {
+      // Warm the L2 with the digit planes the next block's product reads (rows j0 - 128 .. j0 - 1,
+      // bytes [j0, hi) of each, every plane): each 128-byte line is touched by one thread of
+      // the workgroups that share an L2 (workgroups are dealt to the 8 XCDs round-robin).
+      const int nlr = (int)((hi - j0 + 127) / 128);  // lines per row and plane
+      const int nl = LIMBS * BW * nlr;
+      const int per_xcd = (int)((gridDim.x + 7 - (blockIdx.x & 7)) / 8);
+      for (int i = (int)(blockIdx.x >> 3) * 256 + tid; i < nl; i += per_xcd * 256) {
+        const int l = i / (BW * nlr), rem = i - l * (BW * nlr);
+        const int r = rem / nlr, c = rem - r * nlr;
+        pf ^= *reinterpret_cast<const int*>(p.D + l * p.plane + (j0 - BW + r) * p.ldd + j0 + 128 * c);
+      }
       issue_pack(b - 1, Bidle);
       load_ops(b - 1, yn, gn, bn);
     }
@@ -705,6 +717,7 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
       }
     }
 
+    asm volatile("" ::"v"(pf));  // the warming loads have long landed here
     // outputs of the block
     double asum = 0.0;
     int nexc = 0;
