@@ -41,7 +41,7 @@ FAMILIES = {
     "gemm_trail": ("mfma", "mfma_f64", 1e-12),
     "gemm_y": ("mfma", "mfma_f64", 1e-12),
     "gemm_chol": ("mfma", "mfma_f64", 1e-12),
-    "chol_update": ("mfma", "mfma_f64", 1e-12),
+    "chol_step": ("mfma", "mfma_f64", 1e-12),
     "potrf_panel": ("alu", "valu_f64", 1e-12),
     "gemm_dist": ("mfma", "mfma_f64", 1e-12),
     "syrk_bf16": ("mfma", "mfma_bf16", 1e-12),

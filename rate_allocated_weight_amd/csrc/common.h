@@ -121,11 +121,11 @@ int launch_diag_check(const double* S, int64_t n, int64_t lds, int* flags, hipSt
 int launch_potrf_panel(double* A, int64_t lda, int64_t kb, int nbk, int64_t n, int64_t* info,
                        hipStream_t st);
 int launch_zero_lower(double* A, int64_t n, int64_t lda, hipStream_t st);
-// A[c0.., c0..] (m x m, upper tiles) -= X^T X with X = rows r0 .. r0+kr-1 at columns c0 ..
-// (kr = 64); chol_update_ok tells whether its alignment preconditions hold
-bool chol_update_ok(const double* A, int64_t lda, int64_t c0, int kr);
-int launch_chol_update(double* A, int64_t lda, int64_t r0, int64_t c0, int64_t m, int kr,
-                       const int64_t* info, hipStream_t st);
+// One 64-column step after the panel at kb: A[c0.., c0..] (upper tiles, c0 = kb + 64) -= X^T X
+// with X the solved block row, fused with the panel at c0; chol_step_ok tells whether its
+// alignment preconditions hold
+bool chol_step_ok(const double* A, int64_t lda, int64_t c0);
+int launch_chol_step(double* A, int64_t lda, int64_t kb, int64_t n, int64_t* info, hipStream_t st);
 
 // SIC
 int launch_prep(const double* U, int64_t ldu, int64_t n, double* invd, int* flags, hipStream_t st);

@@ -7,14 +7,16 @@
 //                   instructions on the same data, so every copy of U_kk is bitwise identical)
 //                   and applies each pivot's elimination to its slab as it goes, which is the
 //                   triangular solve X = U_kk^-T A_k,rest. Thread (wave w, lane j) holds rows
-//                   16w .. 16w+15 of column j of the diagonal block and of its slab. At pivot k
+//                   8w .. 8w+7 of column j of the diagonal block and of its slab. At pivot k
 //                   the owning wave publishes row k of both through LDS; every thread reads the
-//                   pivot and the 16 row entries it needs with all loads in flight and scales
+//                   pivot and the 8 row entries it needs with all loads in flight and scales
 //                   by 1/sqrt(p). The update has no branches (rows above the pivot meet a zero
 //                   multiplier); the pivot row buffers alternate with the parity of k, so one
 //                   barrier per pivot suffices. Nothing is written to global memory inside the
 //                   pivot loop.
-//   trailing      : A_rest,rest -= X^T X on upper tiles (fp64 MFMA GEMM, k-major operands)
+//   trailing      : A_rest,rest -= X^T X on upper tiles (fp64 MFMA GEMM, k-major operands).
+//                   k_chol_step launches it together with the next panel, whose workgroups
+//                   first apply the update to the next block row themselves.
 // The first failing pivot (1-based, global) is recorded in *info; later steps see it and
 // return immediately.
 #include "common.h"
@@ -23,7 +25,8 @@ namespace wsic {
 namespace {
 
 constexpr int NB = 64;
-constexpr int RPW = NB / 4;  // rows per wave
+constexpr int PANEL_WAVES = 8;
+constexpr int RPW = NB / PANEL_WAVES;  // rows per wave
 
 // 1/sqrt(p) to ~1 ulp: hardware estimate refined by two Newton steps
 __device__ __forceinline__ double rsqrt_f64(double p) {
@@ -34,29 +37,17 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
   return y;
 }
 
-__global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int64_t kb, int nbk,
-                                                     int64_t n, int64_t* info) {
-  // raw row k of the diagonal block and of this workgroup's slab, double-buffered by the parity
-  // of k so that one barrier per pivot separates its writes from the previous pivot's reads
-  __shared__ double row[2][NB];
-  __shared__ double srow[2][NB];
-  if (*info != 0) return;
+// The pivot loop of one panel workgroup and its stores. a[s], sl[s] hold rows RPW w + s of
+// column j of the diagonal block and of this workgroup's slab (block b > 0), as loaded.
+__device__ __forceinline__ void panel_factor(double (&a)[RPW], double (&sl)[RPW], double* A,
+                                             int64_t lda, int64_t kb, int nbk, int64_t n,
+                                             int64_t* info, int b, double (*row)[NB],
+                                             double (*srow)[NB]) {
   const int j = threadIdx.x & 63;
-  // the wave index, known to the compiler as wave-uniform
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = blockIdx.x;
   const int64_t c = kb + (int64_t)b * NB + j;  // slab column (b > 0)
-  const bool has_slab = b > 0;
-  const bool cin = has_slab && c < n;
-
-  double a[RPW], sl[RPW];  // rows 16 w + s of column j: diagonal block, slab
-#pragma unroll
-  for (int s = 0; s < RPW; ++s) {
-    const int i = RPW * w + s;
-    a[s] = (i <= j && j < nbk) ? A[(kb + i) * lda + kb + j] : (i == j ? 1.0 : 0.0);
-    sl[s] = (cin && i < nbk) ? A[(kb + i) * lda + c] : 0.0;
-  }
-  // pivots in four groups of RPW: the group loop stays a loop (code size: the instruction cache
+  const bool cin = b > 0 && c < n;
+  // pivots in groups of RPW: the group loop stays a loop (code size: the instruction cache
   // holds one group), the RPW pivots of a group are unrolled so register indices are constants
 #pragma unroll 1
   for (int wk = 0; wk < NB / RPW; ++wk) {
@@ -114,14 +105,35 @@ __global__ __launch_bounds__(256) void k_potrf_panel(double* A, int64_t lda, int
   }
 }
 
-// Trailing update A22 -= X^T X after a block row: X = rows r0 .. r0+KR-1 of A at columns
-// c0 .. c0+m-1 (the solved block row), A22 = A[c0.., c0..] (m x m), upper tiles only.
-// One 256-thread workgroup per 64 x 64 upper tile (tiles enumerated triangularly): the C tile is
-// loaded into registers first, then the KR x 64 column strips of X for the tile's rows and
-// columns go global -> LDS directly (global_load_lds_dwordx4, lane l of an instruction at byte
-// 16 l) in their natural layout, [k][col], which is already the conflict-free layout of the
-// v_mfma_f64_16x16x4 operands (16 lanes read 16 consecutive doubles of one k row). Diagonal
-// tiles load one strip. 4 waves in 2 x 2, each 32 x 32 = 2 x 2 fragments.
+__global__ __launch_bounds__(64 * PANEL_WAVES) void k_potrf_panel(double* A, int64_t lda, int64_t kb,
+                                                                 int nbk, int64_t n, int64_t* info) {
+  // raw row k of the diagonal block and of this workgroup's slab, double-buffered by the parity
+  // of k so that one barrier per pivot separates its writes from the previous pivot's reads
+  __shared__ double row[2][NB];
+  __shared__ double srow[2][NB];
+  if (*info != 0) return;
+  const int j = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.x;
+  const int64_t c = kb + (int64_t)b * NB + j;
+  const bool cin = b > 0 && c < n;
+  double a[RPW], sl[RPW];
+#pragma unroll
+  for (int s = 0; s < RPW; ++s) {
+    const int i = RPW * w + s;
+    a[s] = (i <= j && j < nbk) ? A[(kb + i) * lda + kb + j] : (i == j ? 1.0 : 0.0);
+    sl[s] = (cin && i < nbk) ? A[(kb + i) * lda + c] : 0.0;
+  }
+  panel_factor(a, sl, A, lda, kb, nbk, n, info, b, row, srow);
+}
+
+// Trailing update A22 -= X^T X after a block row: X = rows r0 .. r0+63 of A at columns
+// c0 .. c0+m-1 (the solved block row), A22 = A[c0.., c0..] (m x m), upper 64 x 64 tiles only.
+// A tile's C values are loaded into registers first, then the 64 x 64 column strips of X for
+// its rows and columns go global -> LDS directly (global_load_lds_dwordx4, lane l of an
+// instruction at byte 16 l) in their natural layout, [k][col], which is already the
+// conflict-free layout of the v_mfma_f64_16x16x4 operands (16 lanes read 16 consecutive doubles
+// of one k row). Diagonal tiles load one strip. 8 waves in 2 x 4, each 32 x 16 = two fragments.
 // Requirements (checked by the launcher): A 16-byte aligned, lda even, c0 even.
 namespace cupd {
 constexpr int T = 64;
@@ -129,90 +141,138 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef double d4 __attribute__((ext_vector_type(4)));
 }  // namespace cupd
 
-template <int KR>
-__global__ __launch_bounds__(256) void k_chol_update(double* A, int64_t lda, int64_t r0, int64_t c0,
-                                                     int64_t m, const int64_t* info) {
-  using namespace cupd;
-  __shared__ __attribute__((aligned(1024))) double Xs[2][KR][T];
-  if (*info != 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // triangular tile index: bid -> (tm <= tn)
-  const int64_t bid = blockIdx.x;
-  int64_t tn = (int64_t)((sqrt(8.0 * (double)bid + 1.0) - 1.0) * 0.5);
-  while ((tn + 1) * (tn + 2) / 2 <= bid) ++tn;
-  while (tn * (tn + 1) / 2 > bid) --tn;
-  const int64_t tm = bid - tn * (tn + 1) / 2;
-  const int64_t i0 = tm * T, j0 = tn * T;
-  const bool diag = (tm == tn);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 15, lk = lane >> 4;
-
-  // C tile of this lane (result layout), loaded first
-  double cold[2][2][4];
+// strip of X: rows r0 .. r0+63 (k) x columns col0 .. col0+63 of A22, as [k][col] in LDS;
+// columns past m repeat the last whole chunk (their results are never stored)
+__device__ __forceinline__ void load_strip(const double* A, int64_t lda, int64_t r0, int64_t c0,
+                                           int64_t m, int64_t col0, double* dst) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t clast = (m - 1) & ~(int64_t)1;
+  // 64 rows x 32 chunks of 16 bytes = 32 instructions, 4 per wave
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t ii = i0 + wm * 32 + i * 16 + lk + 4 * r;
-        const int64_t jj = j0 + wn * 32 + j * 16 + lr;
-        cold[i][j][r] = (ii < m && jj < m) ? A[(c0 + ii) * lda + c0 + jj] : 0.0;
-      }
-
-  // strips: KR rows x 64 columns = KR * 32 chunks of 16 bytes, KR / 2 instructions per strip
-  constexpr int INS = KR / 2 / 4;  // per wave per strip
-  const int64_t clast = (m - 1) & ~(int64_t)1;  // last chunk start inside the row
-#pragma unroll
-  for (int sidx = 0; sidx < 2; ++sidx) {
-    if (sidx == 1 && diag) break;  // uniform
-    const int64_t col0 = (sidx == 0) ? i0 : j0;
-#pragma unroll
-    for (int h = 0; h < INS; ++h) {
-      const int ins = INS * wave + h;
-      const int p = 64 * ins + lane;
-      const int t = p >> 5, ch = p & 31;
-      int64_t cc = col0 + 2 * ch;
-      cc = cc < clast ? cc : clast;
-      __builtin_amdgcn_global_load_lds((const void*)(A + (r0 + t) * lda + c0 + cc),
-                                       (lds_void*)(&Xs[sidx][0][0] + 128 * ins), 16, 0, 0);
-    }
+  for (int h = 0; h < 4; ++h) {
+    const int ins = 4 * w + h;
+    const int p = 64 * ins + lane;
+    const int t = p >> 5, ch = p & 31;
+    int64_t cc = col0 + 2 * ch;
+    cc = cc < clast ? cc : clast;
+    __builtin_amdgcn_global_load_lds((const void*)(A + (r0 + t) * lda + c0 + cc),
+                                     (cupd::lds_void*)(dst + 128 * ins), 16, 0, 0);
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+}
 
-  const double(*Xa)[T] = Xs[0];
-  const double(*Xb)[T] = diag ? Xs[0] : Xs[1];
-  d4 acc[2][2];
+// this wave's part of Xa^T Xb for one tile: rows 32 wm + 16 i + lk + 4 r, column 16 wn + lr
+__device__ __forceinline__ void tile_mfma(const double (*Xa)[cupd::T], const double (*Xb)[cupd::T],
+                                          cupd::d4 (&acc)[2]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 2, wn = w & 3, lr = lane & 15, lk = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) acc[i] = (cupd::d4){0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = (d4){0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-  for (int k4 = 0; k4 < KR / 4; ++k4) {
+  for (int k4 = 0; k4 < cupd::T / 4; ++k4) {
     const int k = 4 * k4 + lk;
-    double a[2], b[2];
+    const double bv = Xb[k][wn * 16 + lr];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = Xa[k][wm * 32 + i * 16 + lr];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = Xb[k][wn * 32 + j * 16 + lr];
+    for (int i = 0; i < 2; ++i)
+      acc[i] = __builtin_amdgcn_mfma_f64_16x16x4f64(Xa[k][wm * 32 + i * 16 + lr], bv, acc[i], 0, 0, 0);
+  }
+}
+
+// One step of the right-looking loop in one launch. X is the solved block row [kb, kb+64),
+// A22 = A[c0.., c0..] with c0 = kb + 64 and m = n - c0.
+//   workgroups 0 .. t-1 (t = ceil(m/64)): the next panel. Workgroup b first applies this step's
+//     update to tiles (0, 0) and (0, b) of A22 (the next diagonal block and its slab), passes
+//     them through LDS into the pivot layout and factors exactly as k_potrf_panel does;
+//   the others: the update of the tiles (tm, tn), 1 <= tm <= tn.
+// The next panel needs only the first tile row of this update, so its pivot chain runs beside
+// the bulk of the update instead of after it.
+__global__ __launch_bounds__(64 * PANEL_WAVES) void k_chol_step(double* A, int64_t lda, int64_t kb,
+                                                               int64_t n, int npanel,
+                                                               int64_t* info) {
+  using namespace cupd;
+  static_assert(PANEL_WAVES == 8, "tile layout: 8 waves in 2 x 4");
+  __shared__ __attribute__((aligned(1024))) double Xs[2][T][T];
+  __shared__ double row[2][NB];
+  __shared__ double srow[2][NB];
+  if (*info != 0) return;
+  const int64_t c0 = kb + NB, m = n - c0;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w >> 2, wn = w & 3, lr = lane & 15, lk = lane >> 4;
+  const int bid = blockIdx.x;
+
+  if (bid < npanel) {
+    const int b = bid;
+    const int64_t j0 = (int64_t)b * T;
+    double cd[2][4], cs[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int r = 0; r < 4; ++r) {
+        const int64_t ii = wm * 32 + i * 16 + lk + 4 * r, jj = wn * 16 + lr;
+        cd[i][r] = (ii < m && jj < m) ? A[(c0 + ii) * lda + c0 + jj] : 0.0;
+        cs[i][r] = (b > 0 && ii < m && j0 + jj < m) ? A[(c0 + ii) * lda + c0 + j0 + jj] : 0.0;
+      }
+    load_strip(A, lda, kb, c0, m, 0, &Xs[0][0][0]);
+    if (b > 0) load_strip(A, lda, kb, c0, m, j0, &Xs[1][0][0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    d4 ad[2], as[2];
+    tile_mfma(Xs[0], Xs[0], ad);
+    if (b > 0) tile_mfma(Xs[0], Xs[1], as);
+    __syncthreads();  // every wave done with the strips
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ii = wm * 32 + i * 16 + lk + 4 * r, jj = wn * 16 + lr;
+        Xs[0][ii][jj] = cd[i][r] - ad[i][r];
+        if (b > 0) Xs[1][ii][jj] = cs[i][r] - as[i][r];
+      }
+    __syncthreads();
+    const int nbk = (int)(m < NB ? m : NB);
+    const int j = lane;
+    const bool cin = b > 0 && c0 + j0 + j < n;
+    double a[RPW], sl[RPW];
+#pragma unroll
+    for (int s = 0; s < RPW; ++s) {
+      const int i = RPW * w + s;
+      a[s] = (i <= j && j < nbk) ? Xs[0][i][j] : (i == j ? 1.0 : 0.0);
+      sl[s] = (cin && i < nbk) ? Xs[1][i][j] : 0.0;
+    }
+    panel_factor(a, sl, A, lda, c0, nbk, n, info, b, row, srow);
+    return;
   }
 
+  // update tile (tm, tn), 1 <= tm <= tn: triangular index over the tiles below the first row
+  const int64_t u = bid - npanel;
+  int64_t tn = (int64_t)((sqrt(8.0 * (double)u + 1.0) - 1.0) * 0.5);
+  while ((tn + 1) * (tn + 2) / 2 <= u) ++tn;
+  while (tn * (tn + 1) / 2 > u) --tn;
+  const int64_t tm = u - tn * (tn + 1) / 2 + 1;
+  ++tn;
+  const int64_t i0 = tm * T, j0 = tn * T;
+  const bool diag = (tm == tn);
+  double cold[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int r = 0; r < 4; ++r) {
+      const int64_t ii = i0 + wm * 32 + i * 16 + lk + 4 * r, jj = j0 + wn * 16 + lr;
+      cold[i][r] = (ii < m && jj < m) ? A[(c0 + ii) * lda + c0 + jj] : 0.0;
+    }
+  load_strip(A, lda, kb, c0, m, i0, &Xs[0][0][0]);
+  if (!diag) load_strip(A, lda, kb, c0, m, j0, &Xs[1][0][0]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  d4 acc[2];
+  tile_mfma(Xs[0], diag ? Xs[0] : Xs[1], acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t ii = i0 + wm * 32 + i * 16 + lk + 4 * r;
-        const int64_t jj = j0 + wn * 32 + j * 16 + lr;
-        if (ii < m && jj < m) A[(c0 + ii) * lda + c0 + jj] = cold[i][j][r] - acc[i][j][r];
-      }
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t ii = i0 + wm * 32 + i * 16 + lk + 4 * r, jj = j0 + wn * 16 + lr;
+      if (ii < m && jj < m) A[(c0 + ii) * lda + c0 + jj] = cold[i][r] - acc[i][r];
+    }
 }
 
 __global__ void k_zero_lower(double* A, int64_t n, int64_t lda) {
@@ -235,27 +295,28 @@ int launch_potrf_panel(double* A, int64_t lda, int64_t kb, int nbk, int64_t n, i
   const int64_t m = n - kb - nbk;  // columns right of the diagonal block
   const unsigned blocks = 1 + (unsigned)((m + NB - 1) / NB);
   const double work = (double)nbk * nbk * nbk / 3.0 + (double)nbk * nbk * m;
-  WSIC_LAUNCH("potrf_panel", work, st, k_potrf_panel, dim3(blocks), dim3(256), 0, A, lda, kb, nbk, n,
+  WSIC_LAUNCH("potrf_panel", work, st, k_potrf_panel, dim3(blocks), dim3(64 * PANEL_WAVES), 0, A, lda, kb, nbk, n,
               info);
   return WSIC_OK;
 }
 
-bool chol_update_ok(const double* A, int64_t lda, int64_t c0, int kr) {
-  return kr == NB && (((uintptr_t)A) & 15) == 0 && (lda % 2) == 0 && (c0 % 2) == 0;
+bool chol_step_ok(const double* A, int64_t lda, int64_t c0) {
+  return (((uintptr_t)A) & 15) == 0 && (lda % 2) == 0 && (c0 % 2) == 0;
 }
 
-int launch_chol_update(double* A, int64_t lda, int64_t r0, int64_t c0, int64_t m, int kr,
-                       const int64_t* info, hipStream_t st) {
-  if (m <= 0) return WSIC_OK;
-  if (!chol_update_ok(A, lda, c0, kr)) {
-    set_error("internal: chol update preconditions");
+int launch_chol_step(double* A, int64_t lda, int64_t kb, int64_t n, int64_t* info,
+                     hipStream_t st) {
+  const int64_t c0 = kb + NB, m = n - c0;
+  if (m <= 0 || !chol_step_ok(A, lda, c0)) {
+    set_error("internal: cholesky step preconditions");
     return WSIC_E_INVAL;
   }
-  const int64_t t = (m + cupd::T - 1) / cupd::T;
+  const int64_t t = (m + NB - 1) / NB;  // panel workgroups: the first tile row of the update
   const int64_t tiles = t * (t + 1) / 2;
-  const double work = (double)m * (double)(m + 1) * (double)kr;
-  WSIC_LAUNCH("chol_update", work, st, k_chol_update<NB>, dim3((unsigned)tiles), dim3(256), 0, A,
-              lda, r0, c0, m, info);
+  const double nbk = (double)(m < NB ? m : NB);
+  const double work = (double)m * (double)(m + 1) * NB + nbk * nbk * nbk / 3.0 + nbk * nbk * (m - nbk);
+  WSIC_LAUNCH("chol_step", work, st, k_chol_step, dim3((unsigned)tiles), dim3(64 * PANEL_WAVES), 0,
+              A, lda, kb, n, (int)t, info);
   return WSIC_OK;
 }
 

@@ -691,13 +691,13 @@ int wsic_cholesky(double* A, int64_t n, int64_t lda, int64_t* info, void* ws, si
     int64_t* dinfo = (int64_t*)ws;
     WSIC_TRY(launch_fill_zero(dinfo, FLAGS_BYTES, st));
     constexpr int NBK = 64;
-    for (int64_t kb = 0; kb < n; kb += NBK) {
-      const int nbk = (int)std::min<int64_t>(NBK, n - kb);
-      WSIC_TRY(launch_potrf_panel(A, lda, kb, nbk, n, dinfo, st));
+    WSIC_TRY(launch_potrf_panel(A, lda, 0, (int)std::min<int64_t>(NBK, n), n, dinfo, st));
+    for (int64_t kb = 0; kb + NBK < n; kb += NBK) {
+      const int nbk = NBK;
       const int64_t m = n - kb - nbk;
-      if (m <= 0) break;
-      if (nbk == NBK && chol_update_ok(A, lda, kb + nbk, nbk)) {
-        WSIC_TRY(launch_chol_update(A, lda, kb, kb + nbk, m, nbk, dinfo, st));
+      if (chol_step_ok(A, lda, kb + nbk)) {
+        // this step's trailing update and the next panel in one launch
+        WSIC_TRY(launch_chol_step(A, lda, kb, n, dinfo, st));
         continue;
       }
       GemmArgs g{};
@@ -715,6 +715,7 @@ int wsic_cholesky(double* A, int64_t n, int64_t lda, int64_t* info, void* ws, si
       g.upper_only = 1;
       const double work = (double)m * (double)(m + 1) * (double)nbk;
       WSIC_TRY(launch_gemm(A_F64_T, EPI_STORE, g, "gemm_chol", work, st));
+      WSIC_TRY(launch_potrf_panel(A, lda, kb + nbk, (int)std::min<int64_t>(NBK, m), n, dinfo, st));
     }
     WSIC_TRY(launch_zero_lower(A, n, lda, st));
     const ReadPiece pi{info, dinfo, sizeof(int64_t)};
