@@ -117,15 +117,18 @@ int launch_mirror_upper(double* S, int64_t n, int64_t lds, hipStream_t st);
 int launch_diag_check(const double* S, int64_t n, int64_t lds, int* flags, hipStream_t st);
 
 // cholesky
-// factor the diagonal block at kb and solve the block row to its right, in place
+// factor the diagonal block at kb (into the 64 x 64 slot ud) and solve the block row to its
+// right in place; launch_put_diag moves a slot's block into A
 int launch_potrf_panel(double* A, int64_t lda, int64_t kb, int nbk, int64_t n, int64_t* info,
-                       hipStream_t st);
+                       double* ud, hipStream_t st);
+int launch_put_diag(double* A, int64_t lda, int64_t kb, int nbk, const double* ud, hipStream_t st);
 int launch_zero_lower(double* A, int64_t n, int64_t lda, hipStream_t st);
 // One 64-column step after the panel at kb: A[c0.., c0..] (upper tiles, c0 = kb + 64) -= X^T X
 // with X the solved block row, fused with the panel at c0; chol_step_ok tells whether its
 // alignment preconditions hold
 bool chol_step_ok(const double* A, int64_t lda, int64_t c0);
-int launch_chol_step(double* A, int64_t lda, int64_t kb, int64_t n, int64_t* info, hipStream_t st);
+int launch_chol_step(double* A, int64_t lda, int64_t kb, int64_t n, int64_t* info,
+                     const double* ud_cur, double* ud_next, hipStream_t st);
 
 // SIC
 int launch_prep(const double* U, int64_t ldu, int64_t n, double* invd, int* flags, hipStream_t st);

@@ -17,6 +17,9 @@
 //   trailing      : A_rest,rest -= X^T X on upper tiles (fp64 MFMA GEMM, k-major operands).
 //                   k_chol_step launches it together with the next panel, whose workgroups
 //                   first apply the update to the next block row themselves.
+// A panel's factored diagonal block goes to one of two NB x NB slots and reaches A in the next
+// launch (or a final copy): with more panel workgroups than fit on the chip at once, a late
+// workgroup would otherwise read workgroup 0's result instead of the block it has to factor.
 // The first failing pivot (1-based, global) is recorded in *info; later steps see it and
 // return immediately.
 #include "common.h"
@@ -39,10 +42,12 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
 
 // The pivot loop of one panel workgroup and its stores. a[s], sl[s] hold rows RPW w + s of
 // column j of the diagonal block and of this workgroup's slab (block b > 0), as loaded.
+// The diagonal block (workgroup 0) goes to ud (NB x NB, zeros below the diagonal), not into A:
+// other panel workgroups of the same launch may not have read A's copy of it yet.
 __device__ __forceinline__ void panel_factor(double (&a)[RPW], double (&sl)[RPW], double* A,
                                              int64_t lda, int64_t kb, int nbk, int64_t n,
                                              int64_t* info, int b, double (*row)[NB],
-                                             double (*srow)[NB]) {
+                                             double (*srow)[NB], double* ud) {
   const int j = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t c = kb + (int64_t)b * NB + j;  // slab column (b > 0)
@@ -97,7 +102,7 @@ __device__ __forceinline__ void panel_factor(double (&a)[RPW], double (&sl)[RPW]
     const int i = RPW * w + s;
     if (i < nbk) {
       if (b == 0) {
-        if (j < nbk) A[(kb + i) * lda + kb + j] = (i <= j) ? a[s] : 0.0;
+        if (j < nbk) ud[i * NB + j] = (i <= j) ? a[s] : 0.0;
       } else if (cin) {
         A[(kb + i) * lda + c] = sl[s];
       }
@@ -106,7 +111,8 @@ __device__ __forceinline__ void panel_factor(double (&a)[RPW], double (&sl)[RPW]
 }
 
 __global__ __launch_bounds__(64 * PANEL_WAVES) void k_potrf_panel(double* A, int64_t lda, int64_t kb,
-                                                                 int nbk, int64_t n, int64_t* info) {
+                                                                 int nbk, int64_t n, int64_t* info,
+                                                                 double* ud) {
   // raw row k of the diagonal block and of this workgroup's slab, double-buffered by the parity
   // of k so that one barrier per pivot separates its writes from the previous pivot's reads
   __shared__ double row[2][NB];
@@ -124,7 +130,20 @@ __global__ __launch_bounds__(64 * PANEL_WAVES) void k_potrf_panel(double* A, int
     a[s] = (i <= j && j < nbk) ? A[(kb + i) * lda + kb + j] : (i == j ? 1.0 : 0.0);
     sl[s] = (cin && i < nbk) ? A[(kb + i) * lda + c] : 0.0;
   }
-  panel_factor(a, sl, A, lda, kb, nbk, n, info, b, row, srow);
+  panel_factor(a, sl, A, lda, kb, nbk, n, info, b, row, srow, ud);
+}
+
+// The factored diagonal block of step kb from its slot into A (64 x 64 block, ld NB slot)
+__device__ __forceinline__ void put_diag(double* A, int64_t lda, int64_t kb, int nbk,
+                                         const double* ud) {
+  for (int e = threadIdx.x; e < nbk * NB; e += blockDim.x) {
+    const int i = e / NB, j = e - i * NB;
+    if (j < nbk) A[(kb + i) * lda + kb + j] = ud[e];
+  }
+}
+
+__global__ void k_put_diag(double* A, int64_t lda, int64_t kb, int nbk, const double* ud) {
+  put_diag(A, lda, kb, nbk, ud);
 }
 
 // Trailing update A22 -= X^T X after a block row: X = rows r0 .. r0+63 of A at columns
@@ -187,7 +206,8 @@ __device__ __forceinline__ void tile_mfma(const double (*Xa)[cupd::T], const dou
 // the bulk of the update instead of after it.
 __global__ __launch_bounds__(64 * PANEL_WAVES) void k_chol_step(double* A, int64_t lda, int64_t kb,
                                                                int64_t n, int npanel,
-                                                               int64_t* info) {
+                                                               int64_t* info, const double* ud_cur,
+                                                               double* ud_next) {
   using namespace cupd;
   static_assert(PANEL_WAVES == 8, "tile layout: 8 waves in 2 x 4");
   __shared__ __attribute__((aligned(1024))) double Xs[2][T][T];
@@ -203,6 +223,8 @@ __global__ __launch_bounds__(64 * PANEL_WAVES) void k_chol_step(double* A, int64
   if (bid < npanel) {
     const int b = bid;
     const int64_t j0 = (int64_t)b * T;
+    // this step's factored diagonal block into A (nothing in this launch reads that block)
+    if (b == 0) put_diag(A, lda, kb, NB, ud_cur);
     double cd[2][4], cs[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -239,7 +261,7 @@ __global__ __launch_bounds__(64 * PANEL_WAVES) void k_chol_step(double* A, int64
       a[s] = (i <= j && j < nbk) ? Xs[0][i][j] : (i == j ? 1.0 : 0.0);
       sl[s] = (cin && i < nbk) ? Xs[1][i][j] : 0.0;
     }
-    panel_factor(a, sl, A, lda, c0, nbk, n, info, b, row, srow);
+    panel_factor(a, sl, A, lda, c0, nbk, n, info, b, row, srow, ud_next);
     return;
   }
 
@@ -287,7 +309,7 @@ __global__ void k_zero_lower(double* A, int64_t n, int64_t lda) {
 }  // namespace
 
 int launch_potrf_panel(double* A, int64_t lda, int64_t kb, int nbk, int64_t n, int64_t* info,
-                       hipStream_t st) {
+                       double* ud, hipStream_t st) {
   if (nbk <= 0 || nbk > NB) {
     set_error("internal: potrf block %d", nbk);
     return WSIC_E_INVAL;
@@ -296,7 +318,12 @@ int launch_potrf_panel(double* A, int64_t lda, int64_t kb, int nbk, int64_t n, i
   const unsigned blocks = 1 + (unsigned)((m + NB - 1) / NB);
   const double work = (double)nbk * nbk * nbk / 3.0 + (double)nbk * nbk * m;
   WSIC_LAUNCH("potrf_panel", work, st, k_potrf_panel, dim3(blocks), dim3(64 * PANEL_WAVES), 0, A, lda, kb, nbk, n,
-              info);
+              info, ud);
+  return WSIC_OK;
+}
+
+int launch_put_diag(double* A, int64_t lda, int64_t kb, int nbk, const double* ud, hipStream_t st) {
+  WSIC_LAUNCH("put_diag", 16.0 * nbk * nbk, st, k_put_diag, dim3(1), dim3(256), 0, A, lda, kb, nbk, ud);
   return WSIC_OK;
 }
 
@@ -305,7 +332,7 @@ bool chol_step_ok(const double* A, int64_t lda, int64_t c0) {
 }
 
 int launch_chol_step(double* A, int64_t lda, int64_t kb, int64_t n, int64_t* info,
-                     hipStream_t st) {
+                     const double* ud_cur, double* ud_next, hipStream_t st) {
   const int64_t c0 = kb + NB, m = n - c0;
   if (m <= 0 || !chol_step_ok(A, lda, c0)) {
     set_error("internal: cholesky step preconditions");
@@ -316,7 +343,7 @@ int launch_chol_step(double* A, int64_t lda, int64_t kb, int64_t n, int64_t* inf
   const double nbk = (double)(m < NB ? m : NB);
   const double work = (double)m * (double)(m + 1) * NB + nbk * nbk * nbk / 3.0 + nbk * nbk * (m - nbk);
   WSIC_LAUNCH("chol_step", work, st, k_chol_step, dim3((unsigned)tiles), dim3(64 * PANEL_WAVES), 0,
-              A, lda, kb, n, (int)t, info);
+              A, lda, kb, n, (int)t, info, ud_cur, ud_next);
   return WSIC_OK;
 }
 

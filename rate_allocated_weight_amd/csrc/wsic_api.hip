@@ -221,6 +221,7 @@ size_t ws_bytes_for(int op, int64_t n_out, int64_t n_in) {
       break;
     case WSIC_OP_CHOLESKY:
       cv.take<int>(FLAGS_BYTES / sizeof(int));
+      cv.take<double>(2 * 64 * 64);  // two diagonal-block slots
       break;
     case WSIC_OP_SIC:
       carve_sic(cv, n_out, n_in);
@@ -688,18 +689,31 @@ int wsic_cholesky(double* A, int64_t n, int64_t lda, int64_t* info, void* ws, si
     *info = 0;
     WSIC_TRY(check_ws(WSIC_OP_CHOLESKY, 0, n, ws, ws_bytes));
     hipStream_t st = (hipStream_t)stream;
-    int64_t* dinfo = (int64_t*)ws;
+    Carve cv(ws);
+    int64_t* dinfo = cv.take<int64_t>(FLAGS_BYTES / sizeof(int64_t));
+    double* slot[2];
+    slot[0] = cv.take<double>(64 * 64);
+    slot[1] = cv.take<double>(64 * 64);
     WSIC_TRY(launch_fill_zero(dinfo, FLAGS_BYTES, st));
     constexpr int NBK = 64;
-    WSIC_TRY(launch_potrf_panel(A, lda, 0, (int)std::min<int64_t>(NBK, n), n, dinfo, st));
-    for (int64_t kb = 0; kb + NBK < n; kb += NBK) {
+    // testing hook: WSIC_CHOL_STEP=0 runs update and next panel as separate launches
+    const char* fe = std::getenv("WSIC_CHOL_STEP");
+    const bool fused = !(fe && fe[0] == '0');
+    // a panel's diagonal block lands in slot[step & 1] and is moved into A afterwards
+    int64_t step = 0;
+    WSIC_TRY(launch_potrf_panel(A, lda, 0, (int)std::min<int64_t>(NBK, n), n, dinfo, slot[0], st));
+    for (int64_t kb = 0; kb + NBK < n; kb += NBK, ++step) {
       const int nbk = NBK;
       const int64_t m = n - kb - nbk;
-      if (chol_step_ok(A, lda, kb + nbk)) {
-        // this step's trailing update and the next panel in one launch
-        WSIC_TRY(launch_chol_step(A, lda, kb, n, dinfo, st));
+      double* cur = slot[step & 1];
+      double* next = slot[(step + 1) & 1];
+      if (fused && chol_step_ok(A, lda, kb + nbk)) {
+        // this step's trailing update and the next panel in one launch (which also moves this
+        // step's diagonal block into A)
+        WSIC_TRY(launch_chol_step(A, lda, kb, n, dinfo, cur, next, st));
         continue;
       }
+      WSIC_TRY(launch_put_diag(A, lda, kb, nbk, cur, st));
       GemmArgs g{};
       g.M = m;
       g.N = m;
@@ -715,7 +729,12 @@ int wsic_cholesky(double* A, int64_t n, int64_t lda, int64_t* info, void* ws, si
       g.upper_only = 1;
       const double work = (double)m * (double)(m + 1) * (double)nbk;
       WSIC_TRY(launch_gemm(A_F64_T, EPI_STORE, g, "gemm_chol", work, st));
-      WSIC_TRY(launch_potrf_panel(A, lda, kb + nbk, (int)std::min<int64_t>(NBK, m), n, dinfo, st));
+      WSIC_TRY(launch_potrf_panel(A, lda, kb + nbk, (int)std::min<int64_t>(NBK, m), n, dinfo, next,
+                                  st));
+    }
+    {  // the last panel's diagonal block
+      const int64_t kb = step * NBK;
+      WSIC_TRY(launch_put_diag(A, lda, kb, (int)(n - kb), slot[step & 1], st));
     }
     WSIC_TRY(launch_zero_lower(A, n, lda, st));
     const ReadPiece pi{info, dinfo, sizeof(int64_t)};
@@ -902,18 +921,22 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
         take(m, h, b);
       }
     } else {
-      // secant on x = log2 c toward H = R - tol/2 through the two latest evaluations (slope -1,
-      // the high-rate law, until two points exist); once both sides of R are known the step must
-      // land strictly inside the bracket, else -- or when the bracket has not halved in two
-      // steps -- bisect.
+      // Secant on x = log2 c toward H = R - tol/2. The pooled entropy is not smooth at fine
+      // scales (a grid change that flips one rounding decision re-routes the interference of
+      // every column left of it), so the slope is taken only from pairs of evaluations at least
+      // SLOPE_DX apart (slope -1, the high-rate law, until such a pair exists); each step starts
+      // from the latest evaluation. Once both sides of R are known the step must land strictly
+      // inside the bracket, else -- or when the bracket has not halved in two steps -- bisect.
+      constexpr double SLOPE_DX = 1.0 / 1024;
       const double Rt = R - 0.5 * o.rate_tol;
       auto accept = [&]() { return have_hi && h_hi > R - o.rate_tol; };
-      double xa = std::log2(c0), ha = 0.0;
+      std::vector<double> xs, hs;
+      double xb = std::log2(c0), hb = 0.0;
       int b = free_buf();
-      WSIC_TRY(eval(c0, b, &ha));
-      take(c0, ha, b);
-      double xb = xa, hb = ha;
-      bool have_two = false;
+      WSIC_TRY(eval(c0, b, &hb));
+      take(c0, hb, b);
+      xs.push_back(xb);
+      hs.push_back(hb);
       double width_prev = INFINITY;
       int slow = 0;
       while (!accept()) {
@@ -925,9 +948,12 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
           if (xh - xl <= o.bracket_log2) break;
         }
         double slope = -1.0;
-        if (have_two && xb != xa) {
-          const double s = (hb - ha) / (xb - xa);
-          if (s < -1e-3) slope = s;
+        for (size_t i = xs.size() - 1; i-- > 0;) {  // the latest evaluation far enough back
+          if (std::fabs(xb - xs[i]) >= SLOPE_DX) {
+            const double sl = (hb - hs[i]) / (xb - xs[i]);
+            if (sl < -0.25 && sl > -4.0) slope = sl;
+            break;
+          }
         }
         double xn = xb + (Rt - hb) / slope;
         if (bracketed) {
@@ -946,11 +972,10 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
         double hn;
         WSIC_TRY(eval(cn, b, &hn));
         take(cn, hn, b);
-        xa = xb;
-        ha = hb;
         xb = xn;
         hb = hn;
-        have_two = true;
+        xs.push_back(xb);
+        hs.push_back(hb);
         if (have_hi && have_lo) {
           const double width = std::log2(c_hi) - std::log2(c_lo);
           slow = (width > 0.5 * width_prev) ? slow + 1 : 0;

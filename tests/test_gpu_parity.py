@@ -106,6 +106,30 @@ def test_cholesky_reports_pivot(device, n, bad):
     assert ei.value.info == info_or == bad
 
 
+def test_cholesky_more_panel_workgroups_than_fit(device, monkeypatch):
+    """n = 20480: a step's panel has 320 workgroups, more than one launch keeps resident, so
+    late panel workgroups start after workgroup 0 has finished. The factor must equal the one
+    from separate update and panel launches bit for bit and reproduce Sigma on sampled entries
+    (regression: the diagonal block was once overwritten in place before all had read it)."""
+    n = 20480
+    say(f"[cholesky-wide] n={n}")
+    g = torch.Generator(device=device).manual_seed(5)
+    R = (torch.rand(n, n, generator=g, device=device, dtype=torch.float64) - 0.5) / n
+    sig = R + R.T  # off-diagonal row sums below 1: with a unit diagonal, positive definite
+    del R
+    sig.diagonal().add_(1.0)
+    U, _ = lib.cholesky(sig.clone())
+    monkeypatch.setenv("WSIC_CHOL_STEP", "0")
+    U_sep, _ = lib.cholesky(sig.clone())
+    assert torch.equal(U, U_sep)
+    rng = np.random.default_rng(6)
+    I = torch.from_numpy(rng.integers(0, n, 4096)).to(device)
+    J = torch.from_numpy(rng.integers(0, n, 4096)).to(device)
+    back = ((U[:, I] * U[:, J]).sum(0) - sig[I, J]).abs().max().item()
+    say(f"  max |(U^T U - Sigma)_ij| on 4096 entries = {back:.3e}")
+    assert back <= 64 * n * 2.0 ** -52
+
+
 # ------------------------------------------------------------------ SIC pass
 def _oracle_factor_on_device(layer):
     L, info = oracle.cholesky_lower(_sigma_oracle(layer))
