@@ -122,9 +122,15 @@ int wsic_sic_quantize(const void* W, int dtype, int64_t n_out, int64_t n_in, int
                       int32_t* codes, int64_t ldq, float* resid, int64_t ldr,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* Default acceptance window of the rate controller (bits per weight). The pooled entropy of SIC
+ * codes is not smooth below ~1e-4 relative changes of c (one flipped rounding decision re-routes
+ * the interference of every column left of it, moving H by a few 1e-5), so a window narrower
+ * than that costs extra passes. */
+#define WSIC_WF_RATE_TOL 8e-5
+
 /* Options of the rate controller; pass NULL for the defaults shown. */
 typedef struct wsic_wf_opts {
-  double rate_tol;     /* accept c once R - rate_tol < H(c) <= R (default 2e-5 bits)        */
+  double rate_tol;     /* accept c once R - rate_tol < H(c) <= R (default WSIC_WF_RATE_TOL)  */
   double bracket_log2; /* or once log2(c_hi / c_lo) <= bracket_log2 (default 2^-20)          */
   int32_t max_passes;  /* SIC passes allowed (default 64)                                   */
   int32_t mode;        /* WSIC_WF_BISECT: start at c_init, double (halve) c until the rate

@@ -210,7 +210,7 @@ _MODES = {"auto": WF_AUTO, "secant": WF_SECANT, "bisect": WF_BISECT}
 
 
 def waterfill(W: torch.Tensor, U: torch.Tensor, target_bits: float, *, mode: str = "auto",
-              rate_tol: float = 2e-5, bracket_log2: float = 2.0 ** -20, max_passes: int = 64,
+              rate_tol: float = 8e-5, bracket_log2: float = 2.0 ** -20, max_passes: int = 64,
               c_init: float = 0.0, want_resid: bool = True, codes: Optional[torch.Tensor] = None,
               resid: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> Dict[str, object]:
     """Grid scale c with pooled code entropy H(c) <= target_bits, and its codes."""

@@ -786,10 +786,10 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
       set_error("waterfill: bad argument");
       return WSIC_E_INVAL;
     }
-    wsic_wf_opts o{2e-5, std::ldexp(1.0, -20), 64, WSIC_WF_AUTO, 0.0};
+    wsic_wf_opts o{WSIC_WF_RATE_TOL, std::ldexp(1.0, -20), 64, WSIC_WF_AUTO, 0.0};
     if (opts) {
       o = *opts;
-      if (!(o.rate_tol >= 0.0)) o.rate_tol = 2e-5;
+      if (!(o.rate_tol >= 0.0)) o.rate_tol = WSIC_WF_RATE_TOL;
       if (!(o.bracket_log2 > 0.0)) o.bracket_log2 = std::ldexp(1.0, -20);
       if (o.max_passes <= 0) o.max_passes = 64;
       if (o.mode != WSIC_WF_AUTO && o.mode != WSIC_WF_SECANT && o.mode != WSIC_WF_BISECT) {
