@@ -2,38 +2,48 @@
 // integer codes are unbounded and entropy coded, so the rate is the entropy of the code
 // histogram).
 //
-// k_hist: each workgroup counts its share of the codes in an LDS window of +-HIST_HALF bins;
-// codes in [-7, 7] (the bulk at 1-4 bits per weight) are first tallied in per-thread
-// registers to avoid LDS atomic contention on a handful of bins. Window counts are then added
-// to a global u64 window; codes outside the window are appended to an overflow list that the
-// host counts exactly.
+// k_hist: each workgroup counts its share of the codes in an LDS window of +-255 bins (wider
+// codes, rare below ~8 bits per weight, go straight to the global window of +-HIST_HALF);
+// codes in [-7, 8] (the bulk at 1-4 bits per weight) are first tallied in per-thread
+// registers and summed over the wave, to avoid LDS atomic contention on a handful of bins.
+// Window counts are then added to a global u64 window; codes outside the window are appended to
+// an overflow list that the host counts exactly.
 // k_entropy_reduce: one workgroup forms sum_k n_k log2 n_k over the window in fp64.
 #include "common.h"
 
 namespace wsic {
 namespace {
 
-constexpr int REG_HALF = 7;  // codes tallied in registers: [-7, 7]
+// codes in [-7, 8] are tallied per thread as 16-bit counters, two to a register; a thread
+// counts at most HIST_PER_THREAD codes, so a wave's sums still fit 16 bits
+constexpr int REG_LO = -7, REG_N = 16;
+constexpr int HIST_PER_THREAD = 1000;
+// LDS window of a workgroup (codes beyond it go to the global window with global atomics)
+constexpr int LDS_HALF = 255, LDS_BINS = 2 * LDS_HALF + 1;
 
 __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ codes, int64_t n_out,
                                               int64_t n_in, int64_t ldq,
                                               unsigned long long* __restrict__ bins,
                                               int32_t* __restrict__ ovf,
                                               unsigned int* __restrict__ ovf_count) {
-  __shared__ unsigned int lb[HIST_BINS];
-  for (int b = threadIdx.x; b < HIST_BINS; b += blockDim.x) lb[b] = 0u;
+  __shared__ unsigned int lb[LDS_BINS];
+  for (int b = threadIdx.x; b < LDS_BINS; b += blockDim.x) lb[b] = 0u;
   __syncthreads();
 
-  unsigned int reg[2 * REG_HALF + 1];
+  unsigned int reg[REG_N / 2];
 #pragma unroll
-  for (int k = 0; k < 2 * REG_HALF + 1; ++k) reg[k] = 0u;
+  for (int k = 0; k < REG_N / 2; ++k) reg[k] = 0u;
 
   auto count = [&](int v) {
-    if (v >= -REG_HALF && v <= REG_HALF) {
+    const int t = v - REG_LO;
+    if (t >= 0 && t < REG_N) {
+      const unsigned int inc = 1u << (16 * (t & 1));
 #pragma unroll
-      for (int k = -REG_HALF; k <= REG_HALF; ++k) reg[k + REG_HALF] += (v == k) ? 1u : 0u;
+      for (int k = 0; k < REG_N / 2; ++k) reg[k] += ((t >> 1) == k) ? inc : 0u;
+    } else if (v >= -LDS_HALF && v <= LDS_HALF) {
+      atomicAdd(&lb[v + LDS_HALF], 1u);
     } else if (v >= -HIST_HALF && v <= HIST_HALF) {
-      atomicAdd(&lb[v + HIST_HALF], 1u);
+      atomicAdd(&bins[v + HIST_HALF], 1ull);
     } else {
       const unsigned int slot = atomicAdd(ovf_count, 1u);
       if (slot < OVF_CAP) ovf[slot] = v;
@@ -65,12 +75,20 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ codes,
   } else {
     for (int64_t e = gid; e < total; e += stride) count(codes[(e / n_in) * ldq + (e % n_in)]);
   }
+  // register tallies: summed over the wave, one LDS atomic per wave and bin
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int k = 0; k < 2 * REG_HALF + 1; ++k)
-    if (reg[k]) atomicAdd(&lb[k - REG_HALF + HIST_HALF], reg[k]);
+  for (int k = 0; k < REG_N / 2; ++k) {
+    unsigned int v = reg[k];
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    if (lane == 0) {
+      if (v & 0xffffu) atomicAdd(&lb[2 * k + REG_LO + LDS_HALF], v & 0xffffu);
+      if (v >> 16) atomicAdd(&lb[2 * k + 1 + REG_LO + LDS_HALF], v >> 16);
+    }
+  }
   __syncthreads();
-  for (int b = threadIdx.x; b < HIST_BINS; b += blockDim.x)
-    if (lb[b]) atomicAdd(&bins[b], (unsigned long long)lb[b]);
+  for (int b = threadIdx.x; b < LDS_BINS; b += blockDim.x)
+    if (lb[b]) atomicAdd(&bins[b - LDS_HALF + HIST_HALF], (unsigned long long)lb[b]);
 }
 
 __global__ __launch_bounds__(256) void k_entropy_reduce(const unsigned long long* bins,
@@ -118,8 +136,12 @@ __global__ void k_fill_zero(uint32_t* p, size_t words) {
 int launch_hist(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
                 unsigned long long* bins, int32_t* ovf, unsigned int* ovf_count, hipStream_t st) {
   const int64_t total = n_out * n_in;
-  int64_t blocks = (total + 255) / 256;
+  // enough threads that none counts more than HIST_PER_THREAD codes (16-bit wave sums), and at
+  // least ~64 codes per thread so the per-workgroup window clear and flush stay small
+  int64_t blocks = (total + 256 * 64 - 1) / (256 * 64);
+  const int64_t need = (total + 256LL * HIST_PER_THREAD - 1) / (256LL * HIST_PER_THREAD);
   if (blocks > 2048) blocks = 2048;
+  if (blocks < need) blocks = need;
   if (blocks < 1) blocks = 1;
   WSIC_LAUNCH("hist", 4.0 * (double)total, st, k_hist, dim3((unsigned)blocks), dim3(256), 0,
               codes, n_out, n_in, ldq, bins, ovf, ovf_count);
