@@ -47,6 +47,12 @@ struct Guard {
   float bnd[8];  // the bound, rounded up to float
 };
 
+// x >= 0 to float, rounded up (a few instructions instead of the library's directed rounding)
+__device__ __forceinline__ float f32_up(double x) {
+  const float f = (float)x;
+  return ((double)f < x) ? __int_as_float(__float_as_int(f) + 1) : f;
+}
+
 // Step J of the in-block recursion (J = 127 ... 0), then the remaining ones. Columns past the
 // end of a ragged last block hold z = 0 and all-zero B entries, so their steps change nothing
 // and need no branch. A column's target is final once its own step has run (later steps only
@@ -468,7 +474,7 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
     issue_pack(nb - 1, BsA);
     load_ops(nb - 1, yv, gv, b0);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) bsf[s] = __double2float_ru(b0[s]);
+    for (int s = 0; s < 8; ++s) bsf[s] = f32_up(b0[s]);
   }
 
   auto do_block = [&](int b, double* Bcur, double* Bidle) {
@@ -579,12 +585,16 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
 
     double z[8], gin_v[8];
     Guard g;
+    // the bound S 2^-P (guard scale) per row, rounded up; times the column scale and a margin
+    // that covers the float product's rounding
+    const float tb = f32_up(S * LIMB_EPS * p.guard_scale) * (1.0f + 0x1p-22f);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int j = l16 + 16 * s;
       const bool in = active && j < w;
-      z[s] = in ? yv[s] * p.invc - gv[s] - fz[s] : 0.0;
-      g.bnd[s] = (in && gin) ? __double2float_ru((double)bsf[s] * S * LIMB_EPS * p.guard_scale) : 0.0f;
+      const double zv = yv[s] * p.invc - gv[s] - fz[s];
+      z[s] = in ? zv : 0.0;
+      g.bnd[s] = (in && gin) ? tb * bsf[s] : 0.0f;
     }
     if (active && cnt > 0) {
       // exact interference of the excess of large codes to the right (fp64); the list may have
@@ -779,7 +789,7 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
     for (int s = 0; s < 8; ++s) {
       yv[s] = yn[s];
       gv[s] = gn[s];
-      bsf[s] = __double2float_ru(bn[s]);
+      bsf[s] = f32_up(bn[s]);
     }
     // int8 codes in LDS visible to every wave; every wave done with this block's packed B
     // before it becomes the idle buffer. (Global stores are not waited for here: the next
