@@ -220,6 +220,31 @@ def main():
         cand = [(k, L.profile_read(k)["ms"]) for k in L.profile_names() if k in FAMILIES]
         return max(cand, key=lambda kv: kv[1])[0] if cand else None
 
+    # every family's rate against its own peak, from the warm-up step (all families evented)
+    families = {}
+    if not args.no_profile and args.warmup > 0:
+        for name in L.profile_names():
+            if name not in FAMILIES:
+                continue
+            p = L.profile_read(name)
+            bound, peak_key, scale = FAMILIES[name]
+            peak, unit = PEAKS[peak_key]
+            ach = p["work"] * scale / max(1e-12, p["ms"] * 1e-3)
+            families[name] = {"ms_per_step": round(p["ms"] / args.warmup, 4), "launches": p["launches"],
+                              "achieved": round(ach, 3), "peak": peak, "unit": unit,
+                              "frac": round(ach / peak, 4)}
+    trailing = None
+    if "gemm_trail_i8" in families:
+        # the int8 limb product of the interference (trailing update) measured as the algorithmic
+        # product it replaces: 2 M N K flops, i.e. its int8 ops over the 5 digit planes
+        f = families["gemm_trail_i8"]
+        tf = f["achieved"] / 5.0
+        trailing = {"kernel": "gemm_trail_i8", "algorithmic_tflops": round(tf, 2),
+                    "peak_fp32_mfma_tflops": PEAKS["mfma_f32"][0],
+                    "frac_of_fp32_mfma_peak": round(tf / PEAKS["mfma_f32"][0], 4),
+                    "note": "GEMM part only (above the 512-column super-blocks); the product inside "
+                            "the super-block launches is counted with sic_leaf"}
+
     if not args.no_profile:
         L.profile_enable(False)
         if args.warmup > 0:
@@ -287,6 +312,8 @@ def main():
         "value_from_U": round(n_out * n_in / (ms_from_u * 1e-3) / 1e9, 6),
         "roofline": roofline,
         "kernels": kernels,
+        "families_warmup": families,
+        "trailing_update": trailing,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

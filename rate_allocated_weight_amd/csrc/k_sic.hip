@@ -19,6 +19,8 @@
 // block keeps rows 0 .. 16*(j/16+1)-1, zero from row j on, so that in step j every lane reads
 // its entries unconditionally (a zero leaves finished targets unchanged). Column j = 16a + r
 // starts at 16 (a+1)(8a + r); a block holds 9216 doubles (72 KiB, two workgroups per CU).
+#include <type_traits>
+
 #include "common.h"
 #include "pipe.h"
 
@@ -70,10 +72,19 @@ __device__ __forceinline__ void load_b(double (&b)[8], const double* __restrict_
   }
 }
 
+// hook(integral_constant<J>) runs at the start of step J: the super-block kernel issues the next
+// block's loads there, spread over the LDS-bound steps instead of in one burst.
+struct NoHook {
+  template <class T>
+  __device__ __forceinline__ void operator()(T) const {}
+};
+
 template <int J>
 struct Steps {
+  template <class H>
   static __device__ __forceinline__ void run(double (&z)[8], const double* __restrict__ bl,
-                                             const double (&b0)[8], const double (&b1)[8]) {
+                                             const double (&b0)[8], const double (&b1)[8], H& hook) {
+    hook(std::integral_constant<int, J>{});
     constexpr int a = J >> 4, l = J & 15;
     constexpr int an = (J - 1) >> 4;  // group of the next step's target (a or a - 1)
     double b2[8];
@@ -83,20 +94,23 @@ struct Steps {
 #pragma unroll
     for (int sp = 0; sp <= a; ++sp)
       if (J == 0 || sp != an) z[sp] = fma(-b0[sp], qb, z[sp]);
-    Steps<J - 1>::run(z, bl, b1, b2);
+    Steps<J - 1>::run(z, bl, b1, b2, hook);
   }
 };
 template <>
 struct Steps<-1> {
+  template <class H>
   static __device__ __forceinline__ void run(double (&)[8], const double*, const double (&)[8],
-                                             const double (&)[8]) {}
+                                             const double (&)[8], H&) {}
 };
 
-__device__ __forceinline__ void run_block(double (&z)[8], const double* __restrict__ bl) {
+template <class H = NoHook>
+__device__ __forceinline__ void run_block(double (&z)[8], const double* __restrict__ bl,
+                                          H&& hook = H{}) {
   double b0[8], b1[8];
   load_b<BW - 1>(b0, bl);
   load_b<BW - 2>(b1, bl);
-  Steps<BW - 1>::run(z, bl, b0, b1);
+  Steps<BW - 1>::run(z, bl, b0, b1, hook);
 }
 
 // I8 = the interference G came from the int8 limb product (k_limb.hip): then the leaf also
@@ -614,31 +628,57 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) gin_v[s] = yv[s] * p.invc - z[s];
-    // the next block's operands are on the way while this block's steps run (issued after the
-    // loads above: the memory counter completes in order)
+    // The next block's loads are issued during this block's steps (LDS-bound, so the memory
+    // instructions fill idle issue slots instead of stalling in one burst): the L2 warm-up of
+    // its digit planes (each 128-byte line touched by one thread of the workgroups that share an
+    // L2; workgroups are dealt to the 8 XCDs round-robin) at the first step, its packed B
+    // (PACK_DMA direct loads per wave) every 6 steps, its Y, G and column scales (one register
+    // each) every 12 steps. They are issued after this block's own loads above: the memory
+    // counter completes in order.
+    // (No branches in the hook: after the last block of the launch it reloads this block's
+    // operands into the idle buffer and registers, which nothing reads.)
     double yn[8], gn[8], bn[8];
     int pf = 0;  // touched digit-plane words (consumed below, never used)
-    if (b > 0) {
-      // Warm the L2 with the digit planes the next block's product reads (rows j0 - 128 .. j0 - 1,
-      // bytes [j0, hi) of each, every plane): each 128-byte line is touched by one thread of
-      // the workgroups that share an L2 (workgroups are dealt to the 8 XCDs round-robin).
-      const int nlr = (int)((hi - j0 + 127) / 128);  // lines per row and plane
-      const int nl = LIMBS * BW * nlr;
-      const int per_xcd = (int)((gridDim.x + 7 - (blockIdx.x & 7)) / 8);
-      for (int i = (int)(blockIdx.x >> 3) * 256 + tid; i < nl; i += per_xcd * 256) {
-        const int l = i / (BW * nlr), rem = i - l * (BW * nlr);
-        const int r = rem / nlr, c = rem - r * nlr;
-        pf ^= *reinterpret_cast<const int*>(p.D + l * p.plane + (j0 - BW + r) * p.ldd + j0 + 128 * c);
+    const int64_t jn0 = b > 0 ? j0 - BW : j0;  // the next block
+    auto hook = [&](auto Jc) __attribute__((always_inline)) {
+      constexpr int J = decltype(Jc)::value;
+      if constexpr (J == BW - 1) {
+        // line i: row i % 128 of the next block, plane (i / 128) % 5, line (i / 128) / 5 of the
+        // row's bytes [j0, hi); at most two per thread, out-of-range indices clamped
+        const int nlr = (int)((hi - j0 + 127) / 128);
+        const int nl = LIMBS * BW * nlr;
+        const int per_xcd = (int)((gridDim.x + 7 - (blockIdx.x & 7)) / 8);
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          int i = ((int)(blockIdx.x >> 3) + it * per_xcd) * 256 + tid;
+          i = i < nl ? i : nl - 1;
+          const int r = i & (BW - 1), t = i >> 7, c = t / LIMBS, l = t - LIMBS * c;
+          const int64_t row_d = jn0 + r < hi ? jn0 + r : hi - 1;  // a ragged block's rows end at hi
+          pf ^= *reinterpret_cast<const int*>(p.D + l * p.plane + row_d * p.ldd + j0 + 128 * c);
+        }
       }
-      issue_pack(b - 1, Bidle);
-      load_ops(b - 1, yn, gn, bn);
-    }
+      constexpr int dj = BW - 2 - J;
+      if constexpr (dj >= 0 && dj % 6 == 0 && dj / 6 < PACK_DMA) {
+        const char* src = reinterpret_cast<const char*>(p.Bpk + (jn0 / BW) * PACK);
+        const int ins = PACK_DMA * wave + dj / 6;
+        pipe::dma16(src + 1024 * ins + 16 * lane, reinterpret_cast<char*>(Bidle) + 1024 * ins);
+      }
+      constexpr int oj = BW - 5 - J;
+      if constexpr (oj >= 0 && oj % 12 == 0 && oj / 12 < 8) {
+        constexpr int sv = oj / 12;
+        const int64_t jc = jn0 + l16 + 16 * sv;
+        const int64_t jcc = jc < hi ? jc : hi - 1;  // (the last block of the matrix may be ragged)
+        yn[sv] = p.Y[rowc * p.ldy + jcc];
+        gn[sv] = HAS_G ? p.G[rowc * p.ldg + jcc] : 0.0;
+        bn[sv] = p.bscale[jcc];
+      }
+    };
 
     // the lane's offset is made opaque here so that the block's LDS addresses are formed inside
     // the loop (immediate offsets) instead of being hoisted into hundreds of live registers
     int lb = l16;
     asm volatile("" : "+v"(lb));
-    run_block(z, Bcur + lb);
+    run_block(z, Bcur + lb, hook);
 
     if (gin) {  // uniform
       // decisions inside the error bound: re-check one by one, re-derive the block if needed
