@@ -632,9 +632,10 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
     // instructions fill idle issue slots instead of stalling in one burst): the L2 warm-up of
     // its digit planes (each 128-byte line touched by one thread of the workgroups that share an
     // L2; workgroups are dealt to the 8 XCDs round-robin) at the first step, its packed B
-    // (PACK_DMA direct loads per wave) every 6 steps, its Y, G and column scales (one register
-    // each) every 12 steps. They are issued after this block's own loads above: the memory
-    // counter completes in order.
+    // (PACK_DMA direct loads per wave) every 3 steps, its Y, G and column scales (one register
+    // each) every 6 steps, all in the first half so they have landed by the end of the block.
+    // They are issued after this block's own loads above: the memory counter completes in
+    // order.
     // (No branches in the hook: after the last block of the launch it reloads this block's
     // operands into the idle buffer and registers, which nothing reads.)
     double yn[8], gn[8], bn[8];
@@ -658,14 +659,14 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
         }
       }
       constexpr int dj = BW - 2 - J;
-      if constexpr (dj >= 0 && dj % 6 == 0 && dj / 6 < PACK_DMA) {
+      if constexpr (dj >= 0 && dj % 3 == 0 && dj / 3 < PACK_DMA) {
         const char* src = reinterpret_cast<const char*>(p.Bpk + (jn0 / BW) * PACK);
-        const int ins = PACK_DMA * wave + dj / 6;
+        const int ins = PACK_DMA * wave + dj / 3;
         pipe::dma16(src + 1024 * ins + 16 * lane, reinterpret_cast<char*>(Bidle) + 1024 * ins);
       }
-      constexpr int oj = BW - 5 - J;
-      if constexpr (oj >= 0 && oj % 12 == 0 && oj / 12 < 8) {
-        constexpr int sv = oj / 12;
+      constexpr int oj = BW - 3 - J;
+      if constexpr (oj >= 0 && oj % 6 == 0 && oj / 6 < 8) {
+        constexpr int sv = oj / 6;
         const int64_t jc = jn0 + l16 + 16 * sv;
         const int64_t jcc = jc < hi ? jc : hi - 1;  // (the last block of the matrix may be ragged)
         yn[sv] = p.Y[rowc * p.ldy + jcc];
@@ -682,11 +683,12 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
 
     if (gin) {  // uniform
       // decisions inside the error bound: re-check one by one, re-derive the block if needed
+      // (LDS-only barriers: the next block's loads in flight need not land here)
       if (tid == 0) {
         n_hit = 0;
         must_redo = 0;
       }
-      __syncthreads();
+      pipe::barrier_lds();
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         if (0.5 - fabs(z[s] - rint(z[s])) <= (double)g.bnd[s]) {
@@ -699,9 +701,11 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
           }
         }
       }
-      __syncthreads();
+      pipe::barrier_lds();
       const int nh = n_hit;
       if (tid == 0 && nh > 0) atomicAdd(p.flags + 2, nh);
+      // the re-check reads codes other waves stored in earlier blocks: fenced barrier first
+      if (nh > 0) __syncthreads();
       if (nh > HIT_CAP) {
         if (tid == 0) must_redo = 1;
       } else {
@@ -724,7 +728,7 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
           __syncthreads();
         }
       }
-      __syncthreads();
+      pipe::barrier_lds();  // must_redo (a redo only follows re-checks, after the fence above)
       if (must_redo) {
         double acc[8];
 #pragma unroll
