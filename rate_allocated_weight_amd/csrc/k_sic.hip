@@ -432,7 +432,8 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
   // one from the reads of the other (the loop below is unrolled by two for that)
   __shared__ __attribute__((aligned(1024))) double BsA[PACK];
   __shared__ __attribute__((aligned(1024))) double BsB[PACK];
-  __shared__ __attribute__((aligned(16))) int8_t q8s[16][SUP_W];
+  // (rows padded by 16 bytes: the 16 rows an operand read touches then sit on different banks)
+  __shared__ __attribute__((aligned(16))) int8_t q8s[16][SUP_W + 16];
   __shared__ int n_hit, must_redo;
   __shared__ int hit_j[HIT_CAP];
   __shared__ int hit_r[HIT_CAP];
@@ -449,7 +450,8 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
   const int nb = (p.w + BW - 1) / BW;
 
   // this workgroup's int8 codes of the range (zero past hi)
-  for (int e = tid; e < 16 * SUP_W / 16; e += 256) reinterpret_cast<uint4*>(&q8s[0][0])[e] = make_uint4(0, 0, 0, 0);
+  for (int e = tid; e < 16 * (SUP_W + 16) / 16; e += 256)
+    reinterpret_cast<uint4*>(&q8s[0][0])[e] = make_uint4(0, 0, 0, 0);
 
   double S = 0.0;  // sum of |q| over the finished columns of this row
   int cnt = 0;     // entries in this row's excess list
@@ -554,28 +556,61 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           if (mrow >= 16) a[t] = (v4i){0, 0, 0, 0};
+        // planes in pairs (two independent accumulation chains interleaved), the fifth alone
 #pragma unroll
-        for (int l = 0; l < LIMBS; ++l) {
+        for (int l = 0; l < LIMBS; l += 2) {
           const int u = q * LIMBS + l;
-          pipe::wait_ahead<4, SUP_RING - 1>(min(nu - 1 - u, SUP_RING - 1));
+          const bool two = l + 1 < LIMBS;
+          const int ul = two ? u + 1 : u;  // the last unit this step needs
+          // units issued so far: 0 .. u + SUP_RING - 1, so after ul the ring holds
+          // SUP_RING - 2 (pair) or SUP_RING - 1 (single) more, fewer at the end
+          pipe::wait_ahead<4, SUP_RING - 1>(min(nu - 1 - ul, two ? SUP_RING - 2 : SUP_RING - 1));
           // read in assembly with its wait inside: the compiler would otherwise order every
           // read of this buffer behind all direct loads in flight
-          const unsigned sb =
+          const unsigned sb0 =
               (unsigned)reinterpret_cast<uintptr_t>((const pipe::lds_char*)(ring + (u % SUP_RING) * 4096));
-          v4i bb[4];
-          asm volatile(
-              "ds_read_b128 %0, %4\n\t"
-              "ds_read_b128 %1, %5\n\t"
-              "ds_read_b128 %2, %6\n\t"
-              "ds_read_b128 %3, %7\n\t"
-              "s_waitcnt lgkmcnt(0)"
-              : "=&v"(bb[0]), "=&v"(bb[1]), "=&v"(bb[2]), "=&v"(bb[3])
-              : "v"(sb + ro[0]), "v"(sb + ro[1]), "v"(sb + ro[2]), "v"(sb + ro[3])
-              : "memory");
+          v4i b0[4], b1[4];
+          if (two) {
+            const unsigned sb1 = (unsigned)reinterpret_cast<uintptr_t>(
+                (const pipe::lds_char*)(ring + ((u + 1) % SUP_RING) * 4096));
+            asm volatile(
+                "ds_read_b128 %0, %8\n\t"
+                "ds_read_b128 %1, %9\n\t"
+                "ds_read_b128 %2, %10\n\t"
+                "ds_read_b128 %3, %11\n\t"
+                "ds_read_b128 %4, %12\n\t"
+                "ds_read_b128 %5, %13\n\t"
+                "ds_read_b128 %6, %14\n\t"
+                "ds_read_b128 %7, %15\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(b0[0]), "=&v"(b0[1]), "=&v"(b0[2]), "=&v"(b0[3]),
+                  "=&v"(b1[0]), "=&v"(b1[1]), "=&v"(b1[2]), "=&v"(b1[3])
+                : "v"(sb0 + ro[0]), "v"(sb0 + ro[1]), "v"(sb0 + ro[2]), "v"(sb0 + ro[3]),
+                  "v"(sb1 + ro[0]), "v"(sb1 + ro[1]), "v"(sb1 + ro[2]), "v"(sb1 + ro[3])
+                : "memory");
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            acc[l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t], bb[t], acc[l], 0, 0, 0);
-          if (u + SUP_RING < nu) issue_u(u + SUP_RING);  // the slot's operands are in registers
+            for (int t = 0; t < 4; ++t) {
+              acc[l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t], b0[t], acc[l], 0, 0, 0);
+              acc[l + 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t], b1[t], acc[l + 1], 0, 0, 0);
+            }
+            // the two slots' operands are in registers
+            if (u + SUP_RING < nu) issue_u(u + SUP_RING);
+            if (u + 1 + SUP_RING < nu) issue_u(u + 1 + SUP_RING);
+          } else {
+            asm volatile(
+                "ds_read_b128 %0, %4\n\t"
+                "ds_read_b128 %1, %5\n\t"
+                "ds_read_b128 %2, %6\n\t"
+                "ds_read_b128 %3, %7\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(b0[0]), "=&v"(b0[1]), "=&v"(b0[2]), "=&v"(b0[3])
+                : "v"(sb0 + ro[0]), "v"(sb0 + ro[1]), "v"(sb0 + ro[2]), "v"(sb0 + ro[3])
+                : "memory");
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              acc[l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t], b0[t], acc[l], 0, 0, 0);
+            if (u + SUP_RING < nu) issue_u(u + SUP_RING);
+          }
         }
       }
       pipe::barrier_lds();  // every wave done with its ring before the staging overwrites it
