@@ -300,7 +300,10 @@ struct HostStage {
 };
 thread_local HostStage t_stage;  // never freed: one small pinned buffer per calling thread
 
-int read_back(const ReadPiece* p, int n, hipStream_t st) {
+// Copies to the calling thread's pinned staging buffer are enqueued and an event recorded
+// (read_back_start); read_back_finish polls the event and copies out. One read-back per thread
+// at a time.
+int read_back_start(const ReadPiece* p, int n, hipStream_t st) {
   size_t total = 0;
   for (int i = 0; i < n; ++i) total += align_up(p[i].bytes, 16);
   HostStage& hs = t_stage;
@@ -319,6 +322,11 @@ int read_back(const ReadPiece* p, int n, hipStream_t st) {
     off += align_up(p[i].bytes, 16);
   }
   WSIC_HIP_TRY(hipEventRecord(hs.ev, st));
+  return WSIC_OK;
+}
+
+int read_back_finish(const ReadPiece* p, int n) {
+  HostStage& hs = t_stage;
   hipError_t e = hipErrorNotReady;
   for (int spin = 0; spin < (1 << 22) && e == hipErrorNotReady; ++spin) e = hipEventQuery(hs.ev);
   if (e == hipErrorNotReady) e = hipEventSynchronize(hs.ev);
@@ -326,12 +334,17 @@ int read_back(const ReadPiece* p, int n, hipStream_t st) {
     set_error("device read-back failed: %s", hipGetErrorString(e));
     return WSIC_E_HIP;
   }
-  off = 0;
+  size_t off = 0;
   for (int i = 0; i < n; ++i) {
     std::memcpy(p[i].host, hs.buf + off, p[i].bytes);
     off += align_up(p[i].bytes, 16);
   }
   return WSIC_OK;
+}
+
+int read_back(const ReadPiece* p, int n, hipStream_t st) {
+  WSIC_TRY(read_back_start(p, n, st));
+  return read_back_finish(p, n);
 }
 
 int read_flags(const int* dflags, int* out, hipStream_t st) {
@@ -581,6 +594,67 @@ int sic_pass(const SicCtx& x, double c, int32_t* codes, int64_t ldq, float* resi
 }
 
 // ============================================================== entropy
+// Rate model for the controller's first two steps: column j's targets in grid units taken as
+// N(0, (g_j / c)^2) with g_j = std(W column j) U_jj (the high-rate reading of WaterSIC's equal
+// per-column distortion), rounded to integers and pooled over the columns. The pooled entropy of
+// that mixture follows the measured H(c) of SIC codes much more closely in slope than the
+// high-rate law (slope -1), which ignores both the low-rate shape and the spread of the g_j.
+// g holds a few dozen quantiles of the g_j.
+double gauss_mix_entropy(const std::vector<double>& g, double c) {
+  double smax = 0.0;
+  for (double v : g) smax = std::max(smax, v / c);
+  const int Q = (int)std::ceil(6.0 * smax) + 1;
+  std::vector<double> P(2 * Q + 1, 0.0);
+  for (double gv : g) {
+    const double sd = gv / c;
+    if (!(sd > 0.0)) {
+      P[Q] += 1.0;
+      continue;
+    }
+    const double k = -1.0 / (sd * M_SQRT2);
+    double lo = 0.5 * std::erfc(k * (-Q - 0.5));  // Phi((q - 1/2) / sd) for q = -Q
+    for (int q = -Q; q <= Q; ++q) {
+      const double hi = 0.5 * std::erfc(k * (q + 0.5));
+      P[q + Q] += hi - lo;
+      lo = hi;
+    }
+  }
+  double h = 0.0;
+  const double inv = 1.0 / (double)g.size();
+  for (double v : P) {
+    const double pv = v * inv;
+    if (pv > 0.0) h -= pv * std::log2(pv);
+  }
+  return h;
+}
+
+std::vector<double> scale_quantiles(const std::vector<double>& var, const std::vector<double>& diag) {
+  std::vector<double> g(var.size());
+  for (size_t j = 0; j < var.size(); ++j) g[j] = std::sqrt(std::max(var[j], 0.0)) * std::fabs(diag[j]);
+  std::sort(g.begin(), g.end());
+  constexpr int NQ = 48;
+  std::vector<double> q(NQ);
+  for (int i = 0; i < NQ; ++i) q[i] = g[std::min(g.size() - 1, (size_t)((i + 0.5) / NQ * g.size()))];
+  return q;
+}
+
+// log2 c with model entropy R (secant on log2 c from x0, a few steps)
+double model_solve(const std::vector<double>& g, double R, double x0) {
+  double xa = x0, ha = gauss_mix_entropy(g, std::exp2(xa));
+  double slope = -1.0;
+  for (int it = 0; it < 8 && std::fabs(ha - R) > 1e-4; ++it) {
+    const double xb = xa + std::min(2.0, std::max(-2.0, (R - ha) / slope));
+    const double hb = gauss_mix_entropy(g, std::exp2(xb));
+    if (xb != xa) {
+      const double sl = (hb - ha) / (xb - xa);
+      if (sl < -0.25 && sl > -4.0) slope = sl;
+    }
+    xa = xb;
+    ha = hb;
+  }
+  return xa;
+}
+
 int entropy_of(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq, const HistWs& h,
                const int* dflags, hipStream_t st, double* H, int64_t* nsym, int* flags_out,
                int* aux_out = nullptr, int* aux2_out = nullptr) {
@@ -805,30 +879,38 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
     Carve cv(ws);
     WfWs wf = carve_wf(cv, n_out, n_in);
     SicCtx x = make_ctx(n_out, n_in, W, dtype, ldw, U, ldu, wf.sic, st);
-    WSIC_TRY(sic_setup(x, false));
 
     const double R = target_bits;
-    // starting grid scale (the setup's flags are read with it, or alone)
+    // Starting grid scale: column variances of W and U's diagonal are read back while the setup
+    // (Y = W U^T) runs; the setup's flags are read after it.
     double c0 = o.c_init;
+    std::vector<double> gq;  // quantiles of std(W_:,j) U_jj for the secant's rate model
     int setup_flags = 0;
     if (!(c0 > 0.0)) {
       WSIC_TRY(launch_colstats(W, dtype, n_out, n_in, ldw, wf.colvar + n_in, wf.colvar, st));
       WSIC_TRY(launch_delta(U, ldu, n_in, 1.0, nullptr, wf.diag, st));
       std::vector<double> var(n_in), diag(n_in);
-      const ReadPiece pv[3] = {{var.data(), wf.colvar, n_in * sizeof(double)},
-                               {diag.data(), wf.diag, n_in * sizeof(double)},
-                               {&setup_flags, x.ws.flags, sizeof(int)}};
-      WSIC_TRY(read_back(pv, 3, st));
-      WSIC_TRY(flags_status(setup_flags, "sic"));
+      const ReadPiece pv[2] = {{var.data(), wf.colvar, n_in * sizeof(double)},
+                               {diag.data(), wf.diag, n_in * sizeof(double)}};
+      WSIC_TRY(read_back_start(pv, 2, st));
+      WSIC_TRY(sic_setup(x, false));
+      WSIC_TRY(read_back_finish(pv, 2));
       double m = 0.0;
       for (int64_t j = 0; j < n_in; ++j) m += var[j] * diag[j] * diag[j];
       m /= (double)n_in;
       if (!(m > 0.0)) m = 1.0;
+      // the oracle's high-rate start (the bisection replays the oracle's sequence from it)
       c0 = std::sqrt(2.0 * M_PI * M_E * m) * std::pow(2.0, -R);
+      if (o.mode == WSIC_WF_SECANT && std::isfinite(c0)) {
+        gq = scale_quantiles(var, diag);
+        const double xm = model_solve(gq, R - 0.5 * o.rate_tol, std::log2(c0));
+        if (std::isfinite(xm)) c0 = std::exp2(xm);
+      }
     } else {
-      WSIC_TRY(read_flags(x.ws.flags, &setup_flags, st));
-      WSIC_TRY(flags_status(setup_flags, "sic"));
+      WSIC_TRY(sic_setup(x, false));
     }
+    WSIC_TRY(read_flags(x.ws.flags, &setup_flags, st));
+    WSIC_TRY(flags_status(setup_flags, "sic"));
 
     // two code buffers: the caller's and one in the workspace; `hi_buf` holds the codes of
     // the best grid scale so far with H <= R
@@ -921,12 +1003,14 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
         take(m, h, b);
       }
     } else {
-      // Secant on x = log2 c toward H = R - tol/2. The pooled entropy is not smooth at fine
-      // scales (a grid change that flips one rounding decision re-routes the interference of
-      // every column left of it), so the slope is taken only from pairs of evaluations at least
-      // SLOPE_DX apart (slope -1, the high-rate law, until such a pair exists); each step starts
-      // from the latest evaluation. Once both sides of R are known the step must land strictly
-      // inside the bracket, else -- or when the bracket has not halved in two steps -- bisect.
+      // Secant on x = log2 c toward H = R - tol/2, from a start where a Gaussian-mixture rate
+      // model (gauss_mix_entropy) gives R. The pooled entropy is not smooth at fine scales (a
+      // grid change that flips one rounding decision re-routes the interference of every
+      // column left of it), so before R is bracketed the slope is taken only from pairs of
+      // evaluations at least SLOPE_DX apart (the model's slope for the first step); each step
+      // starts from the latest evaluation. Once both sides of R are known the step must land
+      // strictly inside the bracket, else -- or when the bracket has not halved in two steps --
+      // bisect.
       constexpr double SLOPE_DX = 1.0 / 1024;
       const double Rt = R - 0.5 * o.rate_tol;
       auto accept = [&]() { return have_hi && h_hi > R - o.rate_tol; };
@@ -948,6 +1032,14 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
           if (xh - xl <= o.bracket_log2) break;
         }
         double slope = -1.0;
+        if (xs.size() == 1 && !gq.empty()) {  // one evaluation: the rate model's local slope
+          const double dx = std::min(2.0, std::max(-2.0, hb - Rt));  // the step at slope -1
+          if (std::fabs(dx) > 1e-9) {
+            const double sl = (gauss_mix_entropy(gq, std::exp2(xb + dx)) -
+                               gauss_mix_entropy(gq, std::exp2(xb))) / dx;
+            if (sl < -0.25 && sl > -4.0) slope = sl;
+          }
+        }
         for (size_t i = xs.size() - 1; i-- > 0;) {  // the latest evaluation far enough back
           if (std::fabs(xb - xs[i]) >= SLOPE_DX) {
             const double sl = (hb - hs[i]) / (xb - xs[i]);
@@ -957,6 +1049,8 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
         }
         double xn = xb + (Rt - hb) / slope;
         if (bracketed) {
+          // (interpolating between the bracket's ends instead was tried: more passes over 20
+          // targets, the ends' rates being as noisy as the slope they would give)
           if (!(xn > xl && xn < xh) || slow >= 2) {
             xn = 0.5 * (xl + xh);
             slow = 0;
@@ -987,7 +1081,6 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
         return WSIC_E_NO_BRACKET;
       }
     }
-    (void)h_lo;
     // the accepted codes must end in the caller's buffers
     if (hi_buf == 1) {
       WSIC_HIP_TRY(hipMemcpy2DAsync(codes, ldq * sizeof(int32_t), wf.codes2, ldq * sizeof(int32_t),
