@@ -57,7 +57,10 @@ enum wsic_op {
   WSIC_OP_SIC = 2,
   WSIC_OP_WATERFILL = 3,
   WSIC_OP_ENTROPY = 4,
-  WSIC_OP_DISTORTION = 5
+  WSIC_OP_DISTORTION = 5,
+  WSIC_OP_CURVATURE = 6,       /* n_out = calibration rows of one call, n_in = classes K */
+  WSIC_OP_SOFTWATER = 7,       /* wsic_softwater_waterfill on an n_out x n_in layer       */
+  WSIC_OP_SOFTWATER_DIST = 8   /* wsic_softwater_distortion                               */
 };
 
 enum wsic_dmode { WSIC_D_RESID = 0, WSIC_D_DIRECT = 1 };
@@ -184,6 +187,63 @@ int wsic_distortion(const void* W, int dtype, int64_t n_out, int64_t n_in, int64
                     const float* resid, int64_t ldr, int mode, double* D_out,
                     void* W_hat, int w_hat_dtype, int64_t ldh,
                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------------------------
+ * SoftWater: class-aware rate allocation for a softmax output layer (web page "SoftWater:
+ * Class-Aware Rate Allocation for Softmax Quantization", Portuguese technical summary, §2).
+ * The layer W (K classes x n inputs, logits W x) is quantized by SIC on the grids
+ *     Delta_kj = c / (sqrt(lambda_k) U_jj),   lambda_k = E[p~_k (1 - p~_k)],
+ * [SoftWater §2 "Aproximação Tratável"], p = softmax(W x) over the calibration inputs, mixed
+ * with the uniform distribution: p~ = (1 - smoothing) p + smoothing / K [§2 "Prior de
+ * Suavização"]. The distortion is the second-order KL estimate
+ *     D = 1/2 sum_k lambda_k (w_k - w_hat_k) Sigma (w_k - w_hat_k)^T   [§2 "Derivação do Objetivo"].
+ * ---------------------------------------------------------------------------------------------
+ */
+
+/*
+ * Class curvatures from one chunk of calibration inputs, accumulated like wsic_covariance:
+ *     lambda <- beta * lambda + alpha * sum_{rows x} p~(x) (1 - p~(x))     (elementwise, K)
+ * Pass alpha = 1/N_total for every chunk, beta = 0 for the first and 1 afterwards.
+ * X: rows x n_in, ldx >= n_in; W: n_classes x n_in, ldw >= n_in; both of `dtype`.
+ * lambda: n_classes fp64 (device). smoothing in [0, 1].
+ * bf16 inputs with n_in, ldx, ldw multiples of 8 (16-byte aligned) run the logits on bf16 MFMA
+ * with fp32 sums; other shapes and f32 inputs sum in fp64. The logits of the chunk are kept in
+ * the workspace (rows x K fp32): split large calibration sets into chunks of rows.
+ * Workspace: wsic_workspace_bytes(WSIC_OP_CURVATURE, rows, n_classes).
+ * Errors: WSIC_E_INVAL; WSIC_E_NONFINITE (X or W holds NaN/Inf, or the result is not finite).
+ */
+int wsic_softmax_curvature(const void* X, int dtype, int64_t rows, int64_t n_in, int64_t ldx,
+                           const void* W, int64_t n_classes, int64_t ldw, double smoothing,
+                           double alpha, double beta, double* lambda, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * Waterfilling with the class-aware grids [SoftWater §2 "Implementação": SIC as in WaterSIC,
+ * rows rescaled per class]: as wsic_waterfill, with row k's steps divided by sqrt(lambda[k]).
+ * lambda: n_out fp64 (device), every entry positive and finite (else WSIC_E_INVAL).
+ * resid (nullable) holds the residuals of the rescaled rows, sqrt(lambda_k) (t_kj - Delta_kj
+ * q_kj), so that sum_j U_jj^2 sum_k resid_kj^2 = 2 D.
+ * Workspace: wsic_workspace_bytes(WSIC_OP_SOFTWATER, n_out, n_in).
+ */
+int wsic_softwater_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                             const double* U, int64_t ldu, const double* lambda,
+                             double target_bits, const wsic_wf_opts* opts, double* c_out,
+                             double* rate_out, int32_t* passes_out, int32_t* codes, int64_t ldq,
+                             float* resid, int64_t ldr, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * KL distortion estimate of a SoftWater quantization [SoftWater §2 "Derivação do Objetivo"]:
+ * *D_out (host) = 1/2 sum_j U_jj^2 sum_k resid_kj^2 from the residuals returned by
+ * wsic_softwater_waterfill (resid required). W_hat (out, nullable): c q_kj / (sqrt(lambda_k)
+ * U_jj) as w_hat_dtype, ldh >= n_in.
+ * Workspace: wsic_workspace_bytes(WSIC_OP_SOFTWATER_DIST, n_out, n_in).
+ */
+int wsic_softwater_distortion(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
+                              const double* U, int64_t ldu, double c, const double* lambda,
+                              const float* resid, int64_t ldr, double* D_out, void* W_hat,
+                              int w_hat_dtype, int64_t ldh, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /*
  * Kernel timing. While enabled, every kernel launch is bracketed by HIP events on its own

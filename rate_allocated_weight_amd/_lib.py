@@ -20,7 +20,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "wsic.h")
 
 OK, E_INVAL, E_NOT_PD, E_NONFINITE, E_NO_BRACKET, E_RANGE, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7
 F32, BF16 = 0, 1
-OP_COVARIANCE, OP_CHOLESKY, OP_SIC, OP_WATERFILL, OP_ENTROPY, OP_DISTORTION = range(6)
+(OP_COVARIANCE, OP_CHOLESKY, OP_SIC, OP_WATERFILL, OP_ENTROPY, OP_DISTORTION, OP_CURVATURE,
+ OP_SOFTWATER, OP_SOFTWATER_DIST) = range(9)
 D_RESID, D_DIRECT = 0, 1
 WF_AUTO, WF_SECANT, WF_BISECT = 0, 1, 2
 
@@ -57,6 +58,13 @@ _SIGS = {
     "wsic_entropy": (ctypes.c_int, [_p, _i64, _i64, _i64, ctypes.POINTER(_d), ctypes.POINTER(_i64), _p, _sz, _p]),
     "wsic_distortion": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, _i64, _d, _p, _i64,
                                        ctypes.c_int, ctypes.POINTER(_d), _p, ctypes.c_int, _i64, _p, _sz, _p]),
+    "wsic_softmax_curvature": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _d, _d, _d,
+                                              _p, _p, _sz, _p]),
+    "wsic_softwater_waterfill": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, _d,
+                                                ctypes.POINTER(WfOpts), ctypes.POINTER(_d), ctypes.POINTER(_d),
+                                                ctypes.POINTER(ctypes.c_int32), _p, _i64, _p, _i64, _p, _sz, _p]),
+    "wsic_softwater_distortion": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i64, _d, _p, _p, _i64,
+                                                 ctypes.POINTER(_d), _p, ctypes.c_int, _i64, _p, _sz, _p]),
     "wsic_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "wsic_profile_reset": (ctypes.c_int, []),
     "wsic_profile_select": (ctypes.c_int, [ctypes.c_char_p]),
@@ -264,6 +272,86 @@ def distortion(W: torch.Tensor, codes: torch.Tensor, U: torch.Tensor, c: float,
         _rowmajor(resid) if resid is not None else n_in, D_DIRECT if mode == "direct" else D_RESID,
         ctypes.byref(d), _p(w_hat.data_ptr() if w_hat is not None else 0), wdt,
         _rowmajor(w_hat) if w_hat is not None else n_in, *_ws_args(ws), _stream(W)))
+    return d.value, w_hat
+
+
+# ------------------------------------------------------------------------------ SoftWater
+def softmax_curvature(X: torch.Tensor, W: torch.Tensor, smoothing: float = 0.0,
+                      lam: Optional[torch.Tensor] = None, alpha: Optional[float] = None,
+                      beta: float = 0.0, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """lambda <- beta*lambda + alpha * sum over rows of X of p~(1 - p~), p~ the smoothed softmax
+    of W x (alpha defaults to 1/rows: the mean over this chunk)."""
+    _need_cuda(X, W)
+    if X.dtype != W.dtype:
+        raise TypeError("X and W must have the same dtype")
+    rows, n = X.shape
+    K = W.shape[0]
+    if W.shape[1] != n:
+        raise ValueError("W must have as many columns as X")
+    if lam is None:
+        lam = torch.zeros(K, dtype=torch.float64, device=X.device)
+    ws = ws if ws is not None else workspace(OP_CURVATURE, rows, K, X.device)
+    a = 1.0 / rows if alpha is None else float(alpha)
+    _check(lib().wsic_softmax_curvature(_p(X.data_ptr()), _dtype_code(X), rows, n, _rowmajor(X), _p(W.data_ptr()),
+                                        K, _rowmajor(W), float(smoothing), a, float(beta), _p(lam.data_ptr()),
+                                        *_ws_args(ws), _stream(X)))
+    return lam
+
+
+def softmax_curvature_chunks(chunks: Sequence[torch.Tensor], W: torch.Tensor, smoothing: float = 0.0,
+                             ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Class curvatures over streamed row chunks (the mean over all rows)."""
+    n_total = sum(int(c.shape[0]) for c in chunks)
+    lam = None
+    for i, c in enumerate(chunks):
+        if ws is None or ws.numel() < workspace_bytes(OP_CURVATURE, c.shape[0], W.shape[0]):
+            ws = workspace(OP_CURVATURE, c.shape[0], W.shape[0], c.device)
+        lam = softmax_curvature(c, W, smoothing, lam, alpha=1.0 / n_total, beta=0.0 if i == 0 else 1.0, ws=ws)
+    return lam
+
+
+def softwater_waterfill(W: torch.Tensor, U: torch.Tensor, lam: torch.Tensor, target_bits: float, *,
+                        mode: str = "auto", rate_tol: float = 8e-5, bracket_log2: float = 2.0 ** -20,
+                        max_passes: int = 64, c_init: float = 0.0, want_resid: bool = True,
+                        ws: Optional[torch.Tensor] = None) -> Dict[str, object]:
+    """Waterfilling on the class-aware grids c / (sqrt(lam_k) U_jj)."""
+    _need_cuda(W, U, lam)
+    n_out, n_in = W.shape
+    if lam.dtype != torch.float64 or lam.numel() != n_out:
+        raise ValueError("lam must be float64 with one entry per row of W")
+    codes = torch.empty((n_out, n_in), dtype=torch.int32, device=W.device)
+    resid = torch.empty((n_out, n_in), dtype=torch.float32, device=W.device) if want_resid else None
+    ws = ws if ws is not None else workspace(OP_SOFTWATER, n_out, n_in, W.device)
+    opts = WfOpts(rate_tol, bracket_log2, max_passes, _MODES[mode], c_init)
+    c_out, rate_out, passes = _d(0), _d(0), ctypes.c_int32(0)
+    _check(lib().wsic_softwater_waterfill(
+        _p(W.data_ptr()), _dtype_code(W), n_out, n_in, _rowmajor(W), _p(U.data_ptr()), _rowmajor(U),
+        _p(lam.data_ptr()), float(target_bits), ctypes.byref(opts), ctypes.byref(c_out), ctypes.byref(rate_out),
+        ctypes.byref(passes), _p(codes.data_ptr()), _rowmajor(codes),
+        _p(resid.data_ptr() if resid is not None else 0), _rowmajor(resid) if resid is not None else n_in,
+        *_ws_args(ws), _stream(W)))
+    return {"c": c_out.value, "rate": rate_out.value, "passes": int(passes.value), "codes": codes,
+            "resid": resid}
+
+
+def softwater_distortion(codes: torch.Tensor, U: torch.Tensor, c: float, lam: torch.Tensor,
+                         resid: torch.Tensor, w_hat_dtype: Optional[torch.dtype] = None,
+                         ws: Optional[torch.Tensor] = None):
+    """Second-order KL estimate 1/2 sum_k lam_k e_k Sigma e_k^T from the residuals; optionally W_hat."""
+    _need_cuda(codes, U, lam, resid)
+    n_out, n_in = codes.shape
+    w_hat = None
+    wdt = F32
+    if w_hat_dtype is not None:
+        w_hat = torch.empty((n_out, n_in), dtype=w_hat_dtype, device=codes.device)
+        wdt = _dtype_code(w_hat)
+    ws = ws if ws is not None else workspace(OP_SOFTWATER_DIST, n_out, n_in, codes.device)
+    d = _d(0)
+    _check(lib().wsic_softwater_distortion(
+        _p(codes.data_ptr()), n_out, n_in, _rowmajor(codes), _p(U.data_ptr()), _rowmajor(U), float(c),
+        _p(lam.data_ptr()), _p(resid.data_ptr()), _rowmajor(resid), ctypes.byref(d),
+        _p(w_hat.data_ptr() if w_hat is not None else 0), wdt, _rowmajor(w_hat) if w_hat is not None else n_in,
+        *_ws_args(ws), _stream(codes)))
     return d.value, w_hat
 
 

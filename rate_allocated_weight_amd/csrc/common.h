@@ -60,6 +60,7 @@ enum FlagBits : int {
   FLAG_RANGE = 2,
   FLAG_BAD_DIAG = 4,
   FLAG_OVERFLOW_LIST = 8,
+  FLAG_BAD_SCALE = 16,  // a class curvature that is not positive and finite
 };
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
@@ -192,8 +193,9 @@ int launch_gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t* A8, int64_t ld
                    int64_t ldd, int64_t plane, const double* escale, double* C, int64_t ldc,
                    double beta, hipStream_t st);
 int colstats_doubles(int64_t n_out, int64_t n_in);
+// column variances of diag(rs) W (rs nullable: W itself)
 int launch_colstats(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
-                    double* part, double* colvar, hipStream_t st);
+                    double* part, double* colvar, hipStream_t st, const double* rs = nullptr);
 
 // histogram / entropy
 constexpr int HIST_HALF = 2047;
@@ -216,9 +218,35 @@ int launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // distortion
 int launch_dist_resid(const float* resid, int64_t n_out, int64_t n_in, int64_t ldr,
                       const double* U, int64_t ldu, double* partial, int nblk, hipStream_t st);
+// W_hat_ij = c q_ij / (U_jj rs_i) (rs nullable: 1)
 int launch_dequant(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
                    const double* invd, double c, void* W_hat, int w_hat_dtype, int64_t ldh,
-                   hipStream_t st);
+                   hipStream_t st, const double* rs = nullptr);
+
+// softmax curvature (SoftWater): logits, row normalizers, per-class sums
+struct CurvArgs {
+  const void* X;
+  const void* W;
+  int dtype;
+  int64_t rows, n, ldx, K, ldw;
+  double eps, alpha, beta;
+  double* lam;       // K, in/out
+  int* flags;
+  float* Lg;         // rows x ldl logits
+  int64_t ldl;
+  float2* part;      // rows x ntn (max, sum exp) per class tile
+  float* rmax;       // rows
+  double* rinvz;     // rows
+  double* cpart;     // nchunk x K
+  bool force_generic;
+};
+void curvature_dims(int64_t rows, int64_t K, int64_t* ntn, int64_t* nchunk, int64_t* ldl);
+int launch_softmax_curvature(const CurvArgs& a, hipStream_t st);
+// s_k = sqrt(lam_k) (FLAG_BAD_SCALE unless lam_k is positive and finite)
+int launch_row_sqrt(const double* lam, int64_t n, double* s, int* flags, hipStream_t st);
+// Y[r, :] *= s[r]
+int launch_scale_rows(double* Y, int64_t n_out, int64_t n_in, int64_t ldy, const double* s,
+                      hipStream_t st);
 int launch_sum_partials(const double* partial, int64_t n, double* out, hipStream_t st);
 
 }  // namespace wsic

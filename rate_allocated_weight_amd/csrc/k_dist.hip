@@ -56,17 +56,20 @@ __global__ __launch_bounds__(256) void k_sum_partials(const double* partial, int
   if (threadIdx.x == 0) *out = red[0];
 }
 
-// W_hat_ij = Delta_j q_ij with Delta_j = c / U_jj, written as float or bf16 (round to nearest
+// W_hat_ij = Delta_ij q_ij with Delta_ij = c / (U_jj rs_i) (rs_i = 1 without class scales; the
+// SoftWater page, §2 "Aproximação Tratável", divides row i's grid by sqrt(lambda_i)), written as
+// float or bf16 (round to nearest
 // even).
 template <bool BF16>
 __global__ void k_dequant(const int32_t* __restrict__ codes, int64_t n_out, int64_t n_in,
                           int64_t ldq, const double* __restrict__ invd, double c, void* W_hat,
-                          int64_t ldh) {
+                          int64_t ldh, const double* __restrict__ rs) {
   const int64_t total = n_out * n_in;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = e / n_in, j = e % n_in;
-    const float v = (float)((c * invd[j]) * (double)codes[r * ldq + j]);
+    const double step = rs ? (c * invd[j]) / rs[r] : c * invd[j];
+    const float v = (float)(step * (double)codes[r * ldq + j]);
     if (BF16) {
       uint32_t u = __float_as_uint(v);
       u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
@@ -99,7 +102,7 @@ int launch_sum_partials(const double* partial, int64_t n, double* out, hipStream
 
 int launch_dequant(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
                    const double* invd, double c, void* W_hat, int w_hat_dtype, int64_t ldh,
-                   hipStream_t st) {
+                   hipStream_t st, const double* rs) {
   const int64_t total = n_out * n_in;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
@@ -107,10 +110,10 @@ int launch_dequant(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ld
   const double work = (double)total * (4.0 + (w_hat_dtype == WSIC_BF16 ? 2.0 : 4.0));
   if (w_hat_dtype == WSIC_BF16)
     WSIC_LAUNCH("dequant", work, st, k_dequant<true>, dim3((unsigned)blocks), dim3(256), 0, codes,
-                n_out, n_in, ldq, invd, c, W_hat, ldh);
+                n_out, n_in, ldq, invd, c, W_hat, ldh, rs);
   else
     WSIC_LAUNCH("dequant", work, st, k_dequant<false>, dim3((unsigned)blocks), dim3(256), 0, codes,
-                n_out, n_in, ldq, invd, c, W_hat, ldh);
+                n_out, n_in, ldq, invd, c, W_hat, ldh, rs);
   return WSIC_OK;
 }
 

@@ -952,7 +952,8 @@ __global__ void k_check_finite(const T* W, int64_t n_out, int64_t n_in, int64_t 
 constexpr int COLSTAT_ROWS = 256;
 template <typename T>
 __global__ __launch_bounds__(256) void k_colstats(const T* W, int64_t n_out, int64_t n_in,
-                                                  int64_t ldw, double* part) {
+                                                  int64_t ldw, double* part,
+                                                  const double* __restrict__ rs) {
   __shared__ double s1[4][64], s2[4][64];
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const int64_t j = (int64_t)blockIdx.x * 64 + tx;
@@ -961,7 +962,7 @@ __global__ __launch_bounds__(256) void k_colstats(const T* W, int64_t n_out, int
   if (j < n_in) {
     const int64_t r1 = (r0 + COLSTAT_ROWS < n_out) ? r0 + COLSTAT_ROWS : n_out;
     for (int64_t r = r0 + ty; r < r1; r += 4) {
-      const double v = (double)elem<T>(W, r * ldw + j);
+      const double v = rs ? (double)elem<T>(W, r * ldw + j) * rs[r] : (double)elem<T>(W, r * ldw + j);
       a += v;
       b = fma(v, v, b);
     }
@@ -1104,16 +1105,16 @@ int launch_check_finite(const void* W, int dtype, int64_t n_out, int64_t n_in, i
 }
 
 int launch_colstats(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
-                    double* part, double* colvar, hipStream_t st) {
+                    double* part, double* colvar, hipStream_t st, const double* rs) {
   const unsigned gx = (unsigned)((n_in + 63) / 64);
   const unsigned gy = (unsigned)((n_out + COLSTAT_ROWS - 1) / COLSTAT_ROWS);
   const double work = (double)n_out * n_in * (dtype == WSIC_BF16 ? 2.0 : 4.0);
   if (dtype == WSIC_BF16)
     WSIC_LAUNCH("colstats", work, st, k_colstats<uint16_t>, dim3(gx, gy), dim3(256), 0,
-                (const uint16_t*)W, n_out, n_in, ldw, part);
+                (const uint16_t*)W, n_out, n_in, ldw, part, rs);
   else
     WSIC_LAUNCH("colstats", work, st, k_colstats<float>, dim3(gx, gy), dim3(256), 0,
-                (const float*)W, n_out, n_in, ldw, part);
+                (const float*)W, n_out, n_in, ldw, part, rs);
   WSIC_LAUNCH("colstats", 16.0 * gy * n_in, st, k_colstats_finish,
               dim3((unsigned)((n_in + 255) / 256)), dim3(256), 0, part, n_out, n_in, (int)gy, colvar);
   return WSIC_OK;

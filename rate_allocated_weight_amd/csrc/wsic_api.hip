@@ -213,6 +213,42 @@ DistWs carve_dist(Carve& cv, int64_t n_out, int64_t n_in) {
   return d;
 }
 
+// SoftWater class scales s_r = sqrt(lambda_r) and their own check flag
+struct ScaleWs {
+  double* s;
+  int* flags;
+};
+ScaleWs carve_scales(Carve& cv, int64_t n_out) {
+  ScaleWs r;
+  r.s = cv.take<double>((size_t)n_out);
+  r.flags = cv.take<int>(FLAGS_BYTES / sizeof(int));
+  return r;
+}
+
+// softmax curvature of `rows` calibration inputs over K classes
+struct CurvWs {
+  int* flags;
+  float* Lg;
+  int64_t ldl;
+  float2* part;
+  float* rmax;
+  double* rinvz;
+  double* cpart;
+};
+CurvWs carve_curv(Carve& cv, int64_t rows, int64_t K) {
+  int64_t ntn, nchunk, ldl;
+  curvature_dims(rows, K, &ntn, &nchunk, &ldl);
+  CurvWs c;
+  c.flags = cv.take<int>(FLAGS_BYTES / sizeof(int));
+  c.Lg = cv.take<float>((size_t)rows * (size_t)ldl);
+  c.ldl = ldl;
+  c.part = cv.take<float2>((size_t)rows * (size_t)ntn);
+  c.rmax = cv.take<float>((size_t)rows);
+  c.rinvz = cv.take<double>((size_t)rows);
+  c.cpart = cv.take<double>((size_t)nchunk * (size_t)K);
+  return c;
+}
+
 size_t ws_bytes_for(int op, int64_t n_out, int64_t n_in) {
   Carve cv(nullptr);
   switch (op) {
@@ -235,6 +271,17 @@ size_t ws_bytes_for(int op, int64_t n_out, int64_t n_in) {
       break;
     case WSIC_OP_DISTORTION:
       carve_dist(cv, n_out, n_in);
+      break;
+    case WSIC_OP_CURVATURE:
+      carve_curv(cv, n_out, n_in);
+      break;
+    case WSIC_OP_SOFTWATER:
+      carve_wf(cv, n_out, n_in);
+      carve_scales(cv, n_out);
+      break;
+    case WSIC_OP_SOFTWATER_DIST:
+      carve_dist(cv, n_out, n_in);
+      carve_scales(cv, n_out);
       break;
     default:
       return 0;
@@ -357,6 +404,10 @@ int flags_status(int f, const char* what) {
     set_error("%s: NaN or Inf in an input", what);
     return WSIC_E_NONFINITE;
   }
+  if (f & FLAG_BAD_SCALE) {
+    set_error("%s: a class curvature is not positive and finite", what);
+    return WSIC_E_INVAL;
+  }
   if (f & FLAG_BAD_DIAG) {
     set_error("%s: U has a diagonal entry that is not positive and finite", what);
     return WSIC_E_INVAL;
@@ -381,11 +432,12 @@ struct SicCtx {
   bool i8;             // interference by the exact int8 limb product (else fp64 MFMA)
   double guard_scale;  // multiplies the error bound (testing hook; 1 in normal use)
   bool super_launch;   // int8 mode: a range of up to SUPER blocks in one launch (else per block)
+  const double* rs;    // class scales: row r of Y = W U^T is multiplied by rs[r] (nullable)
 };
 
 SicCtx make_ctx(int64_t n_out, int64_t n_in, const void* W, int dtype, int64_t ldw,
                 const double* U, int64_t ldu, const SicWs& ws, hipStream_t st) {
-  SicCtx x{n_out, n_in, W, dtype, ldw, U, ldu, ws, st, true, 1.0, true};
+  SicCtx x{n_out, n_in, W, dtype, ldw, U, ldu, ws, st, true, 1.0, true, nullptr};
   if (const char* e = std::getenv("WSIC_FP64_TRAIL")) x.i8 = (e[0] == '0');
   if (const char* e = std::getenv("WSIC_SUPER_BLOCKS")) x.super_launch = (e[0] != '0');
   if (const char* e = std::getenv("WSIC_GUARD_SCALE")) {
@@ -410,6 +462,9 @@ int sic_setup(const SicCtx& x, bool read_now = true) {
   const double work = (double)x.n_out * (double)x.n_in * (double)(x.n_in + 1);
   WSIC_TRY(launch_gemm_y(x.dtype, x.n_out, x.n_in, x.n_in, x.W, x.ldw, x.U, x.ldu, x.ws.Y, x.n_in,
                          work, x.st));
+  // class-aware grids c / (s_r U_jj) are the plain grids of the rows s_r w_r, whose Y rows are
+  // s_r times those of w_r (SoftWater page, §2 "Aproximação Tratável")
+  if (x.rs) WSIC_TRY(launch_scale_rows(x.ws.Y, x.n_out, x.n_in, x.n_in, x.rs, x.st));
   if (!read_now) return WSIC_OK;
   int f = 0;
   WSIC_TRY(read_flags(x.ws.flags, &f, x.st));
@@ -847,11 +902,12 @@ int wsic_sic_quantize(const void* W, int dtype, int64_t n_out, int64_t n_in, int
   }
 }
 
-int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
-                   const double* U, int64_t ldu, double target_bits, const wsic_wf_opts* opts,
-                   double* c_out, double* rate_out, int32_t* passes_out, int32_t* codes,
-                   int64_t ldq, float* resid, int64_t ldr, void* ws, size_t ws_bytes,
-                   void* stream) {
+// The rate controller over SIC passes; lam (nullable) gives SoftWater's class curvatures.
+static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_out, int64_t n_in,
+                         int64_t ldw, const double* U, int64_t ldu, double target_bits,
+                         const wsic_wf_opts* opts, double* c_out, double* rate_out,
+                         int32_t* passes_out, int32_t* codes, int64_t ldq, float* resid,
+                         int64_t ldr, void* ws, size_t ws_bytes, void* stream) {
   try {
     clear_error();
     WSIC_TRY(check_layer(W, dtype, n_out, n_in, ldw));
@@ -874,11 +930,20 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
     if (o.mode == WSIC_WF_AUTO)
       o.mode = (n_out * n_in < WSIC_WF_AUTO_PARAMS) ? WSIC_WF_BISECT : WSIC_WF_SECANT;
     const bool trace = std::getenv("WSIC_TRACE") != nullptr;
-    WSIC_TRY(check_ws(WSIC_OP_WATERFILL, n_out, n_in, ws, ws_bytes));
+    WSIC_TRY(check_ws(lam ? WSIC_OP_SOFTWATER : WSIC_OP_WATERFILL, n_out, n_in, ws, ws_bytes));
     hipStream_t st = (hipStream_t)stream;
     Carve cv(ws);
     WfWs wf = carve_wf(cv, n_out, n_in);
     SicCtx x = make_ctx(n_out, n_in, W, dtype, ldw, U, ldu, wf.sic, st);
+    if (lam) {
+      const ScaleWs sc = carve_scales(cv, n_out);
+      WSIC_TRY(launch_fill_zero(sc.flags, FLAGS_BYTES, st));
+      WSIC_TRY(launch_row_sqrt(lam, n_out, sc.s, sc.flags, st));
+      int sf = 0;
+      WSIC_TRY(read_flags(sc.flags, &sf, st));
+      WSIC_TRY(flags_status(sf, "softwater_waterfill"));
+      x.rs = sc.s;
+    }
 
     const double R = target_bits;
     // Starting grid scale: column variances of W and U's diagonal are read back while the setup
@@ -887,7 +952,7 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
     std::vector<double> gq;  // quantiles of std(W_:,j) U_jj for the secant's rate model
     int setup_flags = 0;
     if (!(c0 > 0.0)) {
-      WSIC_TRY(launch_colstats(W, dtype, n_out, n_in, ldw, wf.colvar + n_in, wf.colvar, st));
+      WSIC_TRY(launch_colstats(W, dtype, n_out, n_in, ldw, wf.colvar + n_in, wf.colvar, st, x.rs));
       WSIC_TRY(launch_delta(U, ldu, n_in, 1.0, nullptr, wf.diag, st));
       std::vector<double> var(n_in), diag(n_in);
       const ReadPiece pv[2] = {{var.data(), wf.colvar, n_in * sizeof(double)},
@@ -1096,6 +1161,122 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
     return rc;
   } catch (...) {
     set_error("waterfill: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                   const double* U, int64_t ldu, double target_bits, const wsic_wf_opts* opts,
+                   double* c_out, double* rate_out, int32_t* passes_out, int32_t* codes,
+                   int64_t ldq, float* resid, int64_t ldr, void* ws, size_t ws_bytes,
+                   void* stream) {
+  return waterfill_run(nullptr, W, dtype, n_out, n_in, ldw, U, ldu, target_bits, opts, c_out,
+                       rate_out, passes_out, codes, ldq, resid, ldr, ws, ws_bytes, stream);
+}
+
+int wsic_softwater_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                             const double* U, int64_t ldu, const double* lambda,
+                             double target_bits, const wsic_wf_opts* opts, double* c_out,
+                             double* rate_out, int32_t* passes_out, int32_t* codes, int64_t ldq,
+                             float* resid, int64_t ldr, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!lambda) {
+    set_error("softwater_waterfill: lambda is required");
+    return WSIC_E_INVAL;
+  }
+  return waterfill_run(lambda, W, dtype, n_out, n_in, ldw, U, ldu, target_bits, opts, c_out,
+                       rate_out, passes_out, codes, ldq, resid, ldr, ws, ws_bytes, stream);
+}
+
+int wsic_softmax_curvature(const void* X, int dtype, int64_t rows, int64_t n_in, int64_t ldx,
+                           const void* W, int64_t n_classes, int64_t ldw, double smoothing,
+                           double alpha, double beta, double* lambda, void* ws, size_t ws_bytes,
+                           void* stream) {
+  try {
+    clear_error();
+    if (!X || !W || !lambda || rows <= 0 || n_in <= 0 || n_classes <= 0 || ldx < n_in ||
+        ldw < n_in || (dtype != WSIC_F32 && dtype != WSIC_BF16) || !(smoothing >= 0.0) ||
+        !(smoothing <= 1.0) || !std::isfinite(alpha) || !std::isfinite(beta)) {
+      set_error("softmax_curvature: bad argument");
+      return WSIC_E_INVAL;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_CURVATURE, rows, n_classes, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    Carve cv(ws);
+    const CurvWs cw = carve_curv(cv, rows, n_classes);
+    WSIC_TRY(launch_fill_zero(cw.flags, FLAGS_BYTES, st));
+    WSIC_TRY(launch_check_finite(X, dtype, rows, n_in, ldx, cw.flags, st));
+    WSIC_TRY(launch_check_finite(W, dtype, n_classes, n_in, ldw, cw.flags, st));
+    int f = 0;
+    WSIC_TRY(read_flags(cw.flags, &f, st));
+    WSIC_TRY(flags_status(f, "softmax_curvature"));
+    CurvArgs a{};
+    a.X = X;
+    a.W = W;
+    a.dtype = dtype;
+    a.rows = rows;
+    a.n = n_in;
+    a.ldx = ldx;
+    a.K = n_classes;
+    a.ldw = ldw;
+    a.eps = smoothing;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.lam = lambda;
+    a.flags = cw.flags;
+    a.Lg = cw.Lg;
+    a.ldl = cw.ldl;
+    a.part = cw.part;
+    a.rmax = cw.rmax;
+    a.rinvz = cw.rinvz;
+    a.cpart = cw.cpart;
+    // testing hook: WSIC_LOGITS_GENERIC=1 takes the fp64 VALU logits for bf16 inputs too
+    if (const char* e = std::getenv("WSIC_LOGITS_GENERIC")) a.force_generic = (e[0] == '1');
+    WSIC_TRY(launch_softmax_curvature(a, st));
+    WSIC_TRY(read_flags(cw.flags, &f, st));
+    return flags_status(f, "softmax_curvature");
+  } catch (...) {
+    set_error("softmax_curvature: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_softwater_distortion(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
+                              const double* U, int64_t ldu, double c, const double* lambda,
+                              const float* resid, int64_t ldr, double* D_out, void* W_hat,
+                              int w_hat_dtype, int64_t ldh, void* ws, size_t ws_bytes,
+                              void* stream) {
+  try {
+    clear_error();
+    if (!codes || n_out <= 0 || n_in <= 0 || ldq < n_in || !U || ldu < n_in || !(c > 0.0) ||
+        !std::isfinite(c) || !lambda || !resid || ldr < n_in || !D_out ||
+        (W_hat && (ldh < n_in || (w_hat_dtype != WSIC_F32 && w_hat_dtype != WSIC_BF16)))) {
+      set_error("softwater_distortion: bad argument");
+      return WSIC_E_INVAL;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_SOFTWATER_DIST, n_out, n_in, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    Carve cv(ws);
+    DistWs d = carve_dist(cv, n_out, n_in);
+    const ScaleWs sc = carve_scales(cv, n_out);
+    WSIC_TRY(launch_fill_zero(d.flags, FLAGS_BYTES, st));
+    WSIC_TRY(launch_prep(U, ldu, n_in, d.invd, d.flags, st));
+    WSIC_TRY(launch_row_sqrt(lambda, n_out, sc.s, d.flags, st));
+    if (W_hat)
+      WSIC_TRY(launch_dequant(codes, n_out, n_in, ldq, d.invd, c, W_hat, w_hat_dtype, ldh, st, sc.s));
+    // the residuals of the class-aware SIC are those of the rows s_r w_r: sum_j U_jj^2 sum_r r_rj^2
+    // is sum_r lambda_r e_r Sigma e_r^T, twice the KL estimate
+    const int64_t np = ((n_in + 255) / 256) * ((n_out + 255) / 256);
+    WSIC_TRY(launch_dist_resid(resid, n_out, n_in, ldr, U, ldu, d.partial, (int)np, st));
+    WSIC_TRY(launch_sum_partials(d.partial, np, d.out, st));
+    int f = 0;
+    double D2 = 0.0;
+    const ReadPiece pd[2] = {{&D2, d.out, sizeof(double)}, {&f, d.flags, sizeof(int)}};
+    WSIC_TRY(read_back(pd, 2, st));
+    *D_out = 0.5 * D2;
+    return flags_status(f, "softwater_distortion");
+  } catch (...) {
+    set_error("softwater_distortion: internal exception");
     return WSIC_E_INVAL;
   }
 }
