@@ -48,6 +48,8 @@ FAMILIES = {
     "sic_leaf": ("hbm", "hbm", 1e-9),
     "hist": ("hbm", "hbm", 1e-9),
     "dist_resid": ("hbm", "hbm", 1e-9),
+    "logits_bf16": ("mfma", "mfma_bf16", 1e-12),
+    "curvature": ("hbm", "hbm", 1e-9),
 }
 
 
@@ -81,6 +83,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=32)
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
+    ap.add_argument("--softwater", action="store_true",
+                    help="class-aware grids of a softmax head: class curvatures from the calibration "
+                         "inputs, then waterfilling on c / (sqrt(lambda_k) U_jj) and the KL estimate")
+    ap.add_argument("--smoothing", type=float, default=0.05,
+                    help="weight of the uniform distribution mixed into the calibration softmax")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run one device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -140,6 +147,51 @@ def cpu_baseline(layer, target, sample_rows):
     }
 
 
+def cpu_baseline_softwater(layer, target, sample_rows, smoothing, curv_rows=64):
+    """The SoftWater oracle on the host: full covariance and factorization, class curvatures on
+    `curv_rows` calibration rows (scaled to all rows), the waterfill search on `sample_rows`
+    classes (scaled to all classes)."""
+    import numpy as np
+
+    from oracle import softwater as sw
+    from oracle import watersic as ws
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = min(16, len(os.sched_getaffinity(0)))
+    ctx = threadpool_limits(cores) if threadpool_limits else None
+    try:
+        t0 = time.perf_counter()
+        sigma = ws.covariance(layer.x_chunks)
+        t1 = time.perf_counter()
+        L, info = ws.cholesky_lower(sigma)
+        t2 = time.perf_counter()
+        X0 = np.asarray(layer.x_chunks[0][:curv_rows], dtype=np.float64)
+        lam = sw.softmax_curvature([X0], layer.w, smoothing)
+        t3 = time.perf_counter()
+        rows = np.linspace(0, layer.n_out - 1, sample_rows).astype(np.int64)
+        wf = sw.waterfill(layer.w[rows], L, lam[rows], target)
+        t4 = time.perf_counter()
+    finally:
+        if ctx is not None:
+            ctx.unregister() if hasattr(ctx, "unregister") else None
+    t_cov, t_chol, t_curv, t_wf = t1 - t0, t2 - t1, t3 - t2, t4 - t3
+    t_full = t_cov + t_chol + t_curv * (layer.n_rows / curv_rows) + t_wf * (layer.n_out / sample_rows)
+    return {
+        "value": layer.n_out * layer.n_in / t_full / 1e9,
+        "unit": "Gparams/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"full covariance ({t_cov:.2f} s) and Cholesky ({t_chol:.2f} s) of {layer.n_rows}x{layer.n_in}; "
+                   f"class curvatures on {curv_rows} of {layer.n_rows} calibration rows ({t_curv:.2f} s, scaled "
+                   f"by {layer.n_rows / curv_rows:.0f}); waterfill on {sample_rows} of {layer.n_out} classes "
+                   f"({t_wf:.2f} s, {len(wf['trace'])} passes, scaled by {layer.n_out / sample_rows:.0f})"),
+        "seconds": round(t_cov + t_chol + t_curv + t_wf, 2),
+    }
+
+
 def main():
     args = parse()
     if args.copy_calibration_mib > 0:
@@ -178,14 +230,20 @@ def main():
     ws_wf = L.workspace(L.OP_WATERFILL, n_out, n_in, dev)
     ws_ent = L.workspace(L.OP_ENTROPY, n_out, n_in, dev)
     ws_dist = L.workspace(L.OP_DISTORTION, n_out, n_in, dev)
+    sw = args.softwater
+    if sw:
+        ws_wf = L.workspace(L.OP_SOFTWATER, n_out, n_in, dev)
+        ws_dist = L.workspace(L.OP_SOFTWATER_DIST, n_out, n_in, dev)
+        ws_curv = L.workspace(L.OP_CURVATURE, max(int(c.shape[0]) for c in X), n_out, dev)
+        lam = torch.empty(n_out, dtype=torch.float64, device=dev)
 
     # phase boundaries on the library's stream (the current torch stream)
-    phase_names = ("covariance", "cholesky", "waterfill", "entropy+distortion")
+    phase_names = ("covariance", "cholesky", "curvature", "waterfill", "entropy+distortion")
     phase_ms = {k: 0.0 for k in phase_names}
     phase_events = []
 
     def step(record=False):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if record else None
         if record:
             ev[0].record()
         for i, c in enumerate(X):
@@ -195,13 +253,27 @@ def main():
         U, _ = L.cholesky(sigma, ws=ws_chol)
         if record:
             ev[2].record()
-        wf = L.waterfill(W, U, args.target, mode=args.mode, codes=codes, resid=resid, ws=ws_wf)
+        if sw:
+            for i, c in enumerate(X):
+                L.softmax_curvature(c, W, args.smoothing, lam, alpha=1.0 / n_rows, beta=0.0 if i == 0 else 1.0,
+                                    ws=ws_curv)
         if record:
             ev[3].record()
-        h, _ = L.entropy(codes, ws=ws_ent)
-        D, _ = L.distortion(W, codes, U, wf["c"], resid=resid, ws=ws_dist)
+        if sw:
+            wf = L.softwater_waterfill(W, U, lam, args.target, mode=args.mode, codes=codes, resid=resid,
+                                       ws=ws_wf)
+        else:
+            wf = L.waterfill(W, U, args.target, mode=args.mode, codes=codes, resid=resid, ws=ws_wf)
         if record:
             ev[4].record()
+        if sw:
+            h, _ = L.entropy(wf["codes"], ws=ws_ent)
+            D, _ = L.softwater_distortion(wf["codes"], U, wf["c"], lam, wf["resid"], ws=ws_dist)
+        else:
+            h, _ = L.entropy(codes, ws=ws_ent)
+            D, _ = L.distortion(W, codes, U, wf["c"], resid=resid, ws=ws_dist)
+        if record:
+            ev[5].record()
             phase_events.append(ev)
         return wf, h, D
 
@@ -266,7 +338,7 @@ def main():
     for ev in phase_events:
         for k, name in enumerate(phase_names):
             phase_ms[name] += ev[k].elapsed_time(ev[k + 1]) / args.steps
-    ms_from_u = phase_ms["waterfill"] + phase_ms["entropy+distortion"]
+    ms_from_u = phase_ms["curvature"] + phase_ms["waterfill"] + phase_ms["entropy+distortion"]
 
     kernels = {}
     roofline = None
@@ -291,8 +363,17 @@ def main():
                         "avg_launch_us": v["avg_us"], "launches": v["launches"],
                         "share_of_step": round(v["ms"] / (elapsed * 1e3), 4)}
 
+    if sw:
+        metric = (f"Gparams/s SoftWater class-aware waterfill+SIC ({n_out}x{n_in} softmax head, "
+                  f"{args.target:g} bit/param); % MFMA/HBM roofline")
+        step_name = "covariance+cholesky+class curvatures+class-aware waterfill+entropy+KL distortion"
+    else:
+        metric = "Gparams/s waterfill+SIC quantize (4096x4096, 2 bit/param); % MFMA/HBM roofline"
+        step_name = "covariance+cholesky+waterfill+entropy+distortion"
+    if not sw:
+        phase_ms.pop("curvature")
     out = {
-        "metric": "Gparams/s waterfill+SIC quantize (4096x4096, 2 bit/param); % MFMA/HBM roofline",
+        "metric": metric,
         "value": round(n_out * n_in * args.steps / elapsed / 1e9, 6),
         "unit": "Gparams/s",
         "n_gpus": 1,
@@ -306,7 +387,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "n_out": n_out, "n_in": n_in, "calib_rows": n_rows,
                    "w_dtype": layer.dtype, "target_bits": args.target, "controller": args.mode,
-                   "step": "covariance+cholesky+waterfill+entropy+distortion"},
+                   "step": step_name, **({"smoothing": args.smoothing} if sw else {})},
         "result": {"c": wf["c"], "rate": wf["rate"], "entropy": h, "passes": wf["passes"], "D": D},
         "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
         "value_from_U": round(n_out * n_in / (ms_from_u * 1e-3) / 1e9, 6),
@@ -317,7 +398,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(layer, args.target, args.cpu_sample_rows)
+        out["cpu_baseline"] = (cpu_baseline_softwater(layer, args.target, args.cpu_sample_rows, args.smoothing)
+                               if sw else cpu_baseline(layer, args.target, args.cpu_sample_rows))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -313,14 +313,17 @@ def softmax_curvature_chunks(chunks: Sequence[torch.Tensor], W: torch.Tensor, sm
 def softwater_waterfill(W: torch.Tensor, U: torch.Tensor, lam: torch.Tensor, target_bits: float, *,
                         mode: str = "auto", rate_tol: float = 8e-5, bracket_log2: float = 2.0 ** -20,
                         max_passes: int = 64, c_init: float = 0.0, want_resid: bool = True,
+                        codes: Optional[torch.Tensor] = None, resid: Optional[torch.Tensor] = None,
                         ws: Optional[torch.Tensor] = None) -> Dict[str, object]:
     """Waterfilling on the class-aware grids c / (sqrt(lam_k) U_jj)."""
     _need_cuda(W, U, lam)
     n_out, n_in = W.shape
     if lam.dtype != torch.float64 or lam.numel() != n_out:
         raise ValueError("lam must be float64 with one entry per row of W")
-    codes = torch.empty((n_out, n_in), dtype=torch.int32, device=W.device)
-    resid = torch.empty((n_out, n_in), dtype=torch.float32, device=W.device) if want_resid else None
+    if codes is None:
+        codes = torch.empty((n_out, n_in), dtype=torch.int32, device=W.device)
+    if want_resid and resid is None:
+        resid = torch.empty((n_out, n_in), dtype=torch.float32, device=W.device)
     ws = ws if ws is not None else workspace(OP_SOFTWATER, n_out, n_in, W.device)
     opts = WfOpts(rate_tol, bracket_log2, max_passes, _MODES[mode], c_init)
     c_out, rate_out, passes = _d(0), _d(0), ctypes.c_int32(0)
