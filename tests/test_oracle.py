@@ -331,3 +331,66 @@ def test_quantize_layer_end_to_end_small():
     out = oracle.quantize_layer(lay.w, lay.x_chunks, 2.0)
     assert out["rate"] <= 2.0
     assert out["D"] == pytest.approx(out["D_resid"], rel=1e-10)
+
+
+# ------------------------------------------------------------------ per-column rate and the limit
+def test_entropy_columns_closed_forms():
+    """Each column uniform over 2^k symbols has k bits; a constant column has 0; the pooled
+    entropy is at least the mean column entropy (concavity of entropy under mixing)."""
+    rng = np.random.default_rng(0)
+    k = [1, 3, 0, 5]
+    cols = []
+    for kk in k:
+        v = np.repeat(np.arange(2 ** kk), 64 // 2 ** kk * 4)[:256] + 7 * kk
+        cols.append(rng.permutation(v))
+    q = np.stack(cols, axis=1)
+    assert oracle.entropy_bits_columns(q) == pytest.approx(np.mean(k), abs=1e-12)
+    r = rng.integers(-6, 7, size=(500, 9)) * rng.integers(1, 4, size=9)[None, :]
+    assert oracle.entropy_bits(r) >= oracle.entropy_bits_columns(r) - 1e-12
+
+
+def test_gaussian_rate_identity_and_zero():
+    """Sigma = I: R(D) = 1/2 log2(var / D) for D < var, 0 beyond."""
+    mu = np.ones(7)
+    for D in (0.01, 0.3, 0.9):
+        assert oracle.gaussian_rate(mu, 1.3, D) == pytest.approx(0.5 * np.log2(1.3 / D), rel=1e-12)
+    assert oracle.gaussian_rate(mu, 1.3, 1.3) == 0.0
+
+
+def test_gaussian_rate_water_level_by_hand():
+    """mu = (1, 0.01), var 1, D = 0.1 per weight: the water level theta solves
+    (min(theta, 1) + min(theta, 0.01)) / 2 = 0.1, theta = 0.19; only the first component is
+    coded: R = (1/2)(1/2) log2(1 / 0.19)."""
+    r = oracle.gaussian_rate(np.array([1.0, 0.01]), 1.0, 0.1)
+    assert r == pytest.approx(0.25 * np.log2(1.0 / 0.19), rel=1e-10)
+
+
+def test_gaussian_rate_high_rate_is_log_det():
+    """Below the smallest eigenvalue the water level is D itself and the rate is
+    1/2 log2(var/D) + (1/n) sum_j log2 l_jj (det Sigma from the Cholesky diagonal)."""
+    rng = np.random.default_rng(1)
+    A = rng.standard_normal((10, 10))
+    sigma = A @ A.T + 0.5 * np.eye(10)
+    L, info = oracle.cholesky_lower(sigma)
+    mu = np.linalg.eigvalsh(sigma)
+    D = 0.1 * 0.7 * mu.min()
+    assert oracle.gaussian_rate(mu, 0.7, D) == pytest.approx(oracle.gaussian_rate_high(np.diag(L), 0.7, D),
+                                                             rel=1e-10)
+
+
+def test_watersic_gap_at_high_rate():
+    """[WaterSIC, §3 Limiti teorici]: with per-column entropy coding the rate of WaterSIC sits
+    1/2 log2(2 pi e / 12) = 0.2546 bit above the Gaussian limit at high rate (sanity, +-0.03)."""
+    rng = np.random.default_rng(5)
+    n = 12
+    sigma = 0.9 ** np.abs(np.subtract.outer(np.arange(n), np.arange(n)))
+    L, info = oracle.cholesky_lower(sigma)
+    var_w = 0.02 ** 2
+    W = rng.standard_normal((20000, n)) * np.sqrt(var_w)
+    c = 2.0 ** -5 * 0.02
+    res = oracle.sic_quantize(W, L, c)
+    R = oracle.entropy_bits_columns(res["q"])
+    D = oracle.distortion_from_residuals(res["r"], L) / W.size
+    gap = R - oracle.gaussian_rate(np.linalg.eigvalsh(sigma), var_w, D)
+    assert 4.0 < R < 8.0
+    assert gap == pytest.approx(0.5 * np.log2(2 * np.pi * np.e / 12), abs=0.03)
