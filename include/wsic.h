@@ -60,11 +60,17 @@ enum wsic_op {
   WSIC_OP_DISTORTION = 5,
   WSIC_OP_CURVATURE = 6,       /* n_out = calibration rows of one call, n_in = classes K */
   WSIC_OP_SOFTWATER = 7,       /* wsic_softwater_waterfill on an n_out x n_in layer       */
-  WSIC_OP_SOFTWATER_DIST = 8   /* wsic_softwater_distortion                               */
+  WSIC_OP_SOFTWATER_DIST = 8,  /* wsic_softwater_distortion                               */
+  WSIC_OP_ENTROPY_COLUMNS = 9, /* wsic_entropy_columns on an n_out x n_in code matrix      */
+  WSIC_OP_GAUSS_RATE = 10      /* wsic_gaussian_rate                                      */
 };
 
 enum wsic_dmode { WSIC_D_RESID = 0, WSIC_D_DIRECT = 1 };
 enum wsic_wfmode { WSIC_WF_AUTO = 0, WSIC_WF_SECANT = 1, WSIC_WF_BISECT = 2 };
+/* What the rate controller holds to the target: the entropy of all codes pooled into one table,
+ * or the mean over input columns of each column's code entropy (one entropy code per column,
+ * the setting of the rate gap in [WaterSIC §3]). */
+enum wsic_ratemode { WSIC_RATE_POOLED = 0, WSIC_RATE_COLUMNS = 1 };
 
 /* WSIC_WF_AUTO picks BISECT for layers of fewer than WSIC_WF_AUTO_PARAMS weights, SECANT
  * otherwise. */
@@ -146,6 +152,8 @@ typedef struct wsic_wf_opts {
                           where H(c) moves in visible non-monotone steps, else SECANT     */
   double c_init;       /* > 0: first grid scale tried; 0: high-rate estimate
                           sqrt(2 pi e mean_j(var(W_:,j) U_jj^2)) 2^-R                        */
+  int32_t rate_mode;   /* WSIC_RATE_POOLED (default) or WSIC_RATE_COLUMNS                    */
+  int32_t reserved;    /* 0                                                                  */
 } wsic_wf_opts;
 
 /*
@@ -173,6 +181,32 @@ int wsic_waterfill(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
 int wsic_entropy(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
                  double* bits_per_param, int64_t* n_symbols,
                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Mean per-column code entropy [WaterSIC §3, §2 item 3]:
+ *   H = (1/n_in) sum_j H(codes[:, j]) = log2(n_out) - (1/N) sum_j sum_k n_jk log2 n_jk,
+ * N = n_out * n_in, in bits per code. It never exceeds the pooled entropy (wsic_entropy).
+ * codes: n_out x n_in int32, ldq >= n_in; *bits_per_param (host). Codes beyond +-127 are counted
+ * through an overflow list of bounded size (WSIC_E_RANGE if more than 2^20 such codes).
+ * Workspace: wsic_workspace_bytes(WSIC_OP_ENTROPY_COLUMNS, n_out, n_in).
+ */
+int wsic_entropy_columns(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
+                         double* bits_per_param, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Gaussian rate-distortion limit of a layer at distortion D [WaterSIC §3 Limiti teorici: the
+ * limit is a reverse waterfilling; WaterSIC is within 1/2 log2(2 pi e / 12) = 0.2546 bit of it
+ * at high rate]. Rows of W are modelled as N(0, var I) with var = mean of W^2 (*var_out, host,
+ * nullable); the distortion per weight theta = D / (n_out n_in) is taken below every eigenvalue
+ * of var * Sigma (the high-rate regime), where the limit is
+ *   *rate_out (host) = 1/2 log2(var / theta) + (1/n_in) sum_j log2 U_jj   bits per weight
+ * (det Sigma = prod U_jj^2). When theta exceeds the smallest eigenvalue of var * Sigma this
+ * form is below the true limit (reverse waterfilling raises it); the caller owns that check.
+ * Workspace: wsic_workspace_bytes(WSIC_OP_GAUSS_RATE, n_out, n_in).
+ */
+int wsic_gaussian_rate(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                       const double* U, int64_t ldu, double D, double* rate_out, double* var_out,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Layer distortion [WaterSIC §1]: D = tr((W - W_hat) Sigma (W - W_hat)^T), W_hat_ij = Delta_j q_ij.

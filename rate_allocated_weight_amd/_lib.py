@@ -21,7 +21,9 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "wsic.h")
 OK, E_INVAL, E_NOT_PD, E_NONFINITE, E_NO_BRACKET, E_RANGE, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7
 F32, BF16 = 0, 1
 (OP_COVARIANCE, OP_CHOLESKY, OP_SIC, OP_WATERFILL, OP_ENTROPY, OP_DISTORTION, OP_CURVATURE,
- OP_SOFTWATER, OP_SOFTWATER_DIST) = range(9)
+ OP_SOFTWATER, OP_SOFTWATER_DIST, OP_ENTROPY_COLUMNS, OP_GAUSS_RATE) = range(11)
+RATE_POOLED, RATE_COLUMNS = 0, 1
+_RATE_MODES = {"pooled": RATE_POOLED, "columns": RATE_COLUMNS}
 D_RESID, D_DIRECT = 0, 1
 WF_AUTO, WF_SECANT, WF_BISECT = 0, 1, 2
 
@@ -40,7 +42,8 @@ class WsicError(RuntimeError):
 
 class WfOpts(ctypes.Structure):
     _fields_ = [("rate_tol", ctypes.c_double), ("bracket_log2", ctypes.c_double),
-                ("max_passes", ctypes.c_int32), ("mode", ctypes.c_int32), ("c_init", ctypes.c_double)]
+                ("max_passes", ctypes.c_int32), ("mode", ctypes.c_int32), ("c_init", ctypes.c_double),
+                ("rate_mode", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _SIGS = {
@@ -65,6 +68,9 @@ _SIGS = {
                                                 ctypes.POINTER(ctypes.c_int32), _p, _i64, _p, _i64, _p, _sz, _p]),
     "wsic_softwater_distortion": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i64, _d, _p, _p, _i64,
                                                  ctypes.POINTER(_d), _p, ctypes.c_int, _i64, _p, _sz, _p]),
+    "wsic_entropy_columns": (ctypes.c_int, [_p, _i64, _i64, _i64, ctypes.POINTER(_d), _p, _sz, _p]),
+    "wsic_gaussian_rate": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _d, ctypes.POINTER(_d),
+                                          ctypes.POINTER(_d), _p, _sz, _p]),
     "wsic_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "wsic_profile_reset": (ctypes.c_int, []),
     "wsic_profile_select": (ctypes.c_int, [ctypes.c_char_p]),
@@ -220,8 +226,10 @@ _MODES = {"auto": WF_AUTO, "secant": WF_SECANT, "bisect": WF_BISECT}
 def waterfill(W: torch.Tensor, U: torch.Tensor, target_bits: float, *, mode: str = "auto",
               rate_tol: float = 8e-5, bracket_log2: float = 2.0 ** -20, max_passes: int = 64,
               c_init: float = 0.0, want_resid: bool = True, codes: Optional[torch.Tensor] = None,
-              resid: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> Dict[str, object]:
-    """Grid scale c with pooled code entropy H(c) <= target_bits, and its codes."""
+              resid: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+              rate_mode: str = "pooled") -> Dict[str, object]:
+    """Grid scale c with code entropy H(c) <= target_bits (pooled, or the mean column entropy),
+    and its codes."""
     _need_cuda(W, U)
     n_out, n_in = W.shape
     if codes is None:
@@ -229,7 +237,7 @@ def waterfill(W: torch.Tensor, U: torch.Tensor, target_bits: float, *, mode: str
     if want_resid and resid is None:
         resid = torch.empty((n_out, n_in), dtype=torch.float32, device=W.device)
     ws = ws if ws is not None else workspace(OP_WATERFILL, n_out, n_in, W.device)
-    opts = WfOpts(rate_tol, bracket_log2, max_passes, _MODES[mode], c_init)
+    opts = WfOpts(rate_tol, bracket_log2, max_passes, _MODES[mode], c_init, _RATE_MODES[rate_mode], 0)
     c_out, rate_out, passes = _d(0), _d(0), ctypes.c_int32(0)
     _check(lib().wsic_waterfill(
         _p(W.data_ptr()), _dtype_code(W), n_out, n_in, _rowmajor(W), _p(U.data_ptr()), _rowmajor(U),
@@ -251,6 +259,31 @@ def entropy(codes: torch.Tensor, ws: Optional[torch.Tensor] = None) -> Tuple[flo
     _check(lib().wsic_entropy(_p(codes.data_ptr()), n_out, n_in, _rowmajor(codes), ctypes.byref(h),
                               ctypes.byref(ns), *_ws_args(ws), _stream(codes)))
     return h.value, int(ns.value)
+
+
+def entropy_columns(codes: torch.Tensor, ws: Optional[torch.Tensor] = None) -> float:
+    """Mean over columns of each column's code entropy (bits per code)."""
+    _need_cuda(codes)
+    if codes.dtype != torch.int32:
+        raise TypeError("codes must be int32")
+    n_out, n_in = codes.shape
+    ws = ws if ws is not None else workspace(OP_ENTROPY_COLUMNS, n_out, n_in, codes.device)
+    h = _d(0)
+    _check(lib().wsic_entropy_columns(_p(codes.data_ptr()), n_out, n_in, _rowmajor(codes), ctypes.byref(h),
+                                      *_ws_args(ws), _stream(codes)))
+    return h.value
+
+
+def gaussian_rate(W: torch.Tensor, U: torch.Tensor, D: float, ws: Optional[torch.Tensor] = None):
+    """High-rate Gaussian limit (bits per weight) at total distortion D, and the weight variance."""
+    _need_cuda(W, U)
+    n_out, n_in = W.shape
+    ws = ws if ws is not None else workspace(OP_GAUSS_RATE, n_out, n_in, W.device)
+    r, v = _d(0), _d(0)
+    _check(lib().wsic_gaussian_rate(_p(W.data_ptr()), _dtype_code(W), n_out, n_in, _rowmajor(W), _p(U.data_ptr()),
+                                    _rowmajor(U), float(D), ctypes.byref(r), ctypes.byref(v), *_ws_args(ws),
+                                    _stream(W)))
+    return r.value, v.value
 
 
 def distortion(W: torch.Tensor, codes: torch.Tensor, U: torch.Tensor, c: float,
@@ -325,7 +358,7 @@ def softwater_waterfill(W: torch.Tensor, U: torch.Tensor, lam: torch.Tensor, tar
     if want_resid and resid is None:
         resid = torch.empty((n_out, n_in), dtype=torch.float32, device=W.device)
     ws = ws if ws is not None else workspace(OP_SOFTWATER, n_out, n_in, W.device)
-    opts = WfOpts(rate_tol, bracket_log2, max_passes, _MODES[mode], c_init)
+    opts = WfOpts(rate_tol, bracket_log2, max_passes, _MODES[mode], c_init, RATE_POOLED, 0)
     c_out, rate_out, passes = _d(0), _d(0), ctypes.c_int32(0)
     _check(lib().wsic_softwater_waterfill(
         _p(W.data_ptr()), _dtype_code(W), n_out, n_in, _rowmajor(W), _p(U.data_ptr()), _rowmajor(U),

@@ -223,6 +223,16 @@ int launch_dequant(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ld
                    const double* invd, double c, void* W_hat, int w_hat_dtype, int64_t ldh,
                    hipStream_t st, const double* rs = nullptr);
 
+// per-column histograms: 32 columns x 512 rows per workgroup, LDS window +-127 per column
+constexpr int COL_TILE = 32, COL_ROWS = 512, COL_HALF = 127, COL_BINS = 2 * COL_HALF + 1;
+int launch_hist_cols(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
+                     unsigned* colbins, int2* ovf, unsigned* ovf_count, hipStream_t st);
+int launch_col_entropy(const unsigned* colbins, int64_t n_in, double* colS, hipStream_t st);
+// partial sums of W^2 over nblk workgroups; log2 U_jj per column (FLAG_BAD_DIAG if not positive)
+int launch_sumsq(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw, double* partial,
+                 int nblk, hipStream_t st);
+int launch_logdiag(const double* U, int64_t ldu, int64_t n, double* out, int* flags, hipStream_t st);
+
 // softmax curvature (SoftWater): logits, row normalizers, per-class sums
 struct CurvArgs {
   const void* X;

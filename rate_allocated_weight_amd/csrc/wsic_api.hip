@@ -172,6 +172,27 @@ HistWs carve_hist(Carve& cv) {
 }
 constexpr size_t HIST_CLEAR_BYTES = (HIST_BINS + 32) * sizeof(unsigned long long);
 
+// per-column histograms: bins (n_in x COL_BINS), overflow count right after them (one fill clears
+// both), overflow list of (column, code), per-column sums and their total
+struct ColHistWs {
+  unsigned* bins;
+  unsigned* ovf_count;
+  int2* ovf;
+  double* colS;
+  double* out;
+  int64_t n_in;
+};
+ColHistWs carve_colhist(Carve& cv, int64_t n_in) {
+  ColHistWs h;
+  h.bins = cv.take<unsigned>((size_t)n_in * COL_BINS + 64);
+  h.ovf_count = h.bins ? h.bins + (size_t)n_in * COL_BINS : nullptr;
+  h.ovf = cv.take<int2>(OVF_CAP);
+  h.colS = cv.take<double>((size_t)n_in);
+  h.out = cv.take<double>(1);
+  h.n_in = n_in;
+  return h;
+}
+
 struct WfWs {
   SicWs sic;
   int32_t* codes2;
@@ -179,6 +200,7 @@ struct WfWs {
   double* colvar;
   double* diag;
   HistWs hist;
+  ColHistWs col;
 };
 WfWs carve_wf(Carve& cv, int64_t n_out, int64_t n_in) {
   WfWs w;
@@ -188,6 +210,7 @@ WfWs carve_wf(Carve& cv, int64_t n_out, int64_t n_in) {
   w.colvar = cv.take<double>((size_t)colstats_doubles(n_out, n_in) + n_in);
   w.diag = cv.take<double>((size_t)n_in);
   w.hist = carve_hist(cv);
+  w.col = carve_colhist(cv, n_in);
   return w;
 }
 
@@ -249,6 +272,8 @@ CurvWs carve_curv(Carve& cv, int64_t rows, int64_t K) {
   return c;
 }
 
+constexpr int SUMSQ_BLOCKS = 1024;
+
 size_t ws_bytes_for(int op, int64_t n_out, int64_t n_in) {
   Carve cv(nullptr);
   switch (op) {
@@ -274,6 +299,15 @@ size_t ws_bytes_for(int op, int64_t n_out, int64_t n_in) {
       break;
     case WSIC_OP_CURVATURE:
       carve_curv(cv, n_out, n_in);
+      break;
+    case WSIC_OP_ENTROPY_COLUMNS:
+      cv.take<int>(FLAGS_BYTES / sizeof(int));
+      carve_colhist(cv, n_in);
+      break;
+    case WSIC_OP_GAUSS_RATE:
+      cv.take<int>(FLAGS_BYTES / sizeof(int));
+      cv.take<double>(SUMSQ_BLOCKS + 2);
+      cv.take<double>((size_t)n_in);
       break;
     case WSIC_OP_SOFTWATER:
       carve_wf(cv, n_out, n_in);
@@ -655,7 +689,11 @@ int sic_pass(const SicCtx& x, double c, int32_t* codes, int64_t ldq, float* resi
 // that mixture follows the measured H(c) of SIC codes much more closely in slope than the
 // high-rate law (slope -1), which ignores both the low-rate shape and the spread of the g_j.
 // g holds a few dozen quantiles of the g_j.
-double gauss_mix_entropy(const std::vector<double>& g, double c) {
+// With pooled == false the model is the mean of the per-column entropies instead (the rate of
+// per-column entropy coding).
+double gauss_col_entropy(const std::vector<double>& g, double c);
+double gauss_mix_entropy(const std::vector<double>& g, double c, bool pooled = true) {
+  if (!pooled) return gauss_col_entropy(g, c);
   double smax = 0.0;
   for (double v : g) smax = std::max(smax, v / c);
   const int Q = (int)std::ceil(6.0 * smax) + 1;
@@ -683,6 +721,12 @@ double gauss_mix_entropy(const std::vector<double>& g, double c) {
   return h;
 }
 
+double gauss_col_entropy(const std::vector<double>& g, double c) {
+  double hsum = 0.0;
+  for (double gv : g) hsum += gauss_mix_entropy(std::vector<double>{gv}, c, true);
+  return hsum / (double)g.size();
+}
+
 std::vector<double> scale_quantiles(const std::vector<double>& var, const std::vector<double>& diag) {
   std::vector<double> g(var.size());
   for (size_t j = 0; j < var.size(); ++j) g[j] = std::sqrt(std::max(var[j], 0.0)) * std::fabs(diag[j]);
@@ -694,12 +738,12 @@ std::vector<double> scale_quantiles(const std::vector<double>& var, const std::v
 }
 
 // log2 c with model entropy R (secant on log2 c from x0, a few steps)
-double model_solve(const std::vector<double>& g, double R, double x0) {
-  double xa = x0, ha = gauss_mix_entropy(g, std::exp2(xa));
+double model_solve(const std::vector<double>& g, double R, double x0, bool pooled = true) {
+  double xa = x0, ha = gauss_mix_entropy(g, std::exp2(xa), pooled);
   double slope = -1.0;
   for (int it = 0; it < 8 && std::fabs(ha - R) > 1e-4; ++it) {
     const double xb = xa + std::min(2.0, std::max(-2.0, (R - ha) / slope));
-    const double hb = gauss_mix_entropy(g, std::exp2(xb));
+    const double hb = gauss_mix_entropy(g, std::exp2(xb), pooled);
     if (xb != xa) {
       const double sl = (hb - ha) / (xb - xa);
       if (sl < -0.25 && sl > -4.0) slope = sl;
@@ -747,6 +791,47 @@ int entropy_of(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq, c
   const double N = (double)n_out * (double)n_in;
   *H = std::log2(N) - s / N;
   if (nsym) *nsym = ns;
+  return WSIC_OK;
+}
+
+// Mean over columns of the column entropies: log2(n_out) - (sum_j S_j + overflow terms) / N.
+// dflags (nullable): the SIC pass's three flag words, read back with the result.
+int entropy_cols_of(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
+                    const ColHistWs& h, const int* dflags, hipStream_t st, double* H,
+                    int* flags_out = nullptr, int* aux_out = nullptr, int* aux2_out = nullptr) {
+  WSIC_TRY(launch_fill_zero(h.bins, ((size_t)n_in * COL_BINS + 64) * sizeof(unsigned), st));
+  WSIC_TRY(launch_hist_cols(codes, n_out, n_in, ldq, h.bins, h.ovf, h.ovf_count, st));
+  WSIC_TRY(launch_col_entropy(h.bins, n_in, h.colS, st));
+  WSIC_TRY(launch_sum_partials(h.colS, n_in, h.out, st));
+  double S = 0.0;
+  unsigned novf = 0;
+  int f[3] = {0, 0, 0};
+  ReadPiece pr[3] = {{&S, h.out, sizeof(double)}, {&novf, h.ovf_count, sizeof(unsigned)},
+                     {f, dflags, sizeof f}};
+  WSIC_TRY(read_back(pr, dflags ? 3 : 2, st));
+  if (flags_out) *flags_out = f[0];
+  if (aux_out) *aux_out = f[1];
+  if (aux2_out) *aux2_out = f[2];
+  if (novf > 0) {
+    if (novf > OVF_CAP) {
+      set_error("entropy_columns: %u codes beyond +-%d exceed the overflow list (%u)", novf, COL_HALF,
+                OVF_CAP);
+      return WSIC_E_RANGE;
+    }
+    std::vector<int2> v(novf);
+    const ReadPiece po{v.data(), h.ovf, v.size() * sizeof(int2)};
+    WSIC_TRY(read_back(&po, 1, st));
+    std::sort(v.begin(), v.end(), [](int2 a, int2 b) { return a.x != b.x ? a.x < b.x : a.y < b.y; });
+    size_t i = 0;
+    while (i < v.size()) {
+      size_t k = i;
+      while (k < v.size() && v[k].x == v[i].x && v[k].y == v[i].y) ++k;
+      const double cnt = (double)(k - i);
+      S += cnt * std::log2(cnt);
+      i = k;
+    }
+  }
+  *H = std::log2((double)n_out) - S / ((double)n_out * (double)n_in);
   return WSIC_OK;
 }
 
@@ -916,7 +1001,7 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
       set_error("waterfill: bad argument");
       return WSIC_E_INVAL;
     }
-    wsic_wf_opts o{WSIC_WF_RATE_TOL, std::ldexp(1.0, -20), 64, WSIC_WF_AUTO, 0.0};
+    wsic_wf_opts o{WSIC_WF_RATE_TOL, std::ldexp(1.0, -20), 64, WSIC_WF_AUTO, 0.0, WSIC_RATE_POOLED, 0};
     if (opts) {
       o = *opts;
       if (!(o.rate_tol >= 0.0)) o.rate_tol = WSIC_WF_RATE_TOL;
@@ -926,9 +1011,14 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
         set_error("waterfill: unknown mode %d", o.mode);
         return WSIC_E_INVAL;
       }
+      if (o.rate_mode != WSIC_RATE_POOLED && o.rate_mode != WSIC_RATE_COLUMNS) {
+        set_error("waterfill: unknown rate mode %d", o.rate_mode);
+        return WSIC_E_INVAL;
+      }
     }
     if (o.mode == WSIC_WF_AUTO)
       o.mode = (n_out * n_in < WSIC_WF_AUTO_PARAMS) ? WSIC_WF_BISECT : WSIC_WF_SECANT;
+    const bool cols = o.rate_mode == WSIC_RATE_COLUMNS;
     const bool trace = std::getenv("WSIC_TRACE") != nullptr;
     WSIC_TRY(check_ws(lam ? WSIC_OP_SOFTWATER : WSIC_OP_WATERFILL, n_out, n_in, ws, ws_bytes));
     hipStream_t st = (hipStream_t)stream;
@@ -968,7 +1058,7 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
       c0 = std::sqrt(2.0 * M_PI * M_E * m) * std::pow(2.0, -R);
       if (o.mode == WSIC_WF_SECANT && std::isfinite(c0)) {
         gq = scale_quantiles(var, diag);
-        const double xm = model_solve(gq, R - 0.5 * o.rate_tol, std::log2(c0));
+        const double xm = model_solve(gq, R - 0.5 * o.rate_tol, std::log2(c0), !cols);
         if (std::isfinite(xm)) c0 = std::exp2(xm);
       }
     } else {
@@ -994,13 +1084,17 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
       ++passes;
       WSIC_TRY(sic_pass_once(x, c, cbuf[buf], ldq, rbuf[buf], ldr));
       int f = 0, nfix = 0, nchk = 0;
-      WSIC_TRY(entropy_of(cbuf[buf], n_out, n_in, ldq, wf.hist, x.ws.pflags, st, H, nullptr, &f,
-                          &nfix, &nchk));
+      auto rate_of = [&](int* fl, int* a1, int* a2) -> int {
+        if (cols)
+          return entropy_cols_of(cbuf[buf], n_out, n_in, ldq, wf.col, x.ws.pflags, st, H, fl, a1, a2);
+        return entropy_of(cbuf[buf], n_out, n_in, ldq, wf.hist, x.ws.pflags, st, H, nullptr, fl, a1, a2);
+      };
+      WSIC_TRY(rate_of(&f, &nfix, &nchk));
       if (x.i8 && (f & FLAG_OVERFLOW_LIST)) {  // a row listed too many large codes: fp64 pass
         SicCtx y = x;
         y.i8 = false;
         WSIC_TRY(sic_pass_once(y, c, cbuf[buf], ldq, rbuf[buf], ldr));
-        WSIC_TRY(entropy_of(cbuf[buf], n_out, n_in, ldq, wf.hist, x.ws.pflags, st, H, nullptr, &f));
+        WSIC_TRY(rate_of(&f, nullptr, nullptr));
       }
       if (trace)
         std::fprintf(stderr,
@@ -1100,8 +1194,8 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
         if (xs.size() == 1 && !gq.empty()) {  // one evaluation: the rate model's local slope
           const double dx = std::min(2.0, std::max(-2.0, hb - Rt));  // the step at slope -1
           if (std::fabs(dx) > 1e-9) {
-            const double sl = (gauss_mix_entropy(gq, std::exp2(xb + dx)) -
-                               gauss_mix_entropy(gq, std::exp2(xb))) / dx;
+            const double sl = (gauss_mix_entropy(gq, std::exp2(xb + dx), !cols) -
+                               gauss_mix_entropy(gq, std::exp2(xb), !cols)) / dx;
             if (sl < -0.25 && sl > -4.0) slope = sl;
           }
         }
@@ -1277,6 +1371,65 @@ int wsic_softwater_distortion(const int32_t* codes, int64_t n_out, int64_t n_in,
     return flags_status(f, "softwater_distortion");
   } catch (...) {
     set_error("softwater_distortion: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_entropy_columns(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
+                         double* bits_per_param, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    if (!codes || !bits_per_param || n_out <= 0 || n_in <= 0 || ldq < n_in) {
+      set_error("entropy_columns: bad argument");
+      return WSIC_E_INVAL;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_ENTROPY_COLUMNS, n_out, n_in, ws, ws_bytes));
+    Carve cv(ws);
+    cv.take<int>(FLAGS_BYTES / sizeof(int));
+    const ColHistWs h = carve_colhist(cv, n_in);
+    return entropy_cols_of(codes, n_out, n_in, ldq, h, nullptr, (hipStream_t)stream, bits_per_param);
+  } catch (...) {
+    set_error("entropy_columns: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_gaussian_rate(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                       const double* U, int64_t ldu, double D, double* rate_out, double* var_out,
+                       void* ws, size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    WSIC_TRY(check_layer(W, dtype, n_out, n_in, ldw));
+    if (!U || ldu < n_in || !(D > 0.0) || !std::isfinite(D) || !rate_out) {
+      set_error("gaussian_rate: bad argument");
+      return WSIC_E_INVAL;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_GAUSS_RATE, n_out, n_in, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    Carve cv(ws);
+    int* flags = cv.take<int>(FLAGS_BYTES / sizeof(int));
+    double* part = cv.take<double>(SUMSQ_BLOCKS + 2);
+    double* logd = cv.take<double>((size_t)n_in);
+    double* sums = part + SUMSQ_BLOCKS;  // [0] sum w^2, [1] sum log2 U_jj
+    const int64_t total = n_out * n_in;
+    const int nblk = (int)std::min<int64_t>(SUMSQ_BLOCKS, (total + 255) / 256);
+    WSIC_TRY(launch_fill_zero(flags, FLAGS_BYTES, st));
+    WSIC_TRY(launch_sumsq(W, dtype, n_out, n_in, ldw, part, nblk, st));
+    WSIC_TRY(launch_sum_partials(part, nblk, sums, st));
+    WSIC_TRY(launch_logdiag(U, ldu, n_in, logd, flags, st));
+    WSIC_TRY(launch_sum_partials(logd, n_in, sums + 1, st));
+    double r[2] = {0.0, 0.0};
+    int f = 0;
+    const ReadPiece pr[2] = {{r, sums, sizeof r}, {&f, flags, sizeof(int)}};
+    WSIC_TRY(read_back(pr, 2, st));
+    WSIC_TRY(flags_status(f, "gaussian_rate"));
+    const double var = r[0] / (double)total;
+    const double theta = D / (double)total;
+    *rate_out = 0.5 * std::log2(var / theta) + r[1] / (double)n_in;
+    if (var_out) *var_out = var;
+    return WSIC_OK;
+  } catch (...) {
+    set_error("gaussian_rate: internal exception");
     return WSIC_E_INVAL;
   }
 }
