@@ -86,6 +86,9 @@ def parse():
     ap.add_argument("--softwater", action="store_true",
                     help="class-aware grids of a softmax head: class curvatures from the calibration "
                          "inputs, then waterfilling on c / (sqrt(lambda_k) U_jj) and the KL estimate")
+    ap.add_argument("--rate-mode", default="pooled", choices=["pooled", "columns"],
+                    help="rate held to the target: pooled code entropy, or the mean per-column entropy "
+                         "(then the gap to the Gaussian limit is reported)")
     ap.add_argument("--smoothing", type=float, default=0.05,
                     help="weight of the uniform distribution mixed into the calibration softmax")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -228,7 +231,7 @@ def main():
     ws_cov = L.workspace(L.OP_COVARIANCE, 1, n_in, dev)
     ws_chol = L.workspace(L.OP_CHOLESKY, 1, n_in, dev)
     ws_wf = L.workspace(L.OP_WATERFILL, n_out, n_in, dev)
-    ws_ent = L.workspace(L.OP_ENTROPY, n_out, n_in, dev)
+    ws_ent = L.workspace(L.OP_ENTROPY_COLUMNS if args.rate_mode == "columns" else L.OP_ENTROPY, n_out, n_in, dev)
     ws_dist = L.workspace(L.OP_DISTORTION, n_out, n_in, dev)
     sw = args.softwater
     if sw:
@@ -263,12 +266,16 @@ def main():
             wf = L.softwater_waterfill(W, U, lam, args.target, mode=args.mode, codes=codes, resid=resid,
                                        ws=ws_wf)
         else:
-            wf = L.waterfill(W, U, args.target, mode=args.mode, codes=codes, resid=resid, ws=ws_wf)
+            wf = L.waterfill(W, U, args.target, mode=args.mode, codes=codes, resid=resid, ws=ws_wf,
+                             rate_mode=args.rate_mode)
         if record:
             ev[4].record()
         if sw:
             h, _ = L.entropy(wf["codes"], ws=ws_ent)
             D, _ = L.softwater_distortion(wf["codes"], U, wf["c"], lam, wf["resid"], ws=ws_dist)
+        elif args.rate_mode == "columns":
+            h = L.entropy_columns(codes, ws=ws_ent)
+            D, _ = L.distortion(W, codes, U, wf["c"], resid=resid, ws=ws_dist)
         else:
             h, _ = L.entropy(codes, ws=ws_ent)
             D, _ = L.distortion(W, codes, U, wf["c"], resid=resid, ws=ws_dist)
@@ -335,6 +342,16 @@ def main():
     elapsed = t1 - t0
     ms_per_step = 1e3 * elapsed / args.steps
     wf, h, D = results[-1]
+    it_gap = None
+    if args.rate_mode == "columns" and not sw:
+        # after the timed region: the high-rate Gaussian limit at this distortion (the factor U of
+        # the last step is still in sigma)
+        rg, var = L.gaussian_rate(W, sigma, D)
+        it_gap = {"rate_columns": wf["rate"], "gaussian_rate": rg, "gap_bits": wf["rate"] - rg,
+                  "uniform_scalar_gap_bits": 0.5 * math.log2(2 * math.pi * math.e / 12),
+                  "var_w": var, "theta": D / (n_out * n_in),
+                  "note": "Gaussian model of the rows with the weights' variance, high-rate form of "
+                          "reverse waterfilling (exact while theta is below var * min eig Sigma)"}
     for ev in phase_events:
         for k, name in enumerate(phase_names):
             phase_ms[name] += ev[k].elapsed_time(ev[k + 1]) / args.steps
@@ -396,6 +413,9 @@ def main():
         "families_warmup": families,
         "trailing_update": trailing,
     }
+    if it_gap is not None:
+        out["it_gap"] = it_gap
+        out["config"]["rate_mode"] = "columns"
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = (cpu_baseline_softwater(layer, args.target, args.cpu_sample_rows, args.smoothing)
