@@ -62,7 +62,9 @@ enum wsic_op {
   WSIC_OP_SOFTWATER = 7,       /* wsic_softwater_waterfill on an n_out x n_in layer       */
   WSIC_OP_SOFTWATER_DIST = 8,  /* wsic_softwater_distortion                               */
   WSIC_OP_ENTROPY_COLUMNS = 9, /* wsic_entropy_columns on an n_out x n_in code matrix      */
-  WSIC_OP_GAUSS_RATE = 10      /* wsic_gaussian_rate                                      */
+  WSIC_OP_GAUSS_RATE = 10,     /* wsic_gaussian_rate                                      */
+  WSIC_OP_LMMSE = 11,          /* wsic_lmmse_scale                                        */
+  WSIC_OP_LIVE = 12            /* wsic_live_features (n_in = size of Sigma)               */
 };
 
 enum wsic_dmode { WSIC_D_RESID = 0, WSIC_D_DIRECT = 1 };
@@ -86,7 +88,8 @@ const char* wsic_last_error(void);
 const char* wsic_status_str(int status);
 
 /* Bytes of device workspace that call `op` needs for an n_out x n_in layer (n_out is ignored
- * by WSIC_OP_COVARIANCE / WSIC_OP_CHOLESKY; for WSIC_OP_ENTROPY pass the code matrix shape).
+ * by WSIC_OP_COVARIANCE / WSIC_OP_CHOLESKY / WSIC_OP_LIVE; for WSIC_OP_ENTROPY pass the code
+ * matrix shape).
  * Returns 0 for an unknown op. */
 size_t wsic_workspace_bytes(int op, int64_t n_out, int64_t n_in);
 
@@ -207,6 +210,43 @@ int wsic_entropy_columns(const int32_t* codes, int64_t n_out, int64_t n_in, int6
 int wsic_gaussian_rate(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
                        const double* U, int64_t ldu, double D, double* rate_out, double* var_out,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * LMMSE rescale [WaterSIC §2 item 4, "Correzione LMMSE": a linear factor that corrects the
+ * bias of rounding], one factor per output row:
+ *   gamma_k = (w_k Sigma w_hat_k^T) / (w_hat_k Sigma w_hat_k^T)
+ * minimizes the row's output error (w_k - gamma w_hat_k) Sigma (w_k - gamma w_hat_k)^T; the
+ * rescaled row is gamma_k w_hat_k. Computed from Y = W U^T and the SIC residuals (resid from
+ * wsic_sic_quantize / wsic_waterfill, required): U w_hat_k^T = U w_k^T - diag(U) r_k.
+ * gamma (out): n_out fp64 (device); a row quantized to zero keeps gamma = 1.
+ * *D_before, *D_after (host, nullable): tr(E Sigma E^T) without and with the factors.
+ * Workspace: wsic_workspace_bytes(WSIC_OP_LMMSE, n_out, n_in).
+ */
+int wsic_lmmse_scale(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                     const double* U, int64_t ldu, const float* resid, int64_t ldr, double* gamma,
+                     double* D_before, double* D_after, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dead-feature removal [WaterSIC §2 item 4, "Cancellazione delle Feature Morte": input
+ * dimensions of near-zero variance are removed so that the Cholesky factorization stays stable].
+ * A column i is live when Sigma_ii > tau * max_j Sigma_jj (0 <= tau < 1).
+ * wsic_live_features: idx (out, device, n): the live columns in ascending order, idx[0, *n_live);
+ *   pos (out, device, n): each column's position in idx, -1 for a dead one; *n_live (host).
+ *   WSIC_E_INVAL when no column is live. Workspace: wsic_workspace_bytes(WSIC_OP_LIVE, 0, n).
+ * wsic_gather_features: W_live = W[:, idx] (n_out x n_live, same dtype, ldwl >= n_live) and, if
+ *   Sigma is given, Sigma_live = Sigma[idx][:, idx] (n_live x n_live, ldsl >= n_live). The
+ *   quantization then runs on the live layer (wsic_cholesky, wsic_waterfill, ...).
+ * wsic_scatter_codes: codes[:, j] = codes_live[:, pos[j]] for live j, 0 for dead j (a dead
+ *   column's weights multiply inputs of no variance: they are dropped).
+ */
+int wsic_live_features(const double* Sigma, int64_t n, int64_t lds, double tau, int32_t* idx,
+                       int32_t* pos, int64_t* n_live, void* ws, size_t ws_bytes, void* stream);
+int wsic_gather_features(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                         const double* Sigma, int64_t lds, const int32_t* idx, int64_t n_live,
+                         void* W_live, int64_t ldwl, double* Sigma_live, int64_t ldsl,
+                         void* stream);
+int wsic_scatter_codes(const int32_t* codes_live, int64_t n_out, int64_t ldql, const int32_t* pos,
+                       int64_t n_in, int32_t* codes, int64_t ldq, void* stream);
 
 /*
  * Layer distortion [WaterSIC §1]: D = tr((W - W_hat) Sigma (W - W_hat)^T), W_hat_ij = Delta_j q_ij.

@@ -21,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "wsic.h")
 OK, E_INVAL, E_NOT_PD, E_NONFINITE, E_NO_BRACKET, E_RANGE, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7
 F32, BF16 = 0, 1
 (OP_COVARIANCE, OP_CHOLESKY, OP_SIC, OP_WATERFILL, OP_ENTROPY, OP_DISTORTION, OP_CURVATURE,
- OP_SOFTWATER, OP_SOFTWATER_DIST, OP_ENTROPY_COLUMNS, OP_GAUSS_RATE) = range(11)
+ OP_SOFTWATER, OP_SOFTWATER_DIST, OP_ENTROPY_COLUMNS, OP_GAUSS_RATE, OP_LMMSE, OP_LIVE) = range(13)
 RATE_POOLED, RATE_COLUMNS = 0, 1
 _RATE_MODES = {"pooled": RATE_POOLED, "columns": RATE_COLUMNS}
 D_RESID, D_DIRECT = 0, 1
@@ -71,6 +71,12 @@ _SIGS = {
     "wsic_entropy_columns": (ctypes.c_int, [_p, _i64, _i64, _i64, ctypes.POINTER(_d), _p, _sz, _p]),
     "wsic_gaussian_rate": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _d, ctypes.POINTER(_d),
                                           ctypes.POINTER(_d), _p, _sz, _p]),
+    "wsic_lmmse_scale": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, _i64, _p,
+                                        ctypes.POINTER(_d), ctypes.POINTER(_d), _p, _sz, _p]),
+    "wsic_live_features": (ctypes.c_int, [_p, _i64, _i64, _d, _p, _p, ctypes.POINTER(_i64), _p, _sz, _p]),
+    "wsic_gather_features": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
+                                            _p, _i64, _p]),
+    "wsic_scatter_codes": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _p, _i64, _p]),
     "wsic_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "wsic_profile_reset": (ctypes.c_int, []),
     "wsic_profile_select": (ctypes.c_int, [ctypes.c_char_p]),
@@ -284,6 +290,55 @@ def gaussian_rate(W: torch.Tensor, U: torch.Tensor, D: float, ws: Optional[torch
                                     _rowmajor(U), float(D), ctypes.byref(r), ctypes.byref(v), *_ws_args(ws),
                                     _stream(W)))
     return r.value, v.value
+
+
+def lmmse_scale(W: torch.Tensor, U: torch.Tensor, resid: torch.Tensor, ws: Optional[torch.Tensor] = None):
+    """Per-row LMMSE factors gamma (device, float64) and the distortion before and after."""
+    _need_cuda(W, U, resid)
+    n_out, n_in = W.shape
+    gamma = torch.empty(n_out, dtype=torch.float64, device=W.device)
+    ws = ws if ws is not None else workspace(OP_LMMSE, n_out, n_in, W.device)
+    db, da = _d(0), _d(0)
+    _check(lib().wsic_lmmse_scale(_p(W.data_ptr()), _dtype_code(W), n_out, n_in, _rowmajor(W), _p(U.data_ptr()),
+                                  _rowmajor(U), _p(resid.data_ptr()), _rowmajor(resid), _p(gamma.data_ptr()),
+                                  ctypes.byref(db), ctypes.byref(da), *_ws_args(ws), _stream(W)))
+    return gamma, db.value, da.value
+
+
+def live_features(sigma: torch.Tensor, tau: float):
+    """(idx, pos, n_live): live input columns (Sigma_ii > tau max Sigma_jj) and the inverse map."""
+    _need_cuda(sigma)
+    n = sigma.shape[0]
+    idx = torch.empty(n, dtype=torch.int32, device=sigma.device)
+    pos = torch.empty(n, dtype=torch.int32, device=sigma.device)
+    ws = workspace(OP_LIVE, 0, n, sigma.device)
+    nl = _i64(0)
+    _check(lib().wsic_live_features(_p(sigma.data_ptr()), n, _rowmajor(sigma), float(tau), _p(idx.data_ptr()),
+                                    _p(pos.data_ptr()), ctypes.byref(nl), *_ws_args(ws), _stream(sigma)))
+    return idx, pos, int(nl.value)
+
+
+def gather_features(W: torch.Tensor, idx: torch.Tensor, n_live: int, sigma: Optional[torch.Tensor] = None):
+    """W[:, idx[:n_live]] and, if given, sigma[idx][:, idx]."""
+    _need_cuda(W, idx)
+    n_out, n_in = W.shape
+    Wl = torch.empty((n_out, n_live), dtype=W.dtype, device=W.device)
+    Sl = torch.empty((n_live, n_live), dtype=torch.float64, device=W.device) if sigma is not None else None
+    _check(lib().wsic_gather_features(
+        _p(W.data_ptr()), _dtype_code(W), n_out, n_in, _rowmajor(W), _p(sigma.data_ptr() if sigma is not None else 0),
+        _rowmajor(sigma) if sigma is not None else n_in, _p(idx.data_ptr()), n_live, _p(Wl.data_ptr()), n_live,
+        _p(Sl.data_ptr() if Sl is not None else 0), n_live, _stream(W)))
+    return Wl, Sl
+
+
+def scatter_codes(codes_live: torch.Tensor, pos: torch.Tensor, n_in: int) -> torch.Tensor:
+    """Full code matrix: live columns from codes_live, dead columns 0."""
+    _need_cuda(codes_live, pos)
+    n_out = codes_live.shape[0]
+    q = torch.empty((n_out, n_in), dtype=torch.int32, device=codes_live.device)
+    _check(lib().wsic_scatter_codes(_p(codes_live.data_ptr()), n_out, _rowmajor(codes_live), _p(pos.data_ptr()),
+                                    n_in, _p(q.data_ptr()), n_in, _stream(codes_live)))
+    return q
 
 
 def distortion(W: torch.Tensor, codes: torch.Tensor, U: torch.Tensor, c: float,

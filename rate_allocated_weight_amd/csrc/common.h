@@ -233,6 +233,18 @@ int launch_sumsq(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t 
                  int nblk, hipStream_t st);
 int launch_logdiag(const double* U, int64_t ldu, int64_t n, double* out, int* flags, hipStream_t st);
 
+// LMMSE row factors from Y = W U^T and the SIC residuals; dead-feature removal
+int launch_lmmse_rows(const double* Y, int64_t ldy, const float* R, int64_t ldr, const double* U,
+                      int64_t ldu, int64_t n_out, int64_t n_in, double* gamma, double* dbefore,
+                      double* dafter, hipStream_t st);
+int launch_live_scan(const double* S, int64_t n, int64_t lds, double tau, int32_t* idx,
+                     int32_t* pos, long long* live_count, int* flags, hipStream_t st);
+int launch_gather_features(const void* W, int dtype, int64_t n_out, int64_t ldw, const double* S,
+                           int64_t lds, const int32_t* idx, int64_t n_live, void* Wl, int64_t ldwl,
+                           double* Sl, int64_t ldsl, hipStream_t st);
+int launch_scatter_codes(const int32_t* ql, int64_t ldql, const int32_t* pos, int64_t n_in,
+                         int64_t n_out, int32_t* q, int64_t ldq, hipStream_t st);
+
 // softmax curvature (SoftWater): logits, row normalizers, per-class sums
 struct CurvArgs {
   const void* X;

@@ -304,6 +304,15 @@ size_t ws_bytes_for(int op, int64_t n_out, int64_t n_in) {
       cv.take<int>(FLAGS_BYTES / sizeof(int));
       carve_colhist(cv, n_in);
       break;
+    case WSIC_OP_LMMSE:
+      cv.take<int>(FLAGS_BYTES / sizeof(int));
+      cv.take<double>((size_t)n_out * n_in);
+      cv.take<double>(3 * (size_t)n_out + 2);
+      break;
+    case WSIC_OP_LIVE:
+      cv.take<int>(FLAGS_BYTES / sizeof(int));
+      cv.take<long long>(1);
+      break;
     case WSIC_OP_GAUSS_RATE:
       cv.take<int>(FLAGS_BYTES / sizeof(int));
       cv.take<double>(SUMSQ_BLOCKS + 2);
@@ -862,7 +871,9 @@ const char* wsic_status_str(int s) {
 }
 
 size_t wsic_workspace_bytes(int op, int64_t n_out, int64_t n_in) {
-  if (n_in <= 0 || (op != WSIC_OP_COVARIANCE && op != WSIC_OP_CHOLESKY && n_out <= 0)) return 0;
+  if (n_in <= 0 ||
+      (op != WSIC_OP_COVARIANCE && op != WSIC_OP_CHOLESKY && op != WSIC_OP_LIVE && n_out <= 0))
+    return 0;
   return ws_bytes_for(op, n_out, n_in);
 }
 
@@ -1430,6 +1441,112 @@ int wsic_gaussian_rate(const void* W, int dtype, int64_t n_out, int64_t n_in, in
     return WSIC_OK;
   } catch (...) {
     set_error("gaussian_rate: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_lmmse_scale(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                     const double* U, int64_t ldu, const float* resid, int64_t ldr, double* gamma,
+                     double* D_before, double* D_after, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    WSIC_TRY(check_layer(W, dtype, n_out, n_in, ldw));
+    if (!U || ldu < n_in || !resid || ldr < n_in || !gamma) {
+      set_error("lmmse_scale: bad argument");
+      return WSIC_E_INVAL;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_LMMSE, n_out, n_in, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    Carve cv(ws);
+    int* flags = cv.take<int>(FLAGS_BYTES / sizeof(int));
+    double* Y = cv.take<double>((size_t)n_out * n_in);
+    double* rows = cv.take<double>(3 * (size_t)n_out + 2);
+    double* dbefore = rows;
+    double* dafter = rows + n_out;
+    double* sums = rows + 3 * n_out;
+    WSIC_TRY(launch_fill_zero(flags, FLAGS_BYTES, st));
+    WSIC_TRY(launch_prep(U, ldu, n_in, rows + 2 * n_out, flags, st));  // U diagonal checks
+    const double work = (double)n_out * (double)n_in * (double)(n_in + 1);
+    WSIC_TRY(launch_gemm_y(dtype, n_out, n_in, n_in, W, ldw, U, ldu, Y, n_in, work, st));
+    WSIC_TRY(launch_lmmse_rows(Y, n_in, resid, ldr, U, ldu, n_out, n_in, gamma, dbefore, dafter, st));
+    WSIC_TRY(launch_sum_partials(dbefore, n_out, sums, st));
+    WSIC_TRY(launch_sum_partials(dafter, n_out, sums + 1, st));
+    double r[2] = {0.0, 0.0};
+    int f = 0;
+    const ReadPiece pr[2] = {{r, sums, sizeof r}, {&f, flags, sizeof(int)}};
+    WSIC_TRY(read_back(pr, 2, st));
+    if (D_before) *D_before = r[0];
+    if (D_after) *D_after = r[1];
+    return flags_status(f, "lmmse_scale");
+  } catch (...) {
+    set_error("lmmse_scale: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_live_features(const double* Sigma, int64_t n, int64_t lds, double tau, int32_t* idx,
+                       int32_t* pos, int64_t* n_live, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    if (!Sigma || n <= 0 || lds < n || !idx || !pos || !n_live || !(tau >= 0.0) || !(tau < 1.0)) {
+      set_error("live_features: bad argument");
+      return WSIC_E_INVAL;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_LIVE, 0, n, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    Carve cv(ws);
+    int* flags = cv.take<int>(FLAGS_BYTES / sizeof(int));
+    long long* cnt = cv.take<long long>(1);
+    WSIC_TRY(launch_fill_zero(flags, FLAGS_BYTES, st));
+    WSIC_TRY(launch_live_scan(Sigma, n, lds, tau, idx, pos, cnt, flags, st));
+    long long c = 0;
+    int f = 0;
+    const ReadPiece pr[2] = {{&c, cnt, sizeof c}, {&f, flags, sizeof(int)}};
+    WSIC_TRY(read_back(pr, 2, st));
+    *n_live = c;
+    WSIC_TRY(flags_status(f, "live_features"));
+    if (c == 0) {
+      set_error("live_features: every input column is dead");
+      return WSIC_E_INVAL;
+    }
+    return WSIC_OK;
+  } catch (...) {
+    set_error("live_features: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_gather_features(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                         const double* Sigma, int64_t lds, const int32_t* idx, int64_t n_live,
+                         void* W_live, int64_t ldwl, double* Sigma_live, int64_t ldsl,
+                         void* stream) {
+  try {
+    clear_error();
+    WSIC_TRY(check_layer(W, dtype, n_out, n_in, ldw));
+    if (!idx || n_live <= 0 || n_live > n_in || !W_live || ldwl < n_live ||
+        (Sigma && (lds < n_in || !Sigma_live || ldsl < n_live))) {
+      set_error("gather_features: bad argument");
+      return WSIC_E_INVAL;
+    }
+    return launch_gather_features(W, dtype, n_out, ldw, Sigma, lds, idx, n_live, W_live, ldwl,
+                                  Sigma_live, ldsl, (hipStream_t)stream);
+  } catch (...) {
+    set_error("gather_features: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_scatter_codes(const int32_t* codes_live, int64_t n_out, int64_t ldql, const int32_t* pos,
+                       int64_t n_in, int32_t* codes, int64_t ldq, void* stream) {
+  try {
+    clear_error();
+    if (!codes_live || n_out <= 0 || ldql <= 0 || !pos || n_in <= 0 || !codes || ldq < n_in) {
+      set_error("scatter_codes: bad argument");
+      return WSIC_E_INVAL;
+    }
+    return launch_scatter_codes(codes_live, ldql, pos, n_in, n_out, codes, ldq, (hipStream_t)stream);
+  } catch (...) {
+    set_error("scatter_codes: internal exception");
     return WSIC_E_INVAL;
   }
 }

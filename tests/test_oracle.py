@@ -394,3 +394,68 @@ def test_watersic_gap_at_high_rate():
     gap = R - oracle.gaussian_rate(np.linalg.eigvalsh(sigma), var_w, D)
     assert 4.0 < R < 8.0
     assert gap == pytest.approx(0.5 * np.log2(2 * np.pi * np.e / 12), abs=0.03)
+
+
+# ------------------------------------------------------------------ LMMSE rescale
+def _spd(n, seed):
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((n, n))
+    return A @ A.T / n + 0.1 * np.eye(n)
+
+
+def test_lmmse_scale_closed_forms():
+    """gamma = 1 and no distortion when W_hat = W; W_hat = 2 W gives gamma = 1/2 and zero
+    distortion after rescaling; a zero row keeps gamma = 1 and its distortion."""
+    rng = np.random.default_rng(0)
+    S = _spd(6, 1)
+    W = rng.standard_normal((4, 6))
+    r = oracle.lmmse_scale(W, W, S)
+    np.testing.assert_allclose(r["gamma"], 1.0, rtol=1e-12)
+    assert abs(r["D_after"]) < 1e-12
+    r = oracle.lmmse_scale(W, 2 * W, S)
+    np.testing.assert_allclose(r["gamma"], 0.5, rtol=1e-12)
+    np.testing.assert_allclose(r["d_after"], 0.0, atol=1e-12)
+    Wh = W.copy()
+    Wh[2] = 0.0
+    r = oracle.lmmse_scale(W, Wh, S)
+    assert r["gamma"][2] == 1.0 and r["d_after"][2] == pytest.approx(W[2] @ S @ W[2])
+
+
+def test_lmmse_scale_is_the_minimizer():
+    """gamma_k minimizes the row's distortion over a scalar grid (brute force); never worse
+    than gamma = 1; the before-distortion equals tr(E Sigma E^T) of the rows."""
+    rng = np.random.default_rng(3)
+    S = _spd(5, 2)
+    W = rng.standard_normal((3, 5))
+    Wh = np.rint(W * 2) / 2
+    r = oracle.lmmse_scale(W, Wh, S)
+    for k in range(3):
+        g = np.linspace(r["gamma"][k] - 0.1, r["gamma"][k] + 0.1, 2001)
+        d = [(W[k] - x * Wh[k]) @ S @ (W[k] - x * Wh[k]) for x in g]
+        assert min(d) >= r["d_after"][k] - 1e-12
+        assert r["d_after"][k] <= r["d_before"][k] + 1e-15
+    assert r["D_before"] == pytest.approx(oracle.distortion_direct(W, Wh, np.ones(5), S), rel=1e-12)
+
+
+def test_dead_features_removed_without_changing_the_distortion():
+    """Columns of exactly zero variance make Sigma singular (the factorization fails); removing
+    them leaves a factorable Sigma, and a dead column contributes nothing to tr(E Sigma E^T)
+    whatever its weights, so the layer's distortion is that of the live problem."""
+    rng = np.random.default_rng(2)
+    X = rng.standard_normal((300, 9))
+    X[:, [2, 6]] = 0.0
+    sigma = oracle.covariance([X])
+    L, info = oracle.cholesky_lower(sigma)
+    assert info != 0
+    live = oracle.live_features(sigma, 1e-12)
+    np.testing.assert_array_equal(live, [0, 1, 3, 4, 5, 7, 8])
+    S_l = sigma[np.ix_(live, live)]
+    L_l, info = oracle.cholesky_lower(S_l)
+    assert info == 0
+    W = rng.standard_normal((5, 9))
+    res = oracle.sic_quantize(W[:, live], L_l, 0.1)
+    W_hat = np.zeros_like(W)
+    W_hat[:, live] = res["q"] * res["alpha"][None, :]
+    d_full = oracle.distortion_direct(W, W_hat, np.ones(9), sigma)
+    d_live = oracle.distortion_from_residuals(res["r"], L_l)
+    assert d_full == pytest.approx(d_live, rel=1e-10)
