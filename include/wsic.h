@@ -64,7 +64,9 @@ enum wsic_op {
   WSIC_OP_ENTROPY_COLUMNS = 9, /* wsic_entropy_columns on an n_out x n_in code matrix      */
   WSIC_OP_GAUSS_RATE = 10,     /* wsic_gaussian_rate                                      */
   WSIC_OP_LMMSE = 11,          /* wsic_lmmse_scale                                        */
-  WSIC_OP_LIVE = 12            /* wsic_live_features (n_in = size of Sigma)               */
+  WSIC_OP_LIVE = 12,           /* wsic_live_features (n_in = size of Sigma)               */
+  WSIC_OP_RANS_ENC = 13,       /* wsic_rans_encode: n_out = lane_symbols, n_in = codes    */
+  WSIC_OP_RANS_DEC = 14        /* wsic_rans_decode(_dequant): n_in = layer columns (1)    */
 };
 
 enum wsic_dmode { WSIC_D_RESID = 0, WSIC_D_DIRECT = 1 };
@@ -247,6 +249,34 @@ int wsic_gather_features(const void* W, int dtype, int64_t n_out, int64_t n_in, 
                          void* stream);
 int wsic_scatter_codes(const int32_t* codes_live, int64_t n_out, int64_t ldql, const int32_t* pos,
                        int64_t n_in, int32_t* codes, int64_t ldq, void* stream);
+
+/*
+ * Entropy coder of the codes [WaterSIC §2 item 3: the integer codes are stored without a fixed
+ * range through an entropy coder; the rate of the layer is the coder's output]. rANS with a static
+ * table (the pooled histogram of the codes within +-2047 scaled to 2^14, plus an escape symbol for
+ * wider codes, stored raw), 32-bit states, 16-bit words; 64 interleaved streams per group, lane l
+ * of group g coding the codes (g L + k) 64 + l, k < L (L = lane_symbols), with the group's words
+ * in decoding order. The container (device memory, little endian) holds a 64-byte header, the
+ * table, per-group word and escape offsets, the streams' initial states, the escapes and the
+ * 16-bit payload.
+ * wsic_rans_bound: container bytes that suffice for n codes.
+ * wsic_rans_encode: codes n contiguous int32 (flattened row-major); out: device buffer of
+ *   out_cap >= wsic_rans_bound(n, L) bytes; *out_bytes (host): bytes written. n < 2^31.
+ *   Workspace: wsic_workspace_bytes(WSIC_OP_RANS_ENC, lane_symbols, n).
+ * wsic_rans_decode: the n codes back (n must match the container); WSIC_E_INVAL for a container
+ *   that is not one or does not decode to the encoder's start states.
+ *   Workspace: wsic_workspace_bytes(WSIC_OP_RANS_DEC, 0, 1).
+ * wsic_rans_decode_dequant: decodes an n_out x n_in layer straight to W_hat_ij = c q_ij / U_jj
+ *   (w_hat_dtype f32 or bf16, contiguous). Workspace: wsic_workspace_bytes(WSIC_OP_RANS_DEC, 0, n_in).
+ */
+size_t wsic_rans_bound(int64_t n, int32_t lane_symbols);
+int wsic_rans_encode(const int32_t* codes, int64_t n, int32_t lane_symbols, uint8_t* out,
+                     size_t out_cap, size_t* out_bytes, void* ws, size_t ws_bytes, void* stream);
+int wsic_rans_decode(const uint8_t* in, size_t in_bytes, int32_t* codes, int64_t n, void* ws,
+                     size_t ws_bytes, void* stream);
+int wsic_rans_decode_dequant(const uint8_t* in, size_t in_bytes, int64_t n_out, int64_t n_in,
+                             const double* U, int64_t ldu, double c, void* W_hat, int w_hat_dtype,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Layer distortion [WaterSIC §1]: D = tr((W - W_hat) Sigma (W - W_hat)^T), W_hat_ij = Delta_j q_ij.

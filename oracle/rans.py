@@ -23,9 +23,9 @@ range-variant ANS (rANS) with a static table built from the layer's pooled code 
 
 Container (little endian): header u32[16] = (magic 0x534E5257, version 1, N lo, N hi, L, groups,
 lo, nsym, 14, n_esc, payload words, 0...), u16 freq[nsym] (padded to 16 bytes), u32 group word
-offsets[groups + 1], u32 group escape offsets[groups + 1], u32 initial states[64 groups], u16
-payload[words] (padded to 16 bytes), int32 escapes[n_esc]; every section starts at a multiple
-of 16 bytes.
+offsets[groups + 1], u32 group escape offsets[groups + 1], u32 initial states[64 groups], int32
+escapes[n_esc], u16 payload[words]; every section starts at a multiple of 16 bytes and the
+container ends with the payload.
 """
 from __future__ import annotations
 
@@ -118,9 +118,9 @@ def encode(codes: np.ndarray, L: int) -> bytes:
     out += bytes(_align16(len(out)) - len(out))
     out += np.asarray(states, dtype=np.uint32).tobytes()
     out += bytes(_align16(len(out)) - len(out))
-    out += np.asarray(payload, dtype=np.uint16).tobytes()
-    out += bytes(_align16(len(out)) - len(out))
     out += np.asarray(escapes, dtype=np.int32).tobytes()
+    out += bytes(_align16(len(out)) - len(out))
+    out += np.asarray(payload, dtype=np.uint16).tobytes()
     return bytes(out)
 
 
@@ -138,9 +138,9 @@ def decode(blob: bytes) -> np.ndarray:
     off = _align16(off + 4 * (G + 1))
     states = np.frombuffer(blob[off:off + 4 * LANES * G], dtype=np.uint32)
     off = _align16(off + 4 * LANES * G)
-    payload = np.frombuffer(blob[off:off + 2 * nw], dtype=np.uint16)
-    off = _align16(off + 2 * nw)
     escapes = np.frombuffer(blob[off:off + 4 * n_esc], dtype=np.int32)
+    off = _align16(off + 4 * n_esc)
+    payload = np.frombuffer(blob[off:off + 2 * nw], dtype=np.uint16)
     cum = np.concatenate([[0], np.cumsum(f)])
     slot_sym = np.repeat(np.arange(nsym), f)
     out = np.zeros(N, dtype=np.int64)

@@ -21,7 +21,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "wsic.h")
 OK, E_INVAL, E_NOT_PD, E_NONFINITE, E_NO_BRACKET, E_RANGE, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7
 F32, BF16 = 0, 1
 (OP_COVARIANCE, OP_CHOLESKY, OP_SIC, OP_WATERFILL, OP_ENTROPY, OP_DISTORTION, OP_CURVATURE,
- OP_SOFTWATER, OP_SOFTWATER_DIST, OP_ENTROPY_COLUMNS, OP_GAUSS_RATE, OP_LMMSE, OP_LIVE) = range(13)
+ OP_SOFTWATER, OP_SOFTWATER_DIST, OP_ENTROPY_COLUMNS, OP_GAUSS_RATE, OP_LMMSE, OP_LIVE, OP_RANS_ENC,
+ OP_RANS_DEC) = range(15)
 RATE_POOLED, RATE_COLUMNS = 0, 1
 _RATE_MODES = {"pooled": RATE_POOLED, "columns": RATE_COLUMNS}
 D_RESID, D_DIRECT = 0, 1
@@ -77,6 +78,10 @@ _SIGS = {
     "wsic_gather_features": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
                                             _p, _i64, _p]),
     "wsic_scatter_codes": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _p, _i64, _p]),
+    "wsic_rans_bound": (_sz, [_i64, ctypes.c_int32]),
+    "wsic_rans_encode": (ctypes.c_int, [_p, _i64, ctypes.c_int32, _p, _sz, ctypes.POINTER(_sz), _p, _sz, _p]),
+    "wsic_rans_decode": (ctypes.c_int, [_p, _sz, _p, _i64, _p, _sz, _p]),
+    "wsic_rans_decode_dequant": (ctypes.c_int, [_p, _sz, _i64, _i64, _p, _i64, _d, _p, ctypes.c_int, _p, _sz, _p]),
     "wsic_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "wsic_profile_reset": (ctypes.c_int, []),
     "wsic_profile_select": (ctypes.c_int, [ctypes.c_char_p]),
@@ -339,6 +344,49 @@ def scatter_codes(codes_live: torch.Tensor, pos: torch.Tensor, n_in: int) -> tor
     _check(lib().wsic_scatter_codes(_p(codes_live.data_ptr()), n_out, _rowmajor(codes_live), _p(pos.data_ptr()),
                                     n_in, _p(q.data_ptr()), n_in, _stream(codes_live)))
     return q
+
+
+def rans_encode(codes: torch.Tensor, lane_symbols: int = 256, out: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, int]:
+    """Entropy-code the (contiguous) int32 codes: (container as a uint8 device tensor, bytes used)."""
+    _need_cuda(codes)
+    if codes.dtype != torch.int32 or not codes.is_contiguous():
+        raise TypeError("codes must be contiguous int32")
+    n = codes.numel()
+    cap = int(lib().wsic_rans_bound(n, lane_symbols))
+    if out is None or out.numel() < cap:
+        out = torch.empty(cap, dtype=torch.uint8, device=codes.device)
+    ws = ws if ws is not None else workspace(OP_RANS_ENC, lane_symbols, n, codes.device)
+    nb = _sz(0)
+    _check(lib().wsic_rans_encode(_p(codes.data_ptr()), n, lane_symbols, _p(out.data_ptr()), out.numel(),
+                                  ctypes.byref(nb), *_ws_args(ws), _stream(codes)))
+    return out, int(nb.value)
+
+
+def rans_decode(blob: torch.Tensor, nbytes: int, n: int, out: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The n int32 codes of a container."""
+    _need_cuda(blob)
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=blob.device)
+    ws = ws if ws is not None else workspace(OP_RANS_DEC, 1, 1, blob.device)
+    _check(lib().wsic_rans_decode(_p(blob.data_ptr()), nbytes, _p(out.data_ptr()), n, *_ws_args(ws),
+                                  _stream(blob)))
+    return out
+
+
+def rans_decode_dequant(blob: torch.Tensor, nbytes: int, n_out: int, n_in: int, U: torch.Tensor, c: float,
+                        dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                        ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """W_hat = c q / U_jj decoded straight from a container."""
+    _need_cuda(blob, U)
+    if out is None:
+        out = torch.empty((n_out, n_in), dtype=dtype, device=blob.device)
+    ws = ws if ws is not None else workspace(OP_RANS_DEC, 1, n_in, blob.device)
+    _check(lib().wsic_rans_decode_dequant(_p(blob.data_ptr()), nbytes, n_out, n_in, _p(U.data_ptr()), _rowmajor(U),
+                                          float(c), _p(out.data_ptr()), _dtype_code(out), *_ws_args(ws),
+                                          _stream(blob)))
+    return out
 
 
 def distortion(W: torch.Tensor, codes: torch.Tensor, U: torch.Tensor, c: float,

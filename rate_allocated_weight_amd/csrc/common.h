@@ -245,6 +245,20 @@ int launch_gather_features(const void* W, int dtype, int64_t n_out, int64_t ldw,
 int launch_scatter_codes(const int32_t* ql, int64_t ldql, const int32_t* pos, int64_t n_in,
                          int64_t n_out, int32_t* q, int64_t ldq, hipStream_t st);
 
+// rANS coder of the codes
+int launch_rans_esc_count(const int32_t* q, int64_t N, int L, int64_t G, uint32_t* cnt, hipStream_t st);
+int launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, hipStream_t st);
+int launch_rans_encode(const int32_t* q, int64_t N, int L, int64_t G, int lo, int nsym,
+                       const uint16_t* freq, const uint32_t* eofs, int32_t* esc_out, uint16_t* temp,
+                       uint32_t* gwords, uint32_t* states, hipStream_t st);
+int launch_rans_compact(const uint16_t* temp, int L, int64_t G, const uint32_t* gwords,
+                        const uint32_t* gofs, uint16_t* payload, hipStream_t st);
+int launch_rans_decode(int mode, const uint16_t* freq, int nsym, int lo, int64_t N, int L, int64_t G,
+                       const uint32_t* gofs, const uint32_t* eofs, const uint32_t* states,
+                       const int32_t* escapes, uint32_t n_esc, const uint16_t* payload,
+                       uint32_t n_words, void* out, int64_t n_in, const double* invd, double c,
+                       int* flags, hipStream_t st);
+
 // softmax curvature (SoftWater): logits, row normalizers, per-class sums
 struct CurvArgs {
   const void* X;

@@ -274,6 +274,60 @@ CurvWs carve_curv(Carve& cv, int64_t rows, int64_t K) {
 
 constexpr int SUMSQ_BLOCKS = 1024;
 
+// ---------------------------------------------------------------- rANS container layout
+constexpr uint32_t RANS_MAGIC = 0x534E5257u, RANS_PROB = 14, RANS_M = 1u << RANS_PROB;
+constexpr int RANS_WIN = 2047, RANS_MAX_SYM = 2 * RANS_WIN + 2;
+inline size_t a16(size_t x) { return (x + 15) / 16 * 16; }
+struct RansLayout {
+  size_t freq, gofs, eofs, states, esc, payload, total;
+};
+RansLayout rans_layout(int64_t G, int64_t nsym, int64_t n_esc, int64_t nw) {
+  RansLayout r;
+  r.freq = 64;
+  r.gofs = a16(r.freq + 2 * (size_t)nsym);
+  r.eofs = a16(r.gofs + 4 * (size_t)(G + 1));
+  r.states = a16(r.eofs + 4 * (size_t)(G + 1));
+  r.esc = a16(r.states + 4 * 64 * (size_t)G);
+  r.payload = a16(r.esc + 4 * (size_t)n_esc);
+  r.total = r.payload + 2 * (size_t)nw;
+  return r;
+}
+int64_t rans_groups(int64_t n, int64_t L) { return (n + 64 * L - 1) / (64 * L); }
+
+// frequencies scaled to 2^14: max(1, floor(c M / N)) for every present symbol, the remainder to the
+// most frequent symbol, an excess taken one by one from the largest frequency above 1 (lowest index
+// first on ties)
+std::vector<uint16_t> rans_normalize(const std::vector<int64_t>& counts, int64_t N) {
+  const size_t n = counts.size();
+  std::vector<int64_t> f(n, 0);
+  int64_t sum = 0;
+  for (size_t i = 0; i < n; ++i) {
+    if (counts[i] > 0) f[i] = std::max<int64_t>(1, (counts[i] * (int64_t)RANS_M) / N);
+    sum += f[i];
+  }
+  int64_t diff = (int64_t)RANS_M - sum;
+  if (diff > 0) {
+    size_t im = 0;
+    for (size_t i = 1; i < n; ++i)
+      if (counts[i] > counts[im]) im = i;
+    f[im] += diff;
+  }
+  while (diff < 0) {
+    size_t im = 0;
+    int64_t best = -1;
+    for (size_t i = 0; i < n; ++i)
+      if (f[i] > 1 && f[i] > best) {
+        best = f[i];
+        im = i;
+      }
+    f[im] -= 1;
+    ++diff;
+  }
+  std::vector<uint16_t> out(n);
+  for (size_t i = 0; i < n; ++i) out[i] = (uint16_t)f[i];
+  return out;
+}
+
 size_t ws_bytes_for(int op, int64_t n_out, int64_t n_in) {
   Carve cv(nullptr);
   switch (op) {
@@ -312,6 +366,18 @@ size_t ws_bytes_for(int op, int64_t n_out, int64_t n_in) {
     case WSIC_OP_LIVE:
       cv.take<int>(FLAGS_BYTES / sizeof(int));
       cv.take<long long>(1);
+      break;
+    case WSIC_OP_RANS_ENC: {  // n_out = symbols per lane, n_in = number of codes
+      const int64_t G = rans_groups(n_in, n_out);
+      cv.take<int>(FLAGS_BYTES / sizeof(int));
+      carve_hist(cv);
+      cv.take<uint32_t>(2 * (size_t)G + 2);
+      cv.take<uint16_t>((size_t)G * 64 * (size_t)n_out);
+      break;
+    }
+    case WSIC_OP_RANS_DEC:  // n_in = columns of the layer (dequantization)
+      cv.take<int>(FLAGS_BYTES / sizeof(int));
+      cv.take<double>((size_t)n_in);
       break;
     case WSIC_OP_GAUSS_RATE:
       cv.take<int>(FLAGS_BYTES / sizeof(int));
@@ -872,7 +938,8 @@ const char* wsic_status_str(int s) {
 
 size_t wsic_workspace_bytes(int op, int64_t n_out, int64_t n_in) {
   if (n_in <= 0 ||
-      (op != WSIC_OP_COVARIANCE && op != WSIC_OP_CHOLESKY && op != WSIC_OP_LIVE && n_out <= 0))
+      (op != WSIC_OP_COVARIANCE && op != WSIC_OP_CHOLESKY && op != WSIC_OP_LIVE && op != WSIC_OP_RANS_DEC &&
+       n_out <= 0))
     return 0;
   return ws_bytes_for(op, n_out, n_in);
 }
@@ -1547,6 +1614,182 @@ int wsic_scatter_codes(const int32_t* codes_live, int64_t n_out, int64_t ldql, c
     return launch_scatter_codes(codes_live, ldql, pos, n_in, n_out, codes, ldq, (hipStream_t)stream);
   } catch (...) {
     set_error("scatter_codes: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+size_t wsic_rans_bound(int64_t n, int32_t lane_symbols) {
+  if (n <= 0 || lane_symbols <= 0) return 0;
+  const int64_t G = rans_groups(n, lane_symbols);
+  return rans_layout(G, RANS_MAX_SYM, n, n).total;
+}
+
+int wsic_rans_encode(const int32_t* codes, int64_t n, int32_t lane_symbols, uint8_t* out,
+                     size_t out_cap, size_t* out_bytes, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    if (!codes || n <= 0 || lane_symbols <= 0 || lane_symbols > 65536 || !out || !out_bytes ||
+        n > 0x7fffffffLL) {
+      set_error("rans_encode: bad argument");
+      return WSIC_E_INVAL;
+    }
+    const int L = lane_symbols;
+    const int64_t G = rans_groups(n, L);
+    if (out_cap < wsic_rans_bound(n, L)) {
+      set_error("rans_encode: output capacity %zu below the bound %zu", out_cap, wsic_rans_bound(n, L));
+      return WSIC_E_WORKSPACE;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_RANS_ENC, L, n, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    Carve cv(ws);
+    cv.take<int>(FLAGS_BYTES / sizeof(int));
+    const HistWs h = carve_hist(cv);
+    uint32_t* cnt = cv.take<uint32_t>(2 * (size_t)G + 2);
+    uint32_t* gwords = cnt + G;
+    uint16_t* temp = cv.take<uint16_t>((size_t)G * 64 * (size_t)L);
+    // table from the pooled histogram (window +-2047; wider codes are the escapes)
+    WSIC_TRY(launch_fill_zero(h.bins, HIST_CLEAR_BYTES, st));
+    WSIC_TRY(launch_hist(codes, 1, n, n, h.bins, h.ovf, h.ovf_count, st));
+    std::vector<unsigned long long> bins(HIST_BINS);
+    unsigned novf = 0;
+    const ReadPiece pb[2] = {{bins.data(), h.bins, HIST_BINS * sizeof(unsigned long long)},
+                             {&novf, h.ovf_count, sizeof(unsigned)}};
+    WSIC_TRY(read_back(pb, 2, st));
+    int lo = 0, hi = 0;
+    bool any = false;
+    for (int b = 0; b < HIST_BINS; ++b)
+      if (bins[b]) {
+        if (!any) lo = b - HIST_HALF;
+        hi = b - HIST_HALF;
+        any = true;
+      }
+    const int nsym = hi - lo + 2;
+    std::vector<int64_t> counts(nsym, 0);
+    for (int v = lo; v <= hi && any; ++v) counts[v - lo] = (int64_t)bins[v + HIST_HALF];
+    counts[nsym - 1] = (int64_t)novf;
+    const std::vector<uint16_t> freq = rans_normalize(counts, n);
+    // escape offsets, then the layout (payload size is known after encoding); the sections before
+    // the escapes and the padding after them are cleared first, so the container is fully defined
+    WSIC_TRY(launch_rans_esc_count(codes, n, L, G, cnt, st));
+    RansLayout lay = rans_layout(G, nsym, 0, 0);
+    WSIC_TRY(launch_fill_zero(out, lay.esc, st));
+    uint32_t* eofs = (uint32_t*)(out + lay.eofs);
+    WSIC_TRY(launch_scan_u32(cnt, G, eofs, st));
+    uint32_t n_esc = 0;
+    const ReadPiece pe{&n_esc, eofs + G, sizeof(uint32_t)};
+    WSIC_TRY(read_back(&pe, 1, st));
+    if (n_esc != novf) {
+      set_error("rans_encode: internal: %u escapes counted, %u in the histogram", n_esc, novf);
+      return WSIC_E_INVAL;
+    }
+    lay = rans_layout(G, nsym, n_esc, 0);
+    if (lay.payload > lay.esc + 4 * (size_t)n_esc)
+      WSIC_TRY(launch_fill_zero(out + lay.esc + 4 * (size_t)n_esc, lay.payload - lay.esc - 4 * (size_t)n_esc, st));
+    WSIC_HIP_TRY(hipMemcpyAsync(out + lay.freq, freq.data(), 2 * freq.size(), hipMemcpyHostToDevice, st));
+    WSIC_TRY(launch_rans_encode(codes, n, L, G, lo, nsym, (const uint16_t*)(out + lay.freq), eofs,
+                                (int32_t*)(out + lay.esc), temp, gwords, (uint32_t*)(out + lay.states), st));
+    uint32_t* gofs = (uint32_t*)(out + lay.gofs);
+    WSIC_TRY(launch_scan_u32(gwords, G, gofs, st));
+    uint32_t nw = 0;
+    const ReadPiece pw{&nw, gofs + G, sizeof(uint32_t)};
+    WSIC_TRY(read_back(&pw, 1, st));
+    lay = rans_layout(G, nsym, n_esc, nw);
+    WSIC_TRY(launch_rans_compact(temp, L, G, gwords, gofs, (uint16_t*)(out + lay.payload), st));
+    uint32_t hdr[16] = {RANS_MAGIC, 1u, (uint32_t)(n & 0xffffffffLL), (uint32_t)(n >> 32), (uint32_t)L,
+                        (uint32_t)G, (uint32_t)lo, (uint32_t)nsym, RANS_PROB, n_esc, nw, 0, 0, 0, 0, 0};
+    WSIC_HIP_TRY(hipMemcpyAsync(out, hdr, sizeof hdr, hipMemcpyHostToDevice, st));
+    WSIC_HIP_TRY(hipStreamSynchronize(st));  // the host buffers of the copies above
+    *out_bytes = lay.total;
+    return WSIC_OK;
+  } catch (...) {
+    set_error("rans_encode: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+static int rans_decode_any(const uint8_t* in, size_t in_bytes, int mode, void* dst, int64_t n,
+                           int64_t n_in, const double* invd, double c, int* flags, hipStream_t st) {
+  if (in_bytes < 64) {
+    set_error("rans_decode: container too short");
+    return WSIC_E_INVAL;
+  }
+  uint32_t hdr[16];
+  WSIC_HIP_TRY(hipMemcpyAsync(hdr, in, sizeof hdr, hipMemcpyDeviceToHost, st));
+  WSIC_HIP_TRY(hipStreamSynchronize(st));
+  const int64_t N = (int64_t)hdr[2] | ((int64_t)hdr[3] << 32);
+  const int L = (int)hdr[4];
+  const int64_t G = hdr[5];
+  const int lo = (int)hdr[6];
+  const int nsym = (int)hdr[7];
+  if (hdr[0] != RANS_MAGIC || hdr[1] != 1u || hdr[8] != RANS_PROB || L <= 0 || nsym < 2 ||
+      nsym > RANS_MAX_SYM || G != rans_groups(N, L)) {
+    set_error("rans_decode: not a code container");
+    return WSIC_E_INVAL;
+  }
+  if (N != n) {
+    set_error("rans_decode: container holds %lld codes, %lld expected", (long long)N, (long long)n);
+    return WSIC_E_INVAL;
+  }
+  const RansLayout lay = rans_layout(G, nsym, hdr[9], hdr[10]);
+  if (in_bytes < lay.total) {
+    set_error("rans_decode: container truncated (%zu of %zu bytes)", in_bytes, lay.total);
+    return WSIC_E_INVAL;
+  }
+  WSIC_TRY(launch_fill_zero(flags, FLAGS_BYTES, st));
+  WSIC_TRY(launch_rans_decode(mode, (const uint16_t*)(in + lay.freq), nsym, lo, N, L, G,
+                              (const uint32_t*)(in + lay.gofs), (const uint32_t*)(in + lay.eofs),
+                              (const uint32_t*)(in + lay.states), (const int32_t*)(in + lay.esc),
+                              hdr[9], (const uint16_t*)(in + lay.payload), hdr[10], dst, n_in, invd, c,
+                              flags, st));
+  int f = 0;
+  WSIC_TRY(read_flags(flags, &f, st));
+  if (f & FLAG_RANGE) {
+    set_error("rans_decode: a stream did not end in its start state (corrupt container)");
+    return WSIC_E_INVAL;
+  }
+  return flags_status(f, "rans_decode");
+}
+
+int wsic_rans_decode(const uint8_t* in, size_t in_bytes, int32_t* codes, int64_t n, void* ws,
+                     size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    if (!in || !codes || n <= 0) {
+      set_error("rans_decode: bad argument");
+      return WSIC_E_INVAL;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_RANS_DEC, 1, 1, ws, ws_bytes));
+    return rans_decode_any(in, in_bytes, 0, codes, n, 1, nullptr, 0.0, (int*)ws, (hipStream_t)stream);
+  } catch (...) {
+    set_error("rans_decode: internal exception");
+    return WSIC_E_INVAL;
+  }
+}
+
+int wsic_rans_decode_dequant(const uint8_t* in, size_t in_bytes, int64_t n_out, int64_t n_in,
+                             const double* U, int64_t ldu, double c, void* W_hat, int w_hat_dtype,
+                             void* ws, size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    if (!in || n_out <= 0 || n_in <= 0 || !U || ldu < n_in || !(c > 0.0) || !std::isfinite(c) ||
+        !W_hat || (w_hat_dtype != WSIC_F32 && w_hat_dtype != WSIC_BF16)) {
+      set_error("rans_decode_dequant: bad argument");
+      return WSIC_E_INVAL;
+    }
+    WSIC_TRY(check_ws(WSIC_OP_RANS_DEC, 1, n_in, ws, ws_bytes));
+    hipStream_t st = (hipStream_t)stream;
+    Carve cv(ws);
+    int* flags = cv.take<int>(FLAGS_BYTES / sizeof(int));
+    double* invd = cv.take<double>((size_t)n_in);
+    WSIC_TRY(launch_fill_zero(flags, FLAGS_BYTES, st));
+    WSIC_TRY(launch_prep(U, ldu, n_in, invd, flags, st));
+    int f = 0;
+    WSIC_TRY(read_flags(flags, &f, st));
+    WSIC_TRY(flags_status(f, "rans_decode_dequant"));
+    return rans_decode_any(in, in_bytes, w_hat_dtype == WSIC_BF16 ? 2 : 1, W_hat, n_out * n_in, n_in,
+                           invd, c, flags, st);
+  } catch (...) {
+    set_error("rans_decode_dequant: internal exception");
     return WSIC_E_INVAL;
   }
 }
