@@ -89,6 +89,8 @@ def parse():
     ap.add_argument("--rate-mode", default="pooled", choices=["pooled", "columns"],
                     help="rate held to the target: pooled code entropy, or the mean per-column entropy "
                          "(then the gap to the Gaussian limit is reported)")
+    ap.add_argument("--coder-lane-symbols", type=int, default=1024,
+                    help="codes per rANS stream for the entropy-coder measurement (0: skip it)")
     ap.add_argument("--smoothing", type=float, default=0.05,
                     help="weight of the uniform distribution mixed into the calibration softmax")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -357,6 +359,49 @@ def main():
             phase_ms[name] += ev[k].elapsed_time(ev[k + 1]) / args.steps
     ms_from_u = phase_ms["curvature"] + phase_ms["waterfill"] + phase_ms["entropy+distortion"]
 
+    # the codes of the last step through the entropy coder (after the timed region): the rate the
+    # coder actually writes against the empirical entropy, and its encode / decode times
+    coder = None
+    if args.coder_lane_symbols > 0:
+        try:
+            cc = (wf["codes"] if sw else codes).contiguous()
+            n = cc.numel()
+            Ls = args.coder_lane_symbols
+            ws_enc = L.workspace(L.OP_RANS_ENC, Ls, n, dev)
+            ws_dec = L.workspace(L.OP_RANS_DEC, 1, n_in, dev)
+            cap = int(L.lib().wsic_rans_bound(n, Ls))
+            blob = torch.empty(cap, dtype=torch.uint8, device=dev)
+            back = torch.empty_like(cc)
+            w16 = torch.empty((n_out, n_in), dtype=torch.bfloat16, device=dev)
+
+            def timed(fn, reps=5):
+                fn()
+                torch.cuda.synchronize()
+                t = time.perf_counter()
+                for _ in range(reps):
+                    r = fn()
+                torch.cuda.synchronize()
+                return r, 1e3 * (time.perf_counter() - t) / reps
+
+            (_, nb), t_enc = timed(lambda: L.rans_encode(cc, Ls, out=blob, ws=ws_enc))
+            _, t_dec = timed(lambda: L.rans_decode(blob, nb, n, out=back, ws=ws_dec))
+            t_dq = None
+            if not sw:  # (the class-aware grids of SoftWater need their row scales: not timed here)
+                _, t_dq = timed(lambda: L.rans_decode_dequant(blob, nb, n_out, n_in, sigma, wf["c"], out=w16,
+                                                              ws=ws_dec))
+            ok = bool(torch.equal(back, cc))
+            coder = {"lane_symbols": Ls, "bytes": nb, "bits_per_code": 8.0 * nb / n, "entropy_bits": wf["rate"],
+                     "excess_bits": 8.0 * nb / n - wf["rate"], "lossless": ok, "encode_ms": round(t_enc, 4),
+                     "decode_ms": round(t_dec, 4),
+                     "decode_to_bf16_ms": round(t_dq, 4) if t_dq is not None else None,
+                     "decode_codes_GBps": round(4.0 * n / (t_dec * 1e-3) / 1e9, 2),
+                     "decode_bf16_GBps": round(2.0 * n / (t_dq * 1e-3) / 1e9, 2) if t_dq is not None else None,
+                     "note": "API calls timed with host clocks (each reads the container header back first)"}
+            if not sw and args.rate_mode == "columns":
+                coder["entropy_bits"] = None  # the step's rate is per column; the coder uses one table
+        except Exception as e:  # the measurement never takes the benchmark down
+            coder = {"error": str(e)}
+
     kernels = {}
     roofline = None
     if not args.no_profile:
@@ -412,6 +457,7 @@ def main():
         "kernels": kernels,
         "families_warmup": families,
         "trailing_update": trailing,
+        "entropy_coder": coder,
     }
     if it_gap is not None:
         out["it_gap"] = it_gap

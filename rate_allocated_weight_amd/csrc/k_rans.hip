@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void k_rans_decode(const uint16_t* __restrict_
   uint32_t x = states[g * RLANES + lane];
   uint32_t wp = gofs[g], ep = eofs[g];
   const uint64_t below = lanes_below(lane);
-  int64_t col = ((g * L) * RLANES + lane) % (n_in > 0 ? n_in : 1);
+  int64_t col = MODE != 0 ? ((g * L) * RLANES + lane) % n_in : 0;
   for (int k = 0; k < L; ++k) {
     const int64_t p = (g * L + k) * RLANES + lane;
     const bool active = p < N;
@@ -222,8 +222,10 @@ __global__ __launch_bounds__(256) void k_rans_decode(const uint16_t* __restrict_
         }
       }
     }
-    col += RLANES;
-    while (col >= n_in && n_in > 0) col -= n_in;
+    if (MODE != 0) {  // the column of the next step's weight
+      col += RLANES;
+      while (col >= n_in) col -= n_in;
+    }
   }
   if (x != RLOW) atomicOr(flags, FLAG_RANGE);  // every stream ends in the encoder's start state
 }
