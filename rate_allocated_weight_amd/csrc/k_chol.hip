@@ -7,13 +7,11 @@
 //                   instructions on the same data, so every copy of U_kk is bitwise identical)
 //                   and applies each pivot's elimination to its slab as it goes, which is the
 //                   triangular solve X = U_kk^-T A_k,rest. Thread (wave w, lane j) holds rows
-//                   8w .. 8w+7 of column j of the diagonal block and of its slab. At pivot k
-//                   the owning wave publishes row k of both through LDS; every thread reads the
-//                   pivot and the 8 row entries it needs with all loads in flight and scales
-//                   by 1/sqrt(p). The update has no branches (rows above the pivot meet a zero
-//                   multiplier); the pivot row buffers alternate with the parity of k, so one
-//                   barrier per pivot suffices. Nothing is written to global memory inside the
-//                   pivot loop.
+//                   8w .. 8w+7 of column j of the diagonal block and of its slab. Pivots go in
+//                   groups of 8: wave w factors pivots 8w .. 8w+7 on its own rows (pivot and
+//                   row entries by readlane, no workgroup barrier), publishes those 8 rows of U
+//                   and X through LDS, and after one barrier the waves below apply them as one
+//                   rank-8 update. Nothing is written to global memory inside the pivot loop.
 //   trailing      : A_rest,rest -= X^T X on upper tiles (fp64 MFMA GEMM, k-major operands).
 //                   k_chol_step launches it together with the next panel, whose workgroups
 //                   first apply the update to the next block row themselves.
@@ -40,62 +38,97 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
   return y;
 }
 
+// Rows published by the owner of a pivot group: the group's rows of U and of the solved slab X,
+// double-buffered by the parity of the group, and the group's first failing pivot (0: none).
+struct PanelLds {
+  double u[2][RPW][NB];
+  double x[2][RPW][NB];
+  int bad[2];
+};
+
+// v from lane `lane` (uniform) of this wave
+__device__ __forceinline__ double lane_bcast(double v, int lane) {
+  const long long bits = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)bits, lane);
+  const int hi = __builtin_amdgcn_readlane((int)(bits >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
 // The pivot loop of one panel workgroup and its stores. a[s], sl[s] hold rows RPW w + s of
 // column j of the diagonal block and of this workgroup's slab (block b > 0), as loaded.
+// Pivots go in groups of RPW, one group per wave: wave wk holds rows RPW wk .. RPW wk + RPW - 1,
+// which have every earlier group's update when its turn comes, so it factors them alone (pivot
+// and row entries of its own rows by readlane, no workgroup barrier), solves its slab rows with
+// them, and publishes the RPW finished rows of U and X through LDS; after one barrier every wave
+// below applies them as one rank-RPW update. Entries left of the diagonal are published as zeros
+// and are scratch in the registers.
 // The diagonal block (workgroup 0) goes to ud (NB x NB, zeros below the diagonal), not into A:
 // other panel workgroups of the same launch may not have read A's copy of it yet.
+// pl may alias the memory the caller staged a and sl through: the first barrier orders them.
 __device__ __forceinline__ void panel_factor(double (&a)[RPW], double (&sl)[RPW], double* A,
                                              int64_t lda, int64_t kb, int nbk, int64_t n,
-                                             int64_t* info, int b, double (*row)[NB],
-                                             double (*srow)[NB], double* ud) {
+                                             int64_t* info, int b, PanelLds* pl, double* ud) {
   const int j = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t c = kb + (int64_t)b * NB + j;  // slab column (b > 0)
   const bool cin = b > 0 && c < n;
-  // pivots in groups of RPW: the group loop stays a loop (code size: the instruction cache
-  // holds one group), the RPW pivots of a group are unrolled so register indices are constants
+  __syncthreads();
 #pragma unroll 1
   for (int wk = 0; wk < NB / RPW; ++wk) {
+    const int k0 = RPW * wk;
+    if (k0 >= nbk) break;  // uniform
+    const int par = wk & 1;
+    if (w == wk) {
+      int bad = 0;
 #pragma unroll
-  for (int sk = 0; sk < RPW; ++sk) {
-    const int k = RPW * wk + sk;
-    if (k < nbk) {  // uniform
-      const int pb = sk & 1;
-      if (w == wk) {
-        // row k of the block is published with zeros left of the diagonal (the lower-triangle
-        // entries a thread holds are scratch, never stored)
-        row[pb][j] = (j >= k) ? a[sk] : 0.0;
-        srow[pb][j] = sl[sk];
-      }
-      __syncthreads();
-      const double p = row[pb][k];
-      const double rj = row[pb][j];
-      const double xs = srow[pb][j];
-      if (!(p > 0.0) || !isfinite(p)) {  // uniform: every thread sees the same pivot
-        if (b == 0 && threadIdx.x == 0) *info = kb + k + 1;
-        return;
-      }
-      const double inv = rsqrt_f64(p);
-      const double sj = rj * inv;  // U(k, j)
-      const double xk = xs * inv;  // X(k, c)
-      // Branch-free elimination: the published row k is zero left of the diagonal, so rows above
-      // the pivot get a zero multiplier and keep their values, and no upper entry is touched by
-      // a column left of the pivot; the pivot row itself is then overwritten with its scaled
-      // entries. U(k,i) U(k,j) = row_k(i) * (U(k,j) / sqrt(p)): one multiplier per column.
-      const double mj = sj * inv, mx = xk * inv;
-      double rr[RPW];
+      for (int sk = 0; sk < RPW; ++sk) {
+        const int k = k0 + sk;
+        if (k < nbk) {  // uniform
+          const double p0 = lane_bcast(a[sk], k);
+          const bool ok = (p0 > 0.0) && isfinite(p0);
+          bad = (bad == 0 && !ok) ? k + 1 : bad;
+          const double p = ok ? p0 : 1.0;
+          const double inv = rsqrt_f64(p);
+          const double u = (j == k) ? p * inv : a[sk] * inv;  // U(k, j), j >= k
+          const double x = sl[sk] * inv;                      // X(k, c)
+          a[sk] = (j >= k) ? u : 0.0;
+          sl[sk] = x;
 #pragma unroll
-      for (int s = 0; s < RPW; ++s) rr[s] = row[pb][RPW * w + s];
+          for (int s = sk + 1; s < RPW; ++s) {
+            const double uks = lane_bcast(u, k0 + s);  // U(k, k0 + s)
+            a[s] = fma(-uks, u, a[s]);
+            sl[s] = fma(-uks, x, sl[s]);
+          }
+        }
+      }
 #pragma unroll
       for (int s = 0; s < RPW; ++s) {
-        a[s] = fma(-rr[s], mj, a[s]);
-        sl[s] = fma(-rr[s], mx, sl[s]);
+        pl->u[par][s][j] = a[s];
+        pl->x[par][s][j] = sl[s];
       }
-      const bool own = (w == wk);
-      a[sk] = own ? ((j == k) ? p * inv : sj) : a[sk];
-      sl[sk] = own ? xk : sl[sk];
+      if (j == 0) pl->bad[par] = bad;
     }
-  }
+    __syncthreads();
+    const int bad = pl->bad[par];
+    if (bad != 0) {  // uniform: every thread read the same flag
+      if (b == 0 && threadIdx.x == 0) *info = kb + bad;
+      return;
+    }
+    if (w > wk) {
+#pragma unroll
+      for (int t = 0; t < RPW; ++t) {
+        if (k0 + t < nbk) {  // uniform
+          const double ut = pl->u[par][t][j];
+          const double xt = pl->x[par][t][j];
+#pragma unroll
+          for (int s = 0; s < RPW; ++s) {
+            const double uis = pl->u[par][t][RPW * w + s];  // U(k0 + t, RPW w + s)
+            a[s] = fma(-uis, ut, a[s]);
+            sl[s] = fma(-uis, xt, sl[s]);
+          }
+        }
+      }
+    }
   }
 #pragma unroll
   for (int s = 0; s < RPW; ++s) {
@@ -113,10 +146,7 @@ __device__ __forceinline__ void panel_factor(double (&a)[RPW], double (&sl)[RPW]
 __global__ __launch_bounds__(64 * PANEL_WAVES) void k_potrf_panel(double* A, int64_t lda, int64_t kb,
                                                                  int nbk, int64_t n, int64_t* info,
                                                                  double* ud) {
-  // raw row k of the diagonal block and of this workgroup's slab, double-buffered by the parity
-  // of k so that one barrier per pivot separates its writes from the previous pivot's reads
-  __shared__ double row[2][NB];
-  __shared__ double srow[2][NB];
+  __shared__ PanelLds pl;
   if (*info != 0) return;
   const int j = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -130,7 +160,7 @@ __global__ __launch_bounds__(64 * PANEL_WAVES) void k_potrf_panel(double* A, int
     a[s] = (i <= j && j < nbk) ? A[(kb + i) * lda + kb + j] : (i == j ? 1.0 : 0.0);
     sl[s] = (cin && i < nbk) ? A[(kb + i) * lda + c] : 0.0;
   }
-  panel_factor(a, sl, A, lda, kb, nbk, n, info, b, row, srow, ud);
+  panel_factor(a, sl, A, lda, kb, nbk, n, info, b, &pl, ud);
 }
 
 // The factored diagonal block of step kb from its slot into A (64 x 64 block, ld NB slot)
@@ -211,8 +241,7 @@ __global__ __launch_bounds__(64 * PANEL_WAVES) void k_chol_step(double* A, int64
   using namespace cupd;
   static_assert(PANEL_WAVES == 8, "tile layout: 8 waves in 2 x 4");
   __shared__ __attribute__((aligned(1024))) double Xs[2][T][T];
-  __shared__ double row[2][NB];
-  __shared__ double srow[2][NB];
+  static_assert(sizeof(PanelLds) <= sizeof(Xs), "panel rows live in the operand strips");
   if (*info != 0) return;
   const int64_t c0 = kb + NB, m = n - c0;
   const int lane = threadIdx.x & 63;
@@ -261,7 +290,8 @@ __global__ __launch_bounds__(64 * PANEL_WAVES) void k_chol_step(double* A, int64
       a[s] = (i <= j && j < nbk) ? Xs[0][i][j] : (i == j ? 1.0 : 0.0);
       sl[s] = (cin && i < nbk) ? Xs[1][i][j] : 0.0;
     }
-    panel_factor(a, sl, A, lda, c0, nbk, n, info, b, row, srow, ud_next);
+    panel_factor(a, sl, A, lda, c0, nbk, n, info, b, reinterpret_cast<PanelLds*>(&Xs[0][0][0]),
+                 ud_next);
     return;
   }
 
