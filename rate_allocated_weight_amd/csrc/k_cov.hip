@@ -129,8 +129,8 @@ __global__ __launch_bounds__(256) void k_syrk_bf16(const uint16_t* __restrict__ 
 
 // bf16 X, pipelined: Sigma tile 128 x 128 per 256-thread workgroup (upper tiles only, enumerated
 // triangularly); 4 waves in 2 x 2, each 64 x 64 = 2 x 2 fragments of v_mfma_f32_32x32x16_bf16.
-// Per K-step of 64 calibration rows the two 64 x 128 row strips of X (the tile's rows and its
-// columns of Sigma) go global -> LDS directly (global_load_lds_dwordx4) through a ring of 4
+// Per K-step of 128 calibration rows the two 128 x 128 row strips of X (the tile's rows and its
+// columns of Sigma) go global -> LDS directly (global_load_lds_dwordx4) through a ring of 2
 // buffers, in X's own row-major layout with the 16-byte chunks of row r XOR-swizzled by 2 (r & 3).
 // The MFMA wants 8 consecutive rows of X per lane; ds_read_b64_tr_b16 delivers them: within each
 // 16-lane group, lane i receives element i % 4 of the 8-byte rows addressed by lanes 4v + i / 4
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void k_syrk_bf16(const uint16_t* __restrict__ 
 // X's span below 2 GiB.
 namespace sdma {
 constexpr int T = 128, TKR = 128, STAGES = 2, FOLD_STEPS = 256 / TKR;
-constexpr int STRIP = TKR * T * 2;  // 16 KiB
+constexpr int STRIP = TKR * T * 2;  // 32 KiB: 128 rows x 128 bf16
 constexpr int STAGE = 2 * STRIP;
 constexpr int INS = STRIP / 4096;   // DMA instructions per wave per strip
 constexpr int DMA = 2 * INS;
