@@ -350,6 +350,36 @@ int wsic_softwater_distortion(const int32_t* codes, int64_t n_out, int64_t n_in,
                               void* stream);
 
 /*
+ * Diagnostic switches (process-wide, default off). They select alternative kernel paths that
+ * compute the same results, so that tests can compare the paths with each other and with the
+ * reference; nothing in normal use needs them. Set them only while no other library call runs.
+ *   WSIC_DBG_FP64_PRODUCT   1: the SIC interference by the fp64 MFMA product instead of the
+ *                              exact int8 digit-plane product (default 0)
+ *   WSIC_DBG_SUPER_BLOCKS   0: one SIC launch per 128-column block instead of up to four
+ *                              (default 1)
+ *   WSIC_DBG_GUARD_SCALE    >= 1: multiplies the int8 product's error bound, so that more
+ *                              rounding decisions are re-checked in fp64 (default 1); values
+ *                              below 1 are refused (they would weaken the exactness guarantee)
+ *   WSIC_DBG_CHOL_FUSED     0: Cholesky update and next panel as separate launches (default 1)
+ *   WSIC_DBG_LOGITS_GENERIC 1: fp64 VALU logits for bf16 curvature inputs too (default 0)
+ *   WSIC_DBG_TRACE          1: one line per SIC pass of the rate controller on stderr (default 0)
+ * wsic_debug_set returns WSIC_E_INVAL for an unknown knob or a value out of range;
+ * wsic_debug_get writes the current value to *value (host); wsic_debug_reset restores every
+ * default.
+ */
+enum wsic_debug_knob {
+  WSIC_DBG_FP64_PRODUCT = 0,
+  WSIC_DBG_SUPER_BLOCKS = 1,
+  WSIC_DBG_GUARD_SCALE = 2,
+  WSIC_DBG_CHOL_FUSED = 3,
+  WSIC_DBG_LOGITS_GENERIC = 4,
+  WSIC_DBG_TRACE = 5
+};
+int wsic_debug_set(int knob, double value);
+int wsic_debug_get(int knob, double* value);
+void wsic_debug_reset(void);
+
+/*
  * Kernel timing. While enabled, every kernel launch is bracketed by HIP events on its own
  * stream; wsic_profile_read synchronizes and returns, for the kernel family `name`, the
  * launch count, the summed event time in ms and the summed algorithmic work (flops for the

@@ -27,6 +27,9 @@ RATE_POOLED, RATE_COLUMNS = 0, 1
 _RATE_MODES = {"pooled": RATE_POOLED, "columns": RATE_COLUMNS}
 D_RESID, D_DIRECT = 0, 1
 WF_AUTO, WF_SECANT, WF_BISECT = 0, 1, 2
+# diagnostic switches (wsic_debug_set)
+DEBUG_KNOBS = {"fp64_product": 0, "super_blocks": 1, "guard_scale": 2, "chol_fused": 3,
+               "logits_generic": 4, "trace": 5}
 
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
@@ -82,6 +85,9 @@ _SIGS = {
     "wsic_rans_encode": (ctypes.c_int, [_p, _i64, ctypes.c_int32, _p, _sz, ctypes.POINTER(_sz), _p, _sz, _p]),
     "wsic_rans_decode": (ctypes.c_int, [_p, _sz, _p, _i64, _p, _sz, _p]),
     "wsic_rans_decode_dequant": (ctypes.c_int, [_p, _sz, _i64, _i64, _p, _i64, _d, _p, ctypes.c_int, _p, _sz, _p]),
+    "wsic_debug_set": (ctypes.c_int, [ctypes.c_int, _d]),
+    "wsic_debug_get": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(_d)]),
+    "wsic_debug_reset": (None, []),
     "wsic_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "wsic_profile_reset": (ctypes.c_int, []),
     "wsic_profile_select": (ctypes.c_int, [ctypes.c_char_p]),
@@ -492,6 +498,39 @@ def softwater_distortion(codes: torch.Tensor, U: torch.Tensor, c: float, lam: to
         _p(w_hat.data_ptr() if w_hat is not None else 0), wdt, _rowmajor(w_hat) if w_hat is not None else n_in,
         *_ws_args(ws), _stream(codes)))
     return d.value, w_hat
+
+
+# ------------------------------------------------------------------------------ diagnostic switches
+def debug_set(knob: str, value: float) -> None:
+    """Select an alternative kernel path (same results) for tests; see wsic_debug_set."""
+    _check(lib().wsic_debug_set(DEBUG_KNOBS[knob], float(value)))
+
+
+def debug_get(knob: str) -> float:
+    v = _d(0)
+    _check(lib().wsic_debug_get(DEBUG_KNOBS[knob], ctypes.byref(v)))
+    return v.value
+
+
+def debug_reset() -> None:
+    lib().wsic_debug_reset()
+
+
+class debug:
+    """Context manager: `with debug(guard_scale=3e4): ...` sets the switches and restores every
+    default on exit."""
+
+    def __init__(self, **knobs: float):
+        self.knobs = knobs
+
+    def __enter__(self):
+        for k, v in self.knobs.items():
+            debug_set(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        debug_reset()
+        return False
 
 
 # ------------------------------------------------------------------------------ kernel timing

@@ -2,6 +2,7 @@
 // controller. All arithmetic runs in the kernels of this library; this file only orders
 // launches on the caller's stream and reads back scalars.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -544,15 +545,23 @@ struct SicCtx {
   const double* rs;    // class scales: row r of Y = W U^T is multiplied by rs[r] (nullable)
 };
 
+// diagnostic switches (wsic_debug_set): alternative paths with the same results
+struct DebugKnobs {
+  std::atomic<bool> fp64_product{false};
+  std::atomic<bool> super_blocks{true};
+  std::atomic<double> guard_scale{1.0};
+  std::atomic<bool> chol_fused{true};
+  std::atomic<bool> logits_generic{false};
+  std::atomic<bool> trace{false};
+};
+DebugKnobs g_dbg;
+
 SicCtx make_ctx(int64_t n_out, int64_t n_in, const void* W, int dtype, int64_t ldw,
                 const double* U, int64_t ldu, const SicWs& ws, hipStream_t st) {
   SicCtx x{n_out, n_in, W, dtype, ldw, U, ldu, ws, st, true, 1.0, true, nullptr};
-  if (const char* e = std::getenv("WSIC_FP64_TRAIL")) x.i8 = (e[0] == '0');
-  if (const char* e = std::getenv("WSIC_SUPER_BLOCKS")) x.super_launch = (e[0] != '0');
-  if (const char* e = std::getenv("WSIC_GUARD_SCALE")) {
-    const double v = std::atof(e);
-    if (v > 0.0) x.guard_scale = v;
-  }
+  x.i8 = !g_dbg.fp64_product.load();
+  x.super_launch = g_dbg.super_blocks.load();
+  x.guard_scale = g_dbg.guard_scale.load();
   return x;
 }
 
@@ -750,7 +759,7 @@ int sic_pass(const SicCtx& x, double c, int32_t* codes, int64_t ldq, float* resi
     WSIC_TRY(sic_pass_once(y, c, codes, ldq, resid, ldr));
     WSIC_TRY(read_back(&pc, 1, x.st));
   }
-  if (std::getenv("WSIC_TRACE") && (f[1] || f[2]))
+  if (g_dbg.trace.load() && (f[1] || f[2]))
     std::fprintf(stderr, "wsic sic pass: %d decision(s) re-checked, %d workgroup(s) re-derived\n",
                  f[2], f[1]);
   if (pass_flags) *pass_flags = f[0];
@@ -920,6 +929,63 @@ extern "C" {
 
 int wsic_version(void) { return WSIC_VERSION; }
 
+int wsic_debug_set(int knob, double v) {
+  using wsic::g_dbg;
+  wsic::clear_error();
+  if (!std::isfinite(v)) {
+    wsic::set_error("debug_set: value is not finite");
+    return WSIC_E_INVAL;
+  }
+  const bool on = v != 0.0;
+  switch (knob) {
+    case WSIC_DBG_FP64_PRODUCT: g_dbg.fp64_product = on; return WSIC_OK;
+    case WSIC_DBG_SUPER_BLOCKS: g_dbg.super_blocks = on; return WSIC_OK;
+    case WSIC_DBG_GUARD_SCALE:
+      if (!(v >= 1.0)) {
+        wsic::set_error("debug_set: guard scale %g below 1 would weaken the exact re-check", v);
+        return WSIC_E_INVAL;
+      }
+      g_dbg.guard_scale = v;
+      return WSIC_OK;
+    case WSIC_DBG_CHOL_FUSED: g_dbg.chol_fused = on; return WSIC_OK;
+    case WSIC_DBG_LOGITS_GENERIC: g_dbg.logits_generic = on; return WSIC_OK;
+    case WSIC_DBG_TRACE: g_dbg.trace = on; return WSIC_OK;
+    default:
+      wsic::set_error("debug_set: unknown knob %d", knob);
+      return WSIC_E_INVAL;
+  }
+}
+
+int wsic_debug_get(int knob, double* v) {
+  using wsic::g_dbg;
+  wsic::clear_error();
+  if (!v) {
+    wsic::set_error("debug_get: value pointer is null");
+    return WSIC_E_INVAL;
+  }
+  switch (knob) {
+    case WSIC_DBG_FP64_PRODUCT: *v = g_dbg.fp64_product.load(); return WSIC_OK;
+    case WSIC_DBG_SUPER_BLOCKS: *v = g_dbg.super_blocks.load(); return WSIC_OK;
+    case WSIC_DBG_GUARD_SCALE: *v = g_dbg.guard_scale.load(); return WSIC_OK;
+    case WSIC_DBG_CHOL_FUSED: *v = g_dbg.chol_fused.load(); return WSIC_OK;
+    case WSIC_DBG_LOGITS_GENERIC: *v = g_dbg.logits_generic.load(); return WSIC_OK;
+    case WSIC_DBG_TRACE: *v = g_dbg.trace.load(); return WSIC_OK;
+    default:
+      wsic::set_error("debug_get: unknown knob %d", knob);
+      return WSIC_E_INVAL;
+  }
+}
+
+void wsic_debug_reset(void) {
+  using wsic::g_dbg;
+  g_dbg.fp64_product = false;
+  g_dbg.super_blocks = true;
+  g_dbg.guard_scale = 1.0;
+  g_dbg.chol_fused = true;
+  g_dbg.logits_generic = false;
+  g_dbg.trace = false;
+}
+
 const char* wsic_last_error(void) { return wsic::last_error(); }
 
 const char* wsic_status_str(int s) {
@@ -988,9 +1054,8 @@ int wsic_cholesky(double* A, int64_t n, int64_t lda, int64_t* info, void* ws, si
     slot[1] = cv.take<double>(64 * 64);
     WSIC_TRY(launch_fill_zero(dinfo, FLAGS_BYTES, st));
     constexpr int NBK = 64;
-    // testing hook: WSIC_CHOL_STEP=0 runs update and next panel as separate launches
-    const char* fe = std::getenv("WSIC_CHOL_STEP");
-    const bool fused = !(fe && fe[0] == '0');
+    // diagnostic switch: update and next panel as separate launches
+    const bool fused = g_dbg.chol_fused.load();
     // a panel's diagonal block lands in slot[step & 1] and is moved into A afterwards
     int64_t step = 0;
     WSIC_TRY(launch_potrf_panel(A, lda, 0, (int)std::min<int64_t>(NBK, n), n, dinfo, slot[0], st));
@@ -1097,7 +1162,7 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
     if (o.mode == WSIC_WF_AUTO)
       o.mode = (n_out * n_in < WSIC_WF_AUTO_PARAMS) ? WSIC_WF_BISECT : WSIC_WF_SECANT;
     const bool cols = o.rate_mode == WSIC_RATE_COLUMNS;
-    const bool trace = std::getenv("WSIC_TRACE") != nullptr;
+    const bool trace = g_dbg.trace.load();
     WSIC_TRY(check_ws(lam ? WSIC_OP_SOFTWATER : WSIC_OP_WATERFILL, n_out, n_in, ws, ws_bytes));
     hipStream_t st = (hipStream_t)stream;
     Carve cv(ws);
@@ -1147,8 +1212,11 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
 
     // two code buffers: the caller's and one in the workspace; `hi_buf` holds the codes of
     // the best grid scale so far with H <= R
+    // (the workspace pair is dense, row stride n_in; the caller's rows may be padded)
     int32_t* cbuf[2] = {codes, wf.codes2};
     float* rbuf[2] = {resid, resid ? wf.resid2 : nullptr};
+    const int64_t qld[2] = {ldq, n_in};
+    const int64_t rld[2] = {ldr, n_in};
     int passes = 0;
     int hi_buf = -1;
     double c_hi = 0, h_hi = 0, c_lo = 0, h_lo = 0;
@@ -1160,18 +1228,20 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
         return WSIC_E_NO_BRACKET;
       }
       ++passes;
-      WSIC_TRY(sic_pass_once(x, c, cbuf[buf], ldq, rbuf[buf], ldr));
+      WSIC_TRY(sic_pass_once(x, c, cbuf[buf], qld[buf], rbuf[buf], rld[buf]));
       int f = 0, nfix = 0, nchk = 0;
       auto rate_of = [&](int* fl, int* a1, int* a2) -> int {
         if (cols)
-          return entropy_cols_of(cbuf[buf], n_out, n_in, ldq, wf.col, x.ws.pflags, st, H, fl, a1, a2);
-        return entropy_of(cbuf[buf], n_out, n_in, ldq, wf.hist, x.ws.pflags, st, H, nullptr, fl, a1, a2);
+          return entropy_cols_of(cbuf[buf], n_out, n_in, qld[buf], wf.col, x.ws.pflags, st, H, fl,
+                                 a1, a2);
+        return entropy_of(cbuf[buf], n_out, n_in, qld[buf], wf.hist, x.ws.pflags, st, H, nullptr,
+                          fl, a1, a2);
       };
       WSIC_TRY(rate_of(&f, &nfix, &nchk));
       if (x.i8 && (f & FLAG_OVERFLOW_LIST)) {  // a row listed too many large codes: fp64 pass
         SicCtx y = x;
         y.i8 = false;
-        WSIC_TRY(sic_pass_once(y, c, cbuf[buf], ldq, rbuf[buf], ldr));
+        WSIC_TRY(sic_pass_once(y, c, cbuf[buf], qld[buf], rbuf[buf], rld[buf]));
         WSIC_TRY(rate_of(&f, nullptr, nullptr));
       }
       if (trace)
@@ -1320,10 +1390,10 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
     }
     // the accepted codes must end in the caller's buffers
     if (hi_buf == 1) {
-      WSIC_HIP_TRY(hipMemcpy2DAsync(codes, ldq * sizeof(int32_t), wf.codes2, ldq * sizeof(int32_t),
+      WSIC_HIP_TRY(hipMemcpy2DAsync(codes, ldq * sizeof(int32_t), wf.codes2, n_in * sizeof(int32_t),
                                     n_in * sizeof(int32_t), n_out, hipMemcpyDeviceToDevice, st));
       if (resid)
-        WSIC_HIP_TRY(hipMemcpy2DAsync(resid, ldr * sizeof(float), wf.resid2, ldr * sizeof(float),
+        WSIC_HIP_TRY(hipMemcpy2DAsync(resid, ldr * sizeof(float), wf.resid2, n_in * sizeof(float),
                                       n_in * sizeof(float), n_out, hipMemcpyDeviceToDevice, st));
       WSIC_HIP_TRY(hipStreamSynchronize(st));
     }
@@ -1402,8 +1472,8 @@ int wsic_softmax_curvature(const void* X, int dtype, int64_t rows, int64_t n_in,
     a.rmax = cw.rmax;
     a.rinvz = cw.rinvz;
     a.cpart = cw.cpart;
-    // testing hook: WSIC_LOGITS_GENERIC=1 takes the fp64 VALU logits for bf16 inputs too
-    if (const char* e = std::getenv("WSIC_LOGITS_GENERIC")) a.force_generic = (e[0] == '1');
+    // diagnostic switch: the fp64 VALU logits for bf16 inputs too
+    a.force_generic = g_dbg.logits_generic.load();
     WSIC_TRY(launch_softmax_curvature(a, st));
     WSIC_TRY(read_flags(cw.flags, &f, st));
     return flags_status(f, "softmax_curvature");

@@ -106,7 +106,7 @@ def test_cholesky_reports_pivot(device, n, bad):
     assert ei.value.info == info_or == bad
 
 
-def test_cholesky_more_panel_workgroups_than_fit(device, monkeypatch):
+def test_cholesky_more_panel_workgroups_than_fit(device):
     """n = 20480: a step's panel has 320 workgroups, more than one launch keeps resident, so
     late panel workgroups start after workgroup 0 has finished. The factor must equal the one
     from separate update and panel launches bit for bit and reproduce Sigma on sampled entries
@@ -119,8 +119,8 @@ def test_cholesky_more_panel_workgroups_than_fit(device, monkeypatch):
     del R
     sig.diagonal().add_(1.0)
     U, _ = lib.cholesky(sig.clone())
-    monkeypatch.setenv("WSIC_CHOL_STEP", "0")
-    U_sep, _ = lib.cholesky(sig.clone())
+    with lib.debug(chol_fused=0):
+        U_sep, _ = lib.cholesky(sig.clone())
     assert torch.equal(U, U_sep)
     rng = np.random.default_rng(6)
     I = torch.from_numpy(rng.integers(0, n, 4096)).to(device)
@@ -179,6 +179,35 @@ def test_sic_strided_inputs(device):
     sic = oracle.sic_quantize(layer.w, L, c)
     assert_codes_parity(codes_big[:, :n_in].cpu().numpy(), sic, label="strided")
     assert torch.all(codes_big[:, n_in:] == -99)
+
+
+@pytest.mark.parametrize("which", ["waterfill", "softwater"])
+@pytest.mark.parametrize("mode", ["bisect", "secant"])
+def test_waterfill_padded_outputs(device, which, mode):
+    """Codes and residuals written through row-padded views (ld > n_in): the search must give
+    the same c, rate, codes and residuals as with dense outputs, and never write the padding
+    (regression: the workspace's second code/residual buffer once took the caller's stride)."""
+    layer = _layer("blockar1_77x520")
+    L, U = _oracle_factor_on_device(layer)
+    n_out, n_in = layer.n_out, layer.n_in
+    Wt = w_tensor(layer)
+    pad = 37
+    codes_big = torch.full((n_out, n_in + pad), -99, dtype=torch.int32, device=device)
+    resid_big = torch.full((n_out, n_in + pad), 1234.5, dtype=torch.float32, device=device)
+    say(f"[waterfill-padded] {which} {mode} {n_out}x{n_in} ld={n_in + pad}")
+    if which == "waterfill":
+        run = lambda **kw: lib.waterfill(Wt, U, 2.0, mode=mode, **kw)
+    else:
+        lam = torch.from_numpy(np.linspace(0.05, 0.25, n_out)).to(device)
+        run = lambda **kw: lib.softwater_waterfill(Wt, U, lam, 2.0, mode=mode, **kw)
+    dense = run()
+    padded = run(codes=codes_big[:, :n_in], resid=resid_big[:, :n_in])
+    say(f"  dense c={dense['c']!r} passes={dense['passes']}; padded c={padded['c']!r} passes={padded['passes']}")
+    assert padded["c"] == dense["c"] and padded["rate"] == dense["rate"]
+    assert torch.equal(codes_big[:, :n_in], dense["codes"])
+    assert torch.equal(resid_big[:, :n_in], dense["resid"])
+    assert torch.all(codes_big[:, n_in:] == -99)
+    assert torch.all(resid_big[:, n_in:] == 1234.5)
 
 
 @pytest.mark.parametrize("name", ["spiked_200x272", "blockar1_77x520"])
@@ -340,20 +369,19 @@ def test_bad_factor_diagonal_is_reported(device):
 
 
 # ------------------------------------------------------------------ interference product variants
-@pytest.mark.parametrize("env", [{"WSIC_FP64_TRAIL": "1"}, {"WSIC_GUARD_SCALE": "1e300"},
-                                 {"WSIC_GUARD_SCALE": "3e4"}, {"WSIC_SUPER_BLOCKS": "0"},
-                                 {"WSIC_SUPER_BLOCKS": "0", "WSIC_GUARD_SCALE": "3e4"}])
+@pytest.mark.parametrize("env", [{"fp64_product": 1}, {"guard_scale": 1e300},
+                                 {"guard_scale": 3e4}, {"super_blocks": 0},
+                                 {"super_blocks": 0, "guard_scale": 3e4}])
 @pytest.mark.parametrize("name", ["spiked_300x333", "blockar1_77x520"])
-def test_sic_parity_product_variants(device, monkeypatch, env, name):
+def test_sic_parity_product_variants(device, env, name):
     """fp64 MFMA interference, and the int8 product with every decision re-derived exactly in
     fp64 (error bound forced huge): both must give the oracle's codes."""
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
     layer = _layer(name)
     L, U = _oracle_factor_on_device(layer)
     c = oracle.initial_scale(layer.w, L, 2.5)
     say(f"[sic-variant] {name} {env}")
-    codes, resid = lib.sic_quantize(w_tensor(layer), U, c, want_resid=True)
+    with lib.debug(**env):
+        codes, resid = lib.sic_quantize(w_tensor(layer), U, c, want_resid=True)
     sic = oracle.sic_quantize(layer.w, L, c)
     assert_codes_parity(codes.cpu().numpy(), sic, label=f"{name} {env}")
 

@@ -53,16 +53,14 @@ def _curv_tol(layer, x_chunks64, fp32_sums):
 
 @pytest.mark.parametrize("name", list(HEADS))
 @pytest.mark.parametrize("eps", [0.0, 0.05])
-def test_curvature_parity(device, name, eps, monkeypatch):
+def test_curvature_parity(device, name, eps):
     layer = _head(name)
     xs = [np.asarray(c, dtype=np.float64) for c in layer.x_chunks]
     ref = sw.softmax_curvature(xs, layer.w, eps)
     mfma = layer.dtype == "bf16"
     for generic in ([False, True] if mfma else [False]):
-        if generic:
-            monkeypatch.setenv("WSIC_LOGITS_GENERIC", "1")
-        lam = lib.softmax_curvature_chunks(x_tensors(layer), w_tensor(layer), eps).cpu().numpy()
-        monkeypatch.delenv("WSIC_LOGITS_GENERIC", raising=False)
+        with lib.debug(logits_generic=1 if generic else 0):
+            lam = lib.softmax_curvature_chunks(x_tensors(layer), w_tensor(layer), eps).cpu().numpy()
         tol = _curv_tol(layer, xs, mfma and not generic)
         rel = np.abs(lam / ref - 1.0)
         say(f"[curvature] {name} eps={eps} generic={generic}: max rel {rel.max():.3e} (tol {tol:.3e})")

@@ -111,3 +111,22 @@ def test_product_path_has_no_oracle_dependency():
             "try:\n    L.lib()\nexcept ImportError as e:\n    print('refused')\n")
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert "refused" in out.stdout, out.stderr
+
+
+def test_debug_switches_are_explicit_and_bounded():
+    """Alternative kernel paths are chosen only through wsic_debug_set (no environment
+    variable), and no value may weaken the int8 product's exact re-check."""
+    W.debug_reset()
+    assert W.debug_get("guard_scale") == 1.0
+    assert W.debug_get("super_blocks") == 1.0 and W.debug_get("fp64_product") == 0.0
+    for bad in (0.5, 0.0, -3.0, float("nan"), float("inf")):
+        with pytest.raises(W.WsicError) as ei:
+            W.debug_set("guard_scale", bad)
+        assert ei.value.status == W.E_INVAL
+        assert W.debug_get("guard_scale") == 1.0
+    with W.debug(guard_scale=3e4, super_blocks=0):
+        assert W.debug_get("guard_scale") == 3e4 and W.debug_get("super_blocks") == 0.0
+    assert W.debug_get("guard_scale") == 1.0 and W.debug_get("super_blocks") == 1.0
+    assert W.lib().wsic_debug_set(99, 1.0) == W.E_INVAL
+    src = open(os.path.join(ROOT, "rate_allocated_weight_amd", "csrc", "wsic_api.hip")).read()
+    assert "getenv" not in src
