@@ -45,8 +45,11 @@ __all__ = [
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bit patterns."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = a.view(np.uint32)
+    if not np.all(np.isfinite(a)):
+        raise ValueError("bf16 rounding of non-finite values is not supported")
+    # finite values: u + 0x8000 stays below 2^32, so 32-bit arithmetic is exact
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return rounded.astype(np.uint16)
 
 
@@ -104,19 +107,24 @@ def _student_t(rng: np.random.Generator, nu: float, shape, std: float) -> np.nda
 def _ar1_rows(rng: np.random.Generator, rows: int, n: int, rho: float, block: int = 0) -> np.ndarray:
     """AR(1) along the feature axis; restarted every ``block`` features when block > 0."""
     z = rng.standard_normal((rows, n))
-    x = np.empty_like(z)
     a = math.sqrt(1.0 - rho * rho)
     if block <= 0:
         block = n
-    starts = np.arange(0, n, block)
-    for off in range(block):
-        cols = starts + off
-        cols = cols[cols < n]
-        if off == 0:
-            x[:, cols] = z[:, cols]
-        else:
-            x[:, cols] = rho * x[:, cols - 1] + a * z[:, cols]
-    return x
+    nblk = -(-n // block)
+    # features laid out (offset in block, row, block) so that each step of the recursion is one
+    # contiguous slab; a ragged last block is padded and cut off again (padding never feeds a
+    # kept feature: the recursion runs along the offset only)
+    zp = np.zeros((rows, nblk * block))
+    zp[:, :n] = z
+    zt = np.ascontiguousarray(zp.reshape(rows, nblk, block).transpose(2, 0, 1))
+    del zp
+    xt = np.empty_like(zt)
+    xt[0] = zt[0]
+    for off in range(1, block):
+        xt[off] = rho * xt[off - 1] + a * zt[off]
+    del zt
+    x = np.ascontiguousarray(xt.transpose(1, 2, 0)).reshape(rows, nblk * block)
+    return x[:, :n] if nblk * block != n else x
 
 
 def _spiked_factors(rng: np.random.Generator, n_in: int, rank: int):
