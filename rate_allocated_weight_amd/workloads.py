@@ -105,26 +105,25 @@ def _student_t(rng: np.random.Generator, nu: float, shape, std: float) -> np.nda
 
 
 def _ar1_rows(rng: np.random.Generator, rows: int, n: int, rho: float, block: int = 0) -> np.ndarray:
-    """AR(1) along the feature axis; restarted every ``block`` features when block > 0."""
+    """AR(1) along the feature axis; restarted every ``block`` features when block > 0.
+
+    x_0 = z_0, x_i = rho x_{i-1} + a z_i (a = sqrt(1 - rho^2)), evaluated in that order by a
+    first-order recursive filter (scipy's lfilter: per element the products a z_i and
+    rho x_{i-1} and their sum, as written)."""
+    from scipy.signal import lfilter
+
     z = rng.standard_normal((rows, n))
     a = math.sqrt(1.0 - rho * rho)
     if block <= 0:
         block = n
-    nblk = -(-n // block)
-    # features laid out (offset in block, row, block) so that each step of the recursion is one
-    # contiguous slab; a ragged last block is padded and cut off again (padding never feeds a
-    # kept feature: the recursion runs along the offset only)
-    zp = np.zeros((rows, nblk * block))
-    zp[:, :n] = z
-    zt = np.ascontiguousarray(zp.reshape(rows, nblk, block).transpose(2, 0, 1))
-    del zp
-    xt = np.empty_like(zt)
-    xt[0] = zt[0]
-    for off in range(1, block):
-        xt[off] = rho * xt[off - 1] + a * zt[off]
-    del zt
-    x = np.ascontiguousarray(xt.transpose(1, 2, 0)).reshape(rows, nblk * block)
-    return x[:, :n] if nblk * block != n else x
+    x = np.empty_like(z)
+    for s0 in range(0, n, block):
+        s1 = min(n, s0 + block)
+        x[:, s0] = z[:, s0]
+        if s1 - s0 > 1:
+            x[:, s0 + 1:s1] = lfilter([a], [1.0, -rho], z[:, s0 + 1:s1], axis=-1,
+                                      zi=rho * z[:, s0:s0 + 1])[0]
+    return x
 
 
 def _spiked_factors(rng: np.random.Generator, n_in: int, rank: int):
