@@ -53,6 +53,19 @@ FAMILIES = {
 }
 
 
+# algorithmic work per launch, as the library counts it for each family
+WORK_UNITS = {
+    "sic_leaf": "bytes: weights in (2 B bf16 / 4 B f32) + int32 codes out, per weight of the launch's "
+                "columns; the design's intermediates (Y, G, residuals, int8 codes) are not counted",
+    "hist": "bytes: 4 per int32 code read",
+    "dist_resid": "bytes: 4 per fp32 residual read",
+    "gemm_trail_i8": "int8 ops: 2 M N K per digit plane, 5 planes",
+    "gemm_y": "fp64 flops: n_out n_in (n_in + 1) (triangular U)",
+    "syrk_bf16": "flops: N n_in (n_in + 1) (upper triangle)",
+    "chol_step": "fp64 flops of the step's update and panel",
+}
+
+
 def measured_traffic(family: str, workload: str):
     """HBM bytes per launch of `family` from the committed counter summary (rocprofv3
     FETCH_SIZE + WRITE_SIZE scaled by a plain copy), or None when there is none for this
@@ -93,6 +106,10 @@ def parse():
                     help="codes per rANS stream for the entropy-coder measurement (0: skip it)")
     ap.add_argument("--smoothing", type=float, default=0.05,
                     help="weight of the uniform distribution mixed into the calibration softmax")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration records (every workload and target)")
+    ap.add_argument("--configs-budget-s", type=float, default=360.0,
+                    help="wall-clock budget of the whole run after which remaining configurations are skipped")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run one device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -112,43 +129,53 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n}), flush=True)
 
 
+def _blas_threads():
+    """Threads the host BLAS actually runs with (what the oracle's numpy calls use)."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [d.get("num_threads") for d in threadpool_info() if d.get("user_api") == "blas"]
+        return int(max(n)) if n else 1
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(layer, target, sample_rows):
-    """The oracle as it stands, on the host: full covariance and factorization of the layer's
-    calibration data, and the waterfill search on `sample_rows` rows of W; the per-row part is
-    scaled to all rows."""
+    """The oracle as it stands, on the host's cores: full covariance and factorization of the
+    layer's calibration data, one full SIC pass over every row of W at the oracle's own grid
+    scale (its high-rate start), and the pass count of the oracle's search (bracketing +
+    geometric bisection) taken from its run on `sample_rows` rows. The whole-layer time is
+    covariance + Cholesky + passes x one full pass."""
     import numpy as np
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    cores = min(16, len(os.sched_getaffinity(0)))
-    ctx = threadpool_limits(cores) if threadpool_limits else None
-    try:
-        t0 = time.perf_counter()
-        sigma = oracle.covariance(layer.x_chunks)
-        t1 = time.perf_counter()
-        L, info = oracle.cholesky_lower(sigma)
-        t2 = time.perf_counter()
-        rows = np.linspace(0, layer.n_out - 1, sample_rows).astype(np.int64)
-        wf = oracle.waterfill(layer.w[rows], L, target)
-        t3 = time.perf_counter()
-    finally:
-        if ctx is not None:
-            ctx.unregister() if hasattr(ctx, "unregister") else None
-    t_cov, t_chol, t_wf = t1 - t0, t2 - t1, t3 - t2
-    t_full = t_cov + t_chol + t_wf * (layer.n_out / sample_rows)
+    affinity = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    sigma = oracle.covariance(layer.x_chunks)
+    t1 = time.perf_counter()
+    L, info = oracle.cholesky_lower(sigma)
+    t2 = time.perf_counter()
+    c0 = oracle.initial_scale(layer.w, L, target)
+    oracle.sic_quantize(layer.w, L, c0)
+    t3 = time.perf_counter()
+    rows = np.linspace(0, layer.n_out - 1, sample_rows).astype(np.int64)
+    wf = oracle.waterfill(layer.w[rows], L, target)
+    t4 = time.perf_counter()
+    passes = len(wf["trace"])
+    t_cov, t_chol, t_pass = t1 - t0, t2 - t1, t3 - t2
+    t_full = t_cov + t_chol + passes * t_pass
     return {
         "value": layer.n_out * layer.n_in / t_full / 1e9,
         "unit": "Gparams/s",
-        "cores": cores,
+        "cores": _blas_threads(),
         "kind": "oracle",
-        "sample": (f"full covariance ({t_cov:.2f} s) and Cholesky ({t_chol:.2f} s) of {layer.n_rows}x{layer.n_in}; "
-                   f"waterfill on {sample_rows} of {layer.n_out} rows ({t_wf:.2f} s, {len(wf['trace'])} passes), "
-                   f"scaled by {layer.n_out / sample_rows:.0f} to the whole layer"),
-        "seconds": round(t_cov + t_chol + t_wf, 2),
+        "sample": (f"measured: covariance ({t_cov:.2f} s) and Cholesky ({t_chol:.2f} s) of {layer.n_rows}x{layer.n_in}, "
+                   f"one SIC pass over all {layer.n_out} rows ({t_pass:.2f} s); the oracle's search needs {passes} "
+                   f"passes (its run on {sample_rows} rows, {t4 - t3:.2f} s), so the whole layer is "
+                   f"{t_cov:.2f} + {t_chol:.2f} + {passes} x {t_pass:.2f} = {t_full:.1f} s"),
+        "seconds": round(t4 - t0, 2),
+        "affinity_cores": affinity,
     }
 
 
@@ -165,8 +192,8 @@ def cpu_baseline_softwater(layer, target, sample_rows, smoothing, curv_rows=64):
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
-    cores = min(16, len(os.sched_getaffinity(0)))
-    ctx = threadpool_limits(cores) if threadpool_limits else None
+    cores = _blas_threads()
+    ctx = None
     try:
         t0 = time.perf_counter()
         sigma = ws.covariance(layer.x_chunks)
@@ -197,7 +224,138 @@ def cpu_baseline_softwater(layer, target, sample_rows, smoothing, curv_rows=64):
     }
 
 
+# Per-configuration records of the default run: every named workload and target, the LM head
+# also with SoftWater grids, and the large down-projection also with dead-feature removal and the
+# LMMSE rescale. (workload, target, variant)
+CONFIG_CASES = [
+    ("ar1_256", 2.0, None),
+    ("attn_4096", 1.0, None),
+    ("attn_4096", 3.0, None),
+    ("attn_4096", 4.0, None),
+    ("mlp_up_11008x4096", 2.0, None),
+    ("lmhead_32000x4096", 1.5, None),
+    ("lmhead_32000x4096", 3.0, None),
+    ("lmhead_32000x4096", 1.5, "softwater"),
+    ("mlp_down_8192x28672", 2.0, None),
+    ("mlp_down_8192x28672", 2.0, "dead_features+lmmse"),
+]
+
+
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2] if len(xs) % 2 else 0.5 * (xs[len(xs) // 2 - 1] + xs[len(xs) // 2])
+
+
+def run_case(L, torch, layer, W, X, target, variant, reps, smoothing=0.05, tau=1e-6):
+    """One configuration, timed like the headline step (inputs in HBM; covariance -> Cholesky ->
+    waterfill -> entropy -> distortion), `reps` timed steps after one warm-up; returns the
+    median step time, the part from U on, passes and results."""
+    dev = W.device
+    n_out, n_in, n_rows = layer.n_out, layer.n_in, layer.n_rows
+    sigma = torch.empty((n_in, n_in), dtype=torch.float64, device=dev)
+    sw = variant == "softwater"
+    fix = variant == "dead_features+lmmse"
+    ws_cov = L.workspace(L.OP_COVARIANCE, 1, n_in, dev)
+    ws_ent = L.workspace(L.OP_ENTROPY, n_out, n_in, dev)
+    lam = torch.empty(n_out, dtype=torch.float64, device=dev) if sw else None
+    ws_curv = L.workspace(L.OP_CURVATURE, max(int(c.shape[0]) for c in X), n_out, dev) if sw else None
+    extra = {}
+
+    def step(ev):
+        ev[0].record()
+        for i, c in enumerate(X):
+            L.covariance(c, sigma, alpha=1.0 / n_rows, beta=0.0 if i == 0 else 1.0, ws=ws_cov)
+        if fix:
+            # dead features: columns with Sigma_ii <= tau max Sigma_jj are taken out before the
+            # factorization and get code 0
+            idx, pos, n_live = L.live_features(sigma, tau)
+            Wq, Sq = L.gather_features(W, idx, n_live, sigma)
+        else:
+            Wq, Sq, n_live = W, sigma, n_in
+        U, _ = L.cholesky(Sq)
+        if sw:
+            for i, c in enumerate(X):
+                L.softmax_curvature(c, W, smoothing, lam, alpha=1.0 / n_rows, beta=0.0 if i == 0 else 1.0,
+                                    ws=ws_curv)
+        ev[1].record()
+        if sw:
+            wf = L.softwater_waterfill(Wq, U, lam, target)
+            h, _ = L.entropy(wf["codes"], ws=ws_ent)
+            D, _ = L.softwater_distortion(wf["codes"], U, wf["c"], lam, wf["resid"])
+        else:
+            wf = L.waterfill(Wq, U, target)
+            h, _ = L.entropy(wf["codes"], ws=ws_ent)
+            D, _ = L.distortion(Wq, wf["codes"], U, wf["c"], resid=wf["resid"])
+        if fix:
+            q_full = L.scatter_codes(wf["codes"], pos, n_in)
+            gamma, d_before, d_after = L.lmmse_scale(Wq, U, wf["resid"])
+            extra.update(n_live=n_live, n_dead=n_in - n_live, tau=tau, D_before_lmmse=d_before,
+                         D_after_lmmse=d_after, gamma_min=float(gamma.min()), gamma_max=float(gamma.max()))
+            del q_full
+        ev[2].record()
+        return wf, h, D
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    step(ev)  # warm-up
+    torch.cuda.synchronize()
+    times, from_u = [], []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        wf, h, D = step(ev)
+        torch.cuda.synchronize()
+        times.append(1e3 * (time.perf_counter() - t0))
+        from_u.append(ev[1].elapsed_time(ev[2]))
+    ms, ms_u = _median(times), _median(from_u)
+    rec = {"workload": layer.name, "target_bits": target, "variant": variant, "n_out": n_out, "n_in": n_in,
+           "calib_rows": n_rows, "reps": reps, "ms_per_step": round(ms, 3),
+           "ms_steps": [round(t, 3) for t in times], "gparams_s": round(n_out * n_in / (ms * 1e-3) / 1e9, 4),
+           "ms_from_U": round(ms_u, 3), "gparams_s_from_U": round(n_out * n_in / (ms_u * 1e-3) / 1e9, 4),
+           "passes": wf["passes"], "c": wf["c"], "rate": wf["rate"], "entropy": h, "D": D}
+    rec.update(extra)
+    return rec
+
+
+def config_records(args, L, torch, headline_layer, headline_W, headline_X, t_start, budget_s):
+    """Every case of CONFIG_CASES except the headline one, within a wall-clock budget."""
+    from rate_allocated_weight_amd import workloads
+
+    dev = torch.device("cuda:0")
+    out = []
+    cur = (None, None, None, None)
+    for name, target, variant in CONFIG_CASES:
+        if name == args.workload and target == args.target and variant is None:
+            continue
+        if time.perf_counter() - t_start > budget_s:
+            out.append({"workload": name, "target_bits": target, "variant": variant,
+                        "skipped": f"wall-clock budget of {budget_s:.0f} s reached"})
+            continue
+        try:
+            if cur[0] != name:
+                cur = (None, None, None, None)
+                torch.cuda.empty_cache()
+                if name == headline_layer.name:
+                    cur = (name, headline_layer, headline_W, headline_X)
+                else:
+                    print(f"[bench] generating {name}", file=sys.stderr, flush=True)
+                    lay = workloads.named_workload(name)
+                    if lay.dtype == "bf16":
+                        Wd = L.bf16_from_bits(lay.w_bits, dev)
+                        Xd = [L.bf16_from_bits(b, dev) for b in lay.x_bits_chunks]
+                    else:
+                        Wd = torch.from_numpy(lay.w).to(dev)
+                        Xd = [torch.from_numpy(c).to(dev) for c in lay.x_chunks]
+                    cur = (name, lay, Wd, Xd)
+            reps = 2 if cur[1].n_in > 8192 else 3
+            print(f"[bench] case {name} R={target} {variant or ''}", file=sys.stderr, flush=True)
+            out.append(run_case(L, torch, cur[1], cur[2], cur[3], target, variant, reps,
+                                smoothing=args.smoothing))
+        except Exception as e:  # a failing case is reported, it does not take the line down
+            out.append({"workload": name, "target_bits": target, "variant": variant, "error": str(e)})
+    return out
+
+
 def main():
+    t_start = time.perf_counter()
     args = parse()
     if args.copy_calibration_mib > 0:
         copy_calibration(args.copy_calibration_mib)
@@ -316,15 +474,18 @@ def main():
                               "frac": round(ach / peak, 4)}
     trailing = None
     if "gemm_trail_i8" in families:
-        # the int8 limb product of the interference (trailing update) measured as the algorithmic
-        # product it replaces: 2 M N K flops, i.e. its int8 ops over the 5 digit planes
+        # the interference (trailing update) runs as an exact int8 digit-plane product: its own
+        # rate is against the int8 peak; beside it, how long the algorithmic product (2 M N K
+        # flops, one fifth of its int8 ops) would take at the fp32 MFMA peak, over its time
         f = families["gemm_trail_i8"]
         tf = f["achieved"] / 5.0
-        trailing = {"kernel": "gemm_trail_i8", "algorithmic_tflops": round(tf, 2),
-                    "peak_fp32_mfma_tflops": PEAKS["mfma_f32"][0],
-                    "frac_of_fp32_mfma_peak": round(tf / PEAKS["mfma_f32"][0], 4),
-                    "note": "GEMM part only (above the 512-column super-blocks); the product inside "
-                            "the super-block launches is counted with sic_leaf"}
+        trailing = {"kernel": "gemm_trail_i8", "achieved_int8_tops": f["achieved"],
+                    "peak_int8_tops": PEAKS["mfma_i8"][0], "frac_of_int8_peak": f["frac"],
+                    "algorithmic_tflops": round(tf, 2),
+                    "fp32_peak_time_over_measured": round(tf / PEAKS["mfma_f32"][0], 4),
+                    "note": "GEMM part only (above the 512-column super-blocks; the product inside the "
+                            "super-block launches is part of sic_leaf). fp32_peak_time_over_measured > 1: "
+                            "the product finishes faster than an fp32 GEMM at peak could"}
 
     if not args.no_profile:
         L.profile_enable(False)
@@ -422,6 +583,9 @@ def main():
                         "traffic": round(traffic) if traffic is not None else None,
                         "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                         "work_per_launch": v["work"] / max(1, v["launches"]),
+                        "work_unit": WORK_UNITS.get(dom, ""),
+                        "traffic_over_algorithmic": (round(traffic / (v["work"] / max(1, v["launches"])), 3)
+                                                     if traffic is not None and bound == "hbm" else None),
                         "avg_launch_us": v["avg_us"], "launches": v["launches"],
                         "share_of_step": round(v["ms"] / (elapsed * 1e3), 4)}
 
@@ -462,6 +626,9 @@ def main():
     if it_gap is not None:
         out["it_gap"] = it_gap
         out["config"]["rate_mode"] = "columns"
+    if not args.no_configs and not sw and args.rate_mode == "pooled":
+        del codes, resid, ws_wf, ws_ent, ws_dist
+        out["configs"] = config_records(args, L, torch, layer, W, X, t_start, args.configs_budget_s)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = (cpu_baseline_softwater(layer, args.target, args.cpu_sample_rows, args.smoothing)

@@ -181,6 +181,7 @@ struct LeafArgs {
   const double* escale;   // 2^(e_j - P)
   int64_t kf0;
   int kf;
+  int w_bytes;  // bytes per weight of the layer (2 bf16, 4 f32): the algorithmic byte count
 };
 int launch_sic_leaf(const LeafArgs& p, bool i8, hipStream_t st);
 // int8 mode: up to 4 blocks [j0, j0 + w) in one launch (w <= 512), interference of the range's

@@ -1026,9 +1026,9 @@ int launch_sic_leaf(const LeafArgs& a, bool i8, hipStream_t st) {
   p.Bpk = a.Bpk + (a.j0 / BW) * PACK;
   p.invc = 1.0 / a.c;
   const unsigned blocks = (unsigned)((a.n_out + 15) / 16);
-  // bytes that must stream: Y (+G) in, codes (+resid, +int8 codes) out
-  const double work = (double)a.n_out * a.w *
-                      (8.0 + (a.G ? 8.0 : 0.0) + 4.0 + (a.resid ? 4.0 : 0.0) + (i8 ? 1.0 : 0.0));
+  // algorithmic bytes of the method's step: the weights in, the int32 codes out (the design's
+  // intermediates -- Y, G, residuals, int8 codes -- are not counted)
+  const double work = (double)a.n_out * a.w * (a.w_bytes + 4.0);
 #define WSIC_LEAF(HG, HR, I8, FU)                                                                  \
   WSIC_LAUNCH("sic_leaf", work, st, (k_sic_leaf<HG, HR, I8, FU>), dim3(blocks), dim3(256), 0, p)
   const bool hg = a.G != nullptr, hr = a.resid != nullptr, fu = a.kf > 0;
@@ -1061,8 +1061,7 @@ int launch_sic_super(const LeafArgs& a, hipStream_t st) {
   LeafArgs p = a;
   p.invc = 1.0 / a.c;
   const unsigned blocks = (unsigned)((a.n_out + 15) / 16);
-  const double work = (double)a.n_out * a.w *
-                      (8.0 + (a.G ? 8.0 : 0.0) + 4.0 + (a.resid ? 4.0 : 0.0) + 1.0);
+  const double work = (double)a.n_out * a.w * (a.w_bytes + 4.0);  // as in launch_sic_leaf
   const bool hg = a.G != nullptr, hr = a.resid != nullptr;
   if (hg && hr)
     WSIC_LAUNCH("sic_leaf", work, st, (k_sic_super<true, true>), dim3(blocks), dim3(256), 0, p);

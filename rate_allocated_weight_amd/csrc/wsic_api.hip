@@ -596,14 +596,14 @@ int sic_setup(const SicCtx& x, bool read_now = true) {
 // by one leaf launch each when super_launch is off).
 constexpr int64_t SUPER = 4;
 
-int sic_leaf_at(const SicCtx& x, int64_t j0, int64_t wb, int64_t hi, double c, int32_t* codes,
-                int64_t ldq, float* resid, int64_t ldr, bool fuse) {
-  const bool has_g = hi < x.n_in;
+// the leaf / super-block arguments shared by every launch of a pass over columns [j0, j0 + w)
+LeafArgs leaf_args(const SicCtx& x, int64_t j0, int64_t w, bool has_g, double c, int32_t* codes,
+                   int64_t ldq, float* resid, int64_t ldr) {
   LeafArgs a{};
   a.n_out = x.n_out;
   a.n_in = x.n_in;
   a.j0 = j0;
-  a.w = (int)wb;
+  a.w = (int)w;
   a.Y = x.ws.Y;
   a.ldy = x.n_in;
   a.G = has_g ? x.ws.G : nullptr;
@@ -625,6 +625,13 @@ int sic_leaf_at(const SicCtx& x, int64_t j0, int64_t wb, int64_t hi, double c, i
   a.absq = x.ws.absq;
   a.ocnt = x.ws.ocnt;
   a.olist = x.ws.olist;
+  a.w_bytes = x.dtype == WSIC_BF16 ? 2 : 4;
+  return a;
+}
+
+int sic_leaf_at(const SicCtx& x, int64_t j0, int64_t wb, int64_t hi, double c, int32_t* codes,
+                int64_t ldq, float* resid, int64_t ldr, bool fuse) {
+  LeafArgs a = leaf_args(x, j0, wb, hi < x.n_in, c, codes, ldq, resid, ldr);
   if (fuse && j0 + BW < hi) {
     a.D = x.ws.D;
     a.ldd = ld_i8(x.n_in);
@@ -641,32 +648,7 @@ int sic_range(const SicCtx& x, int64_t lo, int64_t hi, double c, int32_t* codes,
   const int64_t w = hi - lo;
   const bool has_g = hi < x.n_in;
   if (x.i8 && w <= SUPER * BW && x.super_launch) {
-    LeafArgs a{};
-    a.n_out = x.n_out;
-    a.n_in = x.n_in;
-    a.j0 = lo;
-    a.w = (int)w;
-    a.Y = x.ws.Y;
-    a.ldy = x.n_in;
-    a.G = has_g ? x.ws.G : nullptr;
-    a.ldg = x.n_in;
-    a.Bpk = x.ws.Bpk;
-    a.invd = x.ws.invd;
-    a.c = c;
-    a.codes = codes;
-    a.ldq = ldq;
-    a.resid = resid;
-    a.ldr = ldr;
-    a.flags = x.ws.pflags;
-    a.U = x.U;
-    a.ldu = x.ldu;
-    a.bscale = x.ws.bscale;
-    a.guard_scale = x.guard_scale;
-    a.q8 = x.ws.q8;
-    a.ldq8 = ld_i8(x.n_in);
-    a.absq = x.ws.absq;
-    a.ocnt = x.ws.ocnt;
-    a.olist = x.ws.olist;
+    LeafArgs a = leaf_args(x, lo, w, has_g, c, codes, ldq, resid, ldr);
     a.D = x.ws.D;
     a.ldd = ld_i8(x.n_in);
     a.plane = x.n_in * a.ldd;
@@ -682,35 +664,7 @@ int sic_range(const SicCtx& x, int64_t lo, int64_t hi, double c, int32_t* codes,
     }
     return WSIC_OK;
   }
-  if (w <= BW) {
-    LeafArgs a{};
-    a.n_out = x.n_out;
-    a.n_in = x.n_in;
-    a.j0 = lo;
-    a.w = (int)w;
-    a.Y = x.ws.Y;
-    a.ldy = x.n_in;
-    a.G = has_g ? x.ws.G : nullptr;
-    a.ldg = x.n_in;
-    a.Bpk = x.ws.Bpk;
-    a.invd = x.ws.invd;
-    a.c = c;
-    a.codes = codes;
-    a.ldq = ldq;
-    a.resid = resid;
-    a.ldr = ldr;
-    a.flags = x.ws.pflags;
-    a.U = x.U;
-    a.ldu = x.ldu;
-    a.bscale = x.ws.bscale;
-    a.guard_scale = x.guard_scale;
-    a.q8 = x.ws.q8;
-    a.ldq8 = ld_i8(x.n_in);
-    a.absq = x.ws.absq;
-    a.ocnt = x.ws.ocnt;
-    a.olist = x.ws.olist;
-    return launch_sic_leaf(a, x.i8, x.st);
-  }
+  if (w <= BW) return launch_sic_leaf(leaf_args(x, lo, w, has_g, c, codes, ldq, resid, ldr), x.i8, x.st);
   const int64_t nblk = (w + BW - 1) / BW;
   const int64_t mid = lo + BW * ((nblk + 1) / 2);
   WSIC_TRY(sic_range(x, mid, hi, c, codes, ldq, resid, ldr));
