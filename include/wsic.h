@@ -350,6 +350,25 @@ int wsic_softwater_distortion(const int32_t* codes, int64_t n_out, int64_t n_in,
                               void* stream);
 
 /*
+ * Layer distortion with no allocation of any kind, for callers that cannot allocate device or
+ * pinned host memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments and results as wsic_distortion, without the workspace: the scratch
+ * is a static device buffer of WSIC_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends,
+ * and *D_out is read back by a plain copy into the caller's host memory.
+ * The device is the one current on the calling thread; stream must belong to it.
+ * Returns WSIC_E_WORKSPACE when the layer needs more scratch than the buffer holds
+ * (wsic_workspace_bytes(WSIC_OP_DISTORTION, n_out, n_in) > WSIC_NOALLOC_SCRATCH_BYTES, about
+ * 16 n_in + 8 ceil(n_out / 64) ceil(n_in / 64) bytes; 8192 x 28672 and 32000 x 4096 fit).
+ * All calls on one GPU share its buffer: calls that overlap in time on one GPU (different
+ * streams or threads) race and give undefined results; run them one after another.
+ */
+#define WSIC_NOALLOC_SCRATCH_BYTES (1u << 20)
+int wsic_distortion_noalloc(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                            const int32_t* codes, int64_t ldq, const double* U, int64_t ldu,
+                            double c, const float* resid, int64_t ldr, int mode, double* D_out,
+                            void* W_hat, int w_hat_dtype, int64_t ldh, void* stream);
+
+/*
  * Diagnostic switches (process-wide, default off). They select alternative kernel paths that
  * compute the same results, so that tests can compare the paths with each other and with the
  * reference; nothing in normal use needs them. Set them only while no other library call runs.

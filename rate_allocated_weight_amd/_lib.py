@@ -85,6 +85,8 @@ _SIGS = {
     "wsic_rans_encode": (ctypes.c_int, [_p, _i64, ctypes.c_int32, _p, _sz, ctypes.POINTER(_sz), _p, _sz, _p]),
     "wsic_rans_decode": (ctypes.c_int, [_p, _sz, _p, _i64, _p, _sz, _p]),
     "wsic_rans_decode_dequant": (ctypes.c_int, [_p, _sz, _i64, _i64, _p, _i64, _d, _p, ctypes.c_int, _p, _sz, _p]),
+    "wsic_distortion_noalloc": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, _i64, _d, _p,
+                                               _i64, ctypes.c_int, ctypes.POINTER(_d), _p, ctypes.c_int, _i64, _p]),
     "wsic_debug_set": (ctypes.c_int, [ctypes.c_int, _d]),
     "wsic_debug_get": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(_d)]),
     "wsic_debug_reset": (None, []),
@@ -415,6 +417,24 @@ def distortion(W: torch.Tensor, codes: torch.Tensor, U: torch.Tensor, c: float,
         ctypes.byref(d), _p(w_hat.data_ptr() if w_hat is not None else 0), wdt,
         _rowmajor(w_hat) if w_hat is not None else n_in, *_ws_args(ws), _stream(W)))
     return d.value, w_hat
+
+
+def distortion_noalloc(W: torch.Tensor, codes: torch.Tensor, U: torch.Tensor, c: float,
+                       resid: Optional[torch.Tensor] = None, mode: str = "resid",
+                       w_hat: Optional[torch.Tensor] = None) -> float:
+    """wsic_distortion_noalloc: the same distortion with the library's static scratch (no
+    workspace); `w_hat` (optional) is a caller-allocated output."""
+    _need_cuda(W, codes, U)
+    n_out, n_in = W.shape
+    d = _d(0)
+    _check(lib().wsic_distortion_noalloc(
+        _p(W.data_ptr()), _dtype_code(W), n_out, n_in, _rowmajor(W), _p(codes.data_ptr()), _rowmajor(codes),
+        _p(U.data_ptr()), _rowmajor(U), float(c), _p(resid.data_ptr() if resid is not None else 0),
+        _rowmajor(resid) if resid is not None else n_in, D_DIRECT if mode == "direct" else D_RESID,
+        ctypes.byref(d), _p(w_hat.data_ptr() if w_hat is not None else 0),
+        _dtype_code(w_hat) if w_hat is not None else F32, _rowmajor(w_hat) if w_hat is not None else n_in,
+        _stream(W)))
+    return d.value
 
 
 # ------------------------------------------------------------------------------ SoftWater

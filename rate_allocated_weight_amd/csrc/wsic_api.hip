@@ -9,10 +9,16 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "common.h"
+
+// Scratch of the entry point that allocates nothing (wsic_distortion_noalloc): one copy per GPU,
+// held until the process ends. Host code never uses the array's name as an address: the device
+// address of each GPU's copy comes from hipGetSymbolAddress (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[WSIC_NOALLOC_SCRATCH_BYTES];
 
 namespace wsic {
 
@@ -90,6 +96,41 @@ ProfToken prof_begin(const char* family) {
 void prof_end(ProfToken t, double work) {
   if (t.slot < 0 || t.slot >= (int)g_pending.size()) return;
   g_pending[t.slot].work = work;
+}
+
+// ============================================================== static scratch
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+// Device address of the current device's copy of `scratch`, looked up once per device (with that
+// device current) and kept.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error("hipGetDevice failed: %s", hipGetErrorString(e));
+    return WSIC_E_HIP;
+  }
+  if (dev < 0 || dev >= MAX_DEVICES) {
+    set_error("device index %d out of range", dev);
+    return WSIC_E_INVAL;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error("hipGetSymbolAddress of the static scratch failed on device %d: %s", dev,
+                hipGetErrorString(e));
+      return WSIC_E_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return WSIC_OK;
 }
 
 // ============================================================== workspace layouts
@@ -1840,12 +1881,19 @@ int wsic_entropy(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
   }
 }
 
-int wsic_distortion(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
-                    const int32_t* codes, int64_t ldq, const double* U, int64_t ldu, double c,
-                    const float* resid, int64_t ldr, int mode, double* D_out, void* W_hat,
-                    int w_hat_dtype, int64_t ldh, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace wsic {
+namespace {
+// Shared by wsic_distortion (caller's workspace, pinned staging for the read-back) and
+// wsic_distortion_noalloc (the static scratch, a plain copy into the caller's host memory: no
+// allocation of any kind).
+int distortion_run(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                   const int32_t* codes, int64_t ldq, const double* U, int64_t ldu, double c,
+                   const float* resid, int64_t ldr, int mode, double* D_out, void* W_hat,
+                   int w_hat_dtype, int64_t ldh, void* ws, size_t ws_bytes, void* stream,
+                   bool staged_readback) {
   try {
-    clear_error();
     WSIC_TRY(check_layer(W, dtype, n_out, n_in, ldw));
     if (!codes || ldq < n_in || !U || ldu < n_in || !(c > 0.0) || !std::isfinite(c) || !D_out ||
         (mode != WSIC_D_RESID && mode != WSIC_D_DIRECT) || (mode == WSIC_D_RESID && !resid) ||
@@ -1889,13 +1937,56 @@ int wsic_distortion(const void* W, int dtype, int64_t n_out, int64_t n_in, int64
     }
     WSIC_TRY(launch_sum_partials(d.partial, np, d.out, st));
     int f = 0;
-    const ReadPiece pd[2] = {{D_out, d.out, sizeof(double)}, {&f, d.flags, sizeof(int)}};
-    WSIC_TRY(read_back(pd, 2, st));
+    if (staged_readback) {
+      const ReadPiece pd[2] = {{D_out, d.out, sizeof(double)}, {&f, d.flags, sizeof(int)}};
+      WSIC_TRY(read_back(pd, 2, st));
+    } else {
+      double dh = 0.0;
+      WSIC_HIP_TRY(hipMemcpyAsync(&dh, d.out, sizeof(double), hipMemcpyDeviceToHost, st));
+      WSIC_HIP_TRY(hipMemcpyAsync(&f, d.flags, sizeof(int), hipMemcpyDeviceToHost, st));
+      WSIC_HIP_TRY(hipStreamSynchronize(st));
+      *D_out = dh;
+    }
     return flags_status(f, "distortion");
   } catch (...) {
     set_error("distortion: internal exception");
     return WSIC_E_INVAL;
   }
+}
+}  // namespace
+}  // namespace wsic
+
+extern "C" {
+
+int wsic_distortion(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                    const int32_t* codes, int64_t ldq, const double* U, int64_t ldu, double c,
+                    const float* resid, int64_t ldr, int mode, double* D_out, void* W_hat,
+                    int w_hat_dtype, int64_t ldh, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  return distortion_run(W, dtype, n_out, n_in, ldw, codes, ldq, U, ldu, c, resid, ldr, mode, D_out,
+                        W_hat, w_hat_dtype, ldh, ws, ws_bytes, stream, true);
+}
+
+int wsic_distortion_noalloc(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
+                            const int32_t* codes, int64_t ldq, const double* U, int64_t ldu,
+                            double c, const float* resid, int64_t ldr, int mode, double* D_out,
+                            void* W_hat, int w_hat_dtype, int64_t ldh, void* stream) {
+  clear_error();
+  if (n_out <= 0 || n_in <= 0) {
+    set_error("distortion_noalloc: bad shape");
+    return WSIC_E_INVAL;
+  }
+  const size_t need = ws_bytes_for(WSIC_OP_DISTORTION, n_out, n_in);
+  if (need > WSIC_NOALLOC_SCRATCH_BYTES) {
+    set_error("distortion_noalloc: a %lld x %lld layer needs %zu bytes of scratch, the static "
+              "buffer holds %zu (use wsic_distortion with a workspace)",
+              (long long)n_out, (long long)n_in, need, (size_t)WSIC_NOALLOC_SCRATCH_BYTES);
+    return WSIC_E_WORKSPACE;
+  }
+  void* ws = nullptr;
+  WSIC_TRY(scratch_ptr(&ws));
+  return distortion_run(W, dtype, n_out, n_in, ldw, codes, ldq, U, ldu, c, resid, ldr, mode, D_out,
+                        W_hat, w_hat_dtype, ldh, ws, WSIC_NOALLOC_SCRATCH_BYTES, stream, false);
 }
 
 int wsic_profile_enable(int on) {
