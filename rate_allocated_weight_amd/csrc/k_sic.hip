@@ -471,7 +471,7 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
       pipe::dma16(src + 1024 * ins + 16 * lane, dst + 1024 * ins);
     }
   };
-  auto load_ops = [&](int b, double (&yv)[8], double (&gv)[8], double (&bsc)[8]) {
+  auto load_ops = [&](int b, double (&yv)[8], double (&gv)[8], double (&bsc)[8], double (&dv)[8]) {
     const int64_t j0 = lo + (int64_t)b * BW;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -479,16 +479,19 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
       yv[s] = p.Y[rowc * p.ldy + jc];
       gv[s] = HAS_G ? p.G[rowc * p.ldg + jc] : 0.0;
       bsc[s] = p.bscale[jc];
+      dv[s] = HAS_RESID ? p.invd[jc] : 0.0;
     }
   };
 
-  // Y, G and the bound's column scale (rounded up to float) of the current block
-  double yv[8], gv[8];
+  // Y, G, the bound's column scale (rounded up to float) and 1/U_jj (for the residuals) of the
+  // current block. (1/U_jj is loaded ahead too: read in the output loop, behind its stores, each
+  // load would wait for the stores before it.)
+  double yv[8], gv[8], dv[8];
   float bsf[8];
   {
     double b0[8];
     issue_pack(nb - 1, BsA);
-    load_ops(nb - 1, yv, gv, b0);
+    load_ops(nb - 1, yv, gv, b0, dv);
 #pragma unroll
     for (int s = 0; s < 8; ++s) bsf[s] = f32_up(b0[s]);
   }
@@ -496,6 +499,12 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
   auto do_block = [&](int b, double* Bcur, double* Bidle) {
     const int64_t j0 = lo + (int64_t)b * BW;
     const int w = (int)(hi - j0 < BW ? hi - j0 : BW);
+    // the check's counters start at zero: every read of them in the previous block precedes its
+    // closing barrier, and the barriers before this block's check order the reset before it
+    if (tid == 0) {
+      n_hit = 0;
+      must_redo = 0;
+    }
     const int64_t kf0 = j0 + BW;
     const int kf = (int)(hi - kf0);  // finished columns of the range right of this block
     const bool gin = HAS_G || kf > 0;
@@ -645,19 +654,30 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
       z[s] = in ? zv : 0.0;
       g.bnd[s] = (in && gin) ? tb * bsf[s] : 0.0f;
     }
-    if (active && cnt > 0) {
-      // exact interference of the excess of large codes to the right (fp64); the list may have
-      // grown in this launch, so its entries are read past the L1 cache
-      const int cn = min(cnt, OCAP);
-      const long long* ol = reinterpret_cast<const long long*>(p.olist + row * OCAP);
+    {
+      // Exact interference of the excess of large codes to the right (fp64); the list may have
+      // grown in this launch, so its entries are read past the L1 cache. The loop runs to the
+      // longest list of the wave with every lane's own terms predicated (clamped loads, zero
+      // factors), so that no divergent branch opens here: the compiler has been seen to place
+      // register copies in the join block of such a branch ahead of its exec-mask restore, which
+      // leaves them unwritten in the lanes that skipped it (checked in the assembly at build).
+      const int my_cn = active ? min(cnt, OCAP) : 0;
+      int cn = my_cn;
+      for (int m = 32; m >= 1; m >>= 1) cn = max(cn, __shfl_xor(cn, m, 64));
+      cn = __builtin_amdgcn_readfirstlane(cn);
+      const long long* ol = reinterpret_cast<const long long*>(p.olist + rowc * OCAP);
       for (int o = 0; o < cn; ++o) {
-        const long long raw = __hip_atomic_load(ol + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int ex = (int)(raw & 0xffffffffll), ey = (int)(raw >> 32);
-        const double f = p.invd[ex] * (double)ey;
+        const bool use = o < my_cn;
+        const long long raw =
+            __hip_atomic_load(ol + (use ? o : 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int ex = use ? (int)(raw & 0xffffffffll) : (int)lo;  // lo: any valid column
+        const double f = use ? p.invd[ex] * (double)(int)(raw >> 32) : 0.0;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           const int j = l16 + 16 * s;
-          if (j < w) z[s] -= p.U[(j0 + j) * p.ldu + ex] * f;
+          const int64_t jr = j0 + (j < w ? j : 0);
+          const double t = p.U[jr * p.ldu + ex] * f;
+          z[s] = (j < w) ? z[s] - t : z[s];
         }
       }
     }
@@ -673,7 +693,7 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
     // order.
     // (No branches in the hook: after the last block of the launch it reloads this block's
     // operands into the idle buffer and registers, which nothing reads.)
-    double yn[8], gn[8], bn[8];
+    double yn[8], gn[8], bn[8], dn[8];
     int pf = 0;  // touched digit-plane words (consumed below, never used)
     const int64_t jn0 = b > 0 ? j0 - BW : j0;  // the next block
     auto hook = [&](auto Jc) __attribute__((always_inline)) {
@@ -707,6 +727,7 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
         yn[sv] = p.Y[rowc * p.ldy + jcc];
         gn[sv] = HAS_G ? p.G[rowc * p.ldg + jcc] : 0.0;
         bn[sv] = p.bscale[jcc];
+        dn[sv] = HAS_RESID ? p.invd[jcc] : 0.0;
       }
     };
 
@@ -719,11 +740,6 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
     if (gin) {  // uniform
       // decisions inside the error bound: re-check one by one, re-derive the block if needed
       // (LDS-only barriers: the next block's loads in flight need not land here)
-      if (tid == 0) {
-        n_hit = 0;
-        must_redo = 0;
-      }
-      pipe::barrier_lds();
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         if (0.5 - fabs(z[s] - rint(z[s])) <= (double)g.bnd[s]) {
@@ -825,7 +841,7 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
         }
         qv[s] = qi;
         p.codes[row * p.ldq + j0 + j] = qi;
-        if (HAS_RESID) p.resid[row * p.ldr + j0 + j] = (float)((z[s] - q) * (p.c * p.invd[j0 + j]));
+        if (HAS_RESID) p.resid[row * p.ldr + j0 + j] = (float)((z[s] - q) * (p.c * dv[s]));
         const int q8 = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
         p.q8[row * p.ldq8 + j0 + j] = (int8_t)q8;
         q8s[rloc][(int)(j0 - lo) + j] = (int8_t)q8;
@@ -869,6 +885,7 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
       yv[s] = yn[s];
       gv[s] = gn[s];
       bsf[s] = f32_up(bn[s]);
+      dv[s] = dn[s];
     }
     // int8 codes in LDS visible to every wave; every wave done with this block's packed B
     // before it becomes the idle buffer. (Global stores are not waited for here: the next
