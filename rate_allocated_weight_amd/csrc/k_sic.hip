@@ -662,9 +662,12 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
       // register copies in the join block of such a branch ahead of its exec-mask restore, which
       // leaves them unwritten in the lanes that skipped it (checked in the assembly at build).
       const int my_cn = active ? min(cnt, OCAP) : 0;
-      int cn = my_cn;
-      for (int m = 32; m >= 1; m >>= 1) cn = max(cn, __shfl_xor(cn, m, 64));
-      cn = __builtin_amdgcn_readfirstlane(cn);
+      int cn = 0;
+      if (__ballot(my_cn > 0) != 0) {  // uniform; usually no row of the wave has a list
+        cn = my_cn;
+        for (int m = 32; m >= 1; m >>= 1) cn = max(cn, __shfl_xor(cn, m, 64));
+        cn = __builtin_amdgcn_readfirstlane(cn);
+      }
       const long long* ol = reinterpret_cast<const long long*>(p.olist + rowc * OCAP);
       for (int o = 0; o < cn; ++o) {
         const bool use = o < my_cn;
@@ -753,7 +756,7 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
         }
       }
       pipe::barrier_lds();
-      const int nh = n_hit;
+      const int nh = n_hit;  // uniform: read after the barrier by every thread
       if (tid == 0 && nh > 0) atomicAdd(p.flags + 2, nh);
       // the re-check reads codes other waves stored in earlier blocks: fenced barrier first
       if (nh > 0) __syncthreads();
@@ -779,8 +782,9 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
           __syncthreads();
         }
       }
-      pipe::barrier_lds();  // must_redo (a redo only follows re-checks, after the fence above)
-      if (must_redo) {
+      // must_redo is only ever set after hits; with none it is still the block's reset value
+      if (nh > 0) pipe::barrier_lds();
+      if (nh > 0 && must_redo) {
         double acc[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) acc[s] = 0.0;
