@@ -358,7 +358,8 @@ int wsic_softwater_distortion(const int32_t* codes, int64_t n_out, int64_t n_in,
  * The device is the one current on the calling thread; stream must belong to it.
  * Returns WSIC_E_WORKSPACE when the layer needs more scratch than the buffer holds
  * (wsic_workspace_bytes(WSIC_OP_DISTORTION, n_out, n_in) > WSIC_NOALLOC_SCRATCH_BYTES, about
- * 16 n_in + 8 ceil(n_out / 64) ceil(n_in / 64) bytes; 8192 x 28672 and 32000 x 4096 fit).
+ * 16 n_in + 8 max(ceil(n_out / 64) ceil(n_in / 64), ceil(n_out / 32) ceil(n_in / 1024)) bytes;
+ * 8192 x 28672 and 32000 x 4096 fit).
  * All calls on one GPU share its buffer: calls that overlap in time on one GPU (different
  * streams or threads) race and give undefined results; run them one after another.
  */

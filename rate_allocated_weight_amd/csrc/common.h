@@ -148,6 +148,8 @@ int launch_pack_blocks(const double* U, int64_t ldu, int64_t n, const double* in
 constexpr int LIMBS = 5;
 constexpr double LIMB_EPS = 1.0 / (double)(1ull << (8 * LIMBS - 2));  // 2^-P
 constexpr int OCAP = 64;
+// rows per workgroup of the residual distortion pass (its partials are sized from it)
+constexpr int DIST_ROWS = 32;
 
 struct LeafArgs {
   int64_t n_out, n_in, j0;

@@ -3,35 +3,63 @@
 // The layer distortion tr((W - W_hat) Sigma (W - W_hat)^T) (the output error of Y = W X,
 // WaterSIC page, Sommario tecnico §1) splits per column over the SIC residuals:
 //     D = sum_j U_jj^2 sum_i r_ij^2 .
-// k_dist_resid streams the fp32 residuals once: a workgroup owns a 256-column strip and a
-// slab of rows; each thread keeps one column's sum of squares (fp64), scales it by U_jj^2 and
-// the workgroup writes one partial. Partials are summed in a fixed order by
-// k_sum_partials, so the result is deterministic.
+// k_dist_resid streams the fp32 residuals once: a workgroup owns a strip of 1024 columns (four
+// per thread, read as 16-byte vectors when the rows allow it) and a slab of DIST_ROWS rows, with
+// DIST_UNR rows' loads in flight per thread; each thread keeps its columns' sums of squares in
+// fp64, scales them by U_jj^2, and the workgroup writes one partial. Partials are summed in a
+// fixed order by k_sum_partials, so the result is deterministic.
 #include "common.h"
 
 namespace wsic {
 namespace {
 
-constexpr int ROWS_PER_BLOCK = 256;
+constexpr int DIST_COLS = 1024;  // columns per workgroup: 4 per thread
+constexpr int DIST_UNR = 8;
 
 __global__ __launch_bounds__(256) void k_dist_resid(const float* __restrict__ resid,
                                                     int64_t n_out, int64_t n_in, int64_t ldr,
                                                     const double* __restrict__ U, int64_t ldu,
                                                     double* __restrict__ partial) {
   __shared__ double red[256];
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * ROWS_PER_BLOCK;
-  double s = 0.0;
-  if (j < n_in) {
-    int64_t r1 = r0 + ROWS_PER_BLOCK;
-    if (r1 > n_out) r1 = n_out;
-#pragma unroll 16
-    for (int64_t r = r0; r < r1; ++r) {
-      const double v = (double)resid[r * ldr + j];
-      s = fma(v, v, s);
+  const int64_t j = (int64_t)blockIdx.x * DIST_COLS + 4 * threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * DIST_ROWS;
+  const int64_t r1 = (r0 + DIST_ROWS < n_out) ? r0 + DIST_ROWS : n_out;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  if (j + 3 < n_in && (ldr & 3) == 0 && (((uintptr_t)resid) & 15) == 0) {
+    const float* base = resid + j;
+    for (int64_t r = r0; r < r1; r += DIST_UNR) {
+      float4 v[DIST_UNR];
+#pragma unroll
+      for (int u = 0; u < DIST_UNR; ++u)
+        v[u] = (r + u < r1) ? *reinterpret_cast<const float4*>(base + (r + u) * ldr)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < DIST_UNR; ++u) {
+        acc[0] = fma((double)v[u].x, (double)v[u].x, acc[0]);
+        acc[1] = fma((double)v[u].y, (double)v[u].y, acc[1]);
+        acc[2] = fma((double)v[u].z, (double)v[u].z, acc[2]);
+        acc[3] = fma((double)v[u].w, (double)v[u].w, acc[3]);
+      }
     }
-    const double d = U[j * ldu + j];
-    s *= d * d;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (j + e < n_in) {
+#pragma unroll 8
+        for (int64_t r = r0; r < r1; ++r) {
+          const double v = (double)resid[r * ldr + j + e];
+          acc[e] = fma(v, v, acc[e]);
+        }
+      }
+    }
+  }
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (j + e < n_in) {
+      const double d = U[(j + e) * ldu + j + e];
+      s = fma(acc[e], d * d, s);
+    }
   }
   red[threadIdx.x] = s;
   __syncthreads();
@@ -84,8 +112,8 @@ __global__ void k_dequant(const int32_t* __restrict__ codes, int64_t n_out, int6
 
 int launch_dist_resid(const float* resid, int64_t n_out, int64_t n_in, int64_t ldr,
                       const double* U, int64_t ldu, double* partial, int nblk, hipStream_t st) {
-  const unsigned gx = (unsigned)((n_in + 255) / 256);
-  const unsigned gy = (unsigned)((n_out + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK);
+  const unsigned gx = (unsigned)((n_in + DIST_COLS - 1) / DIST_COLS);
+  const unsigned gy = (unsigned)((n_out + DIST_ROWS - 1) / DIST_ROWS);
   if ((int64_t)gx * gy > nblk) {
     set_error("internal: distortion partials %u x %u > %d", gx, gy, nblk);
     return WSIC_E_WORKSPACE;

@@ -14,10 +14,11 @@
 namespace wsic {
 namespace {
 
-// codes in [-7, 8] are tallied per thread as 16-bit counters, two to a register; a thread
-// counts at most HIST_PER_THREAD codes, so a wave's sums still fit 16 bits
+// codes in [-7, 8] are tallied per thread as 8-bit counters, four to a register; a thread
+// counts at most HIST_PER_THREAD codes, so a counter cannot overflow, and the wave sums are
+// formed in 16-bit halves (at most 64 x 255)
 constexpr int REG_LO = -7, REG_N = 16;
-constexpr int HIST_PER_THREAD = 1000;
+constexpr int HIST_PER_THREAD = 255;
 // LDS window of a workgroup (codes beyond it go to the global window with global atomics)
 constexpr int LDS_HALF = 255, LDS_BINS = 2 * LDS_HALF + 1;
 
@@ -30,16 +31,16 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ codes,
   for (int b = threadIdx.x; b < LDS_BINS; b += blockDim.x) lb[b] = 0u;
   __syncthreads();
 
-  unsigned int reg[REG_N / 2];
+  unsigned int reg[REG_N / 4];
 #pragma unroll
-  for (int k = 0; k < REG_N / 2; ++k) reg[k] = 0u;
+  for (int k = 0; k < REG_N / 4; ++k) reg[k] = 0u;
 
   auto count = [&](int v) {
     const int t = v - REG_LO;
-    if (t >= 0 && t < REG_N) {
-      const unsigned int inc = 1u << (16 * (t & 1));
+    if ((unsigned)t < (unsigned)REG_N) {
+      const unsigned int inc = 1u << (8 * (t & 3));
 #pragma unroll
-      for (int k = 0; k < REG_N / 2; ++k) reg[k] += ((t >> 1) == k) ? inc : 0u;
+      for (int k = 0; k < REG_N / 4; ++k) reg[k] += ((t >> 2) == k) ? inc : 0u;
     } else if (v >= -LDS_HALF && v <= LDS_HALF) {
       atomicAdd(&lb[v + LDS_HALF], 1u);
     } else if (v >= -HIST_HALF && v <= HIST_HALF) {
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ codes,
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if (ldq == n_in && (((uintptr_t)codes) & 15) == 0) {
     // dense: 16-byte loads, UNR of them in flight per thread
-    constexpr int UNR = 4;
+    constexpr int UNR = 8;
     const int4* c4 = reinterpret_cast<const int4*>(codes);
     const int64_t n4 = total / 4;
     for (int64_t e = gid; e < n4; e += stride * UNR) {
@@ -75,15 +76,20 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ codes,
   } else {
     for (int64_t e = gid; e < total; e += stride) count(codes[(e / n_in) * ldq + (e % n_in)]);
   }
-  // register tallies: summed over the wave, one LDS atomic per wave and bin
+  // register tallies: widened to 16-bit halves (bins 4k, 4k+2 and 4k+1, 4k+3), summed over the
+  // wave, one LDS atomic per wave and bin
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int k = 0; k < REG_N / 2; ++k) {
-    unsigned int v = reg[k];
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    if (lane == 0) {
-      if (v & 0xffffu) atomicAdd(&lb[2 * k + REG_LO + LDS_HALF], v & 0xffffu);
-      if (v >> 16) atomicAdd(&lb[2 * k + 1 + REG_LO + LDS_HALF], v >> 16);
+  for (int k = 0; k < REG_N / 4; ++k) {
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) {
+      unsigned int v = (reg[k] >> (8 * odd)) & 0x00ff00ffu;
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      if (lane == 0) {
+        const int b0 = 4 * k + odd + REG_LO + LDS_HALF;
+        if (v & 0xffffu) atomicAdd(&lb[b0], v & 0xffffu);
+        if (v >> 16) atomicAdd(&lb[b0 + 2], v >> 16);
+      }
     }
   }
   __syncthreads();
@@ -136,10 +142,13 @@ __global__ void k_fill_zero(uint32_t* p, size_t words) {
 int launch_hist(const int32_t* codes, int64_t n_out, int64_t n_in, int64_t ldq,
                 unsigned long long* bins, int32_t* ovf, unsigned int* ovf_count, hipStream_t st) {
   const int64_t total = n_out * n_in;
-  // enough threads that none counts more than HIST_PER_THREAD codes (16-bit wave sums), and at
-  // least ~64 codes per thread so the per-workgroup window clear and flush stay small
-  int64_t blocks = (total + 256 * 64 - 1) / (256 * 64);
-  const int64_t need = (total + 256LL * HIST_PER_THREAD - 1) / (256LL * HIST_PER_THREAD);
+  // enough threads that none counts more than HIST_PER_THREAD codes (8-bit tallies): a thread
+  // takes at most 4 ceil(total / (4 threads)) codes of the vector loop plus one of the tail, so
+  // sizing for HIST_PER_THREAD - 7 per thread keeps it below the limit; about 128 codes per
+  // thread otherwise, so the per-workgroup window clear and flush stay small
+  int64_t blocks = (total + 256 * 128 - 1) / (256 * 128);
+  const int64_t per = HIST_PER_THREAD - 7;
+  const int64_t need = (total + 256LL * per - 1) / (256LL * per);
   if (blocks > 2048) blocks = 2048;
   if (blocks < need) blocks = need;
   if (blocks < 1) blocks = 1;

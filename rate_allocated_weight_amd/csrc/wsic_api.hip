@@ -256,10 +256,13 @@ WfWs carve_wf(Carve& cv, int64_t n_out, int64_t n_in) {
   return w;
 }
 
+// partial sums written by k_dist_resid: one per 1024-column by DIST_ROWS-row tile
+int64_t dist_resid_partials(int64_t n_out, int64_t n_in) {
+  return ((n_in + 1023) / 1024) * ((n_out + DIST_ROWS - 1) / DIST_ROWS);
+}
 int64_t dist_partials(int64_t n_out, int64_t n_in) {
-  const int64_t a = ((n_in + 255) / 256) * ((n_out + 255) / 256);
-  const int64_t b = ((n_out + 63) / 64) * ((n_in + 63) / 64);
-  return std::max(a, b);
+  const int64_t b = ((n_out + 63) / 64) * ((n_in + 63) / 64);  // direct mode: one per GEMM tile
+  return std::max(dist_resid_partials(n_out, n_in), b);
 }
 struct DistWs {
   int* flags;
@@ -1503,7 +1506,7 @@ int wsic_softwater_distortion(const int32_t* codes, int64_t n_out, int64_t n_in,
       WSIC_TRY(launch_dequant(codes, n_out, n_in, ldq, d.invd, c, W_hat, w_hat_dtype, ldh, st, sc.s));
     // the residuals of the class-aware SIC are those of the rows s_r w_r: sum_j U_jj^2 sum_r r_rj^2
     // is sum_r lambda_r e_r Sigma e_r^T, twice the KL estimate
-    const int64_t np = ((n_in + 255) / 256) * ((n_out + 255) / 256);
+    const int64_t np = dist_resid_partials(n_out, n_in);
     WSIC_TRY(launch_dist_resid(resid, n_out, n_in, ldr, U, ldu, d.partial, (int)np, st));
     WSIC_TRY(launch_sum_partials(d.partial, np, d.out, st));
     int f = 0;
@@ -1912,7 +1915,7 @@ int distortion_run(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_
       WSIC_TRY(launch_dequant(codes, n_out, n_in, ldq, d.invd, c, W_hat, w_hat_dtype, ldh, st));
     int64_t np = 0;
     if (mode == WSIC_D_RESID) {
-      np = ((n_in + 255) / 256) * ((n_out + 255) / 256);
+      np = dist_resid_partials(n_out, n_in);
       WSIC_TRY(launch_dist_resid(resid, n_out, n_in, ldr, U, ldu, d.partial, (int)np, st));
     } else {
       WSIC_TRY(launch_delta(U, ldu, n_in, c, d.delta, nullptr, st));

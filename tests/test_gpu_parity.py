@@ -401,3 +401,19 @@ def test_sic_parity_large_codes(device, bits):
     sic = oracle.sic_quantize(layer.w, L, c)
     assert_codes_parity(q, sic, label=f"bits={bits}")
     assert big.max() > 0
+
+
+def test_entropy_at_the_per_thread_tally_limit(device):
+    """A layer large enough that the histogram launch gives each thread its maximum share of
+    codes (the 8-bit register tallies must not wrap), all in the tallied range [-7, 8]."""
+    n = 256 * 2048 * 250  # more codes than 2048 workgroups cover at 128 per thread
+    say(f"[entropy] per-thread limit: {n} codes")
+    i = torch.arange(n, device=device, dtype=torch.int64)
+    q = torch.where(i % 3 == 0, 1, torch.where(i % 7 == 0, -7, 0)).to(torch.int32).view(-1, 1024)
+    counts = torch.bincount((q.view(-1).to(torch.int64) + 7)).cpu().numpy()
+    p = counts[counts > 0].astype(np.float64) / n
+    expect = float(-(p * np.log2(p)).sum())
+    h, ns = lib.entropy(q)
+    say(f"  device {h!r} from counts {expect!r}")
+    assert ns == 3
+    assert h == pytest.approx(expect, abs=1e-12)
