@@ -27,12 +27,14 @@ __global__ __launch_bounds__(256) void k_dist_resid(const float* __restrict__ re
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
   if (j + 3 < n_in && (ldr & 3) == 0 && (((uintptr_t)resid) & 15) == 0) {
     const float* base = resid + j;
-    for (int64_t r = r0; r < r1; r += DIST_UNR) {
+    int64_t r = r0;
+    // whole groups: DIST_UNR unconditional loads issued before the first use (a per-load
+    // condition here becomes a branch with its own wait, one load in flight at a time)
+    for (; r + DIST_UNR <= r1; r += DIST_UNR) {
       float4 v[DIST_UNR];
 #pragma unroll
       for (int u = 0; u < DIST_UNR; ++u)
-        v[u] = (r + u < r1) ? *reinterpret_cast<const float4*>(base + (r + u) * ldr)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[u] = *reinterpret_cast<const float4*>(base + (r + u) * ldr);
 #pragma unroll
       for (int u = 0; u < DIST_UNR; ++u) {
         acc[0] = fma((double)v[u].x, (double)v[u].x, acc[0]);
@@ -40,6 +42,13 @@ __global__ __launch_bounds__(256) void k_dist_resid(const float* __restrict__ re
         acc[2] = fma((double)v[u].z, (double)v[u].z, acc[2]);
         acc[3] = fma((double)v[u].w, (double)v[u].w, acc[3]);
       }
+    }
+    for (; r < r1; ++r) {
+      const float4 v = *reinterpret_cast<const float4*>(base + r * ldr);
+      acc[0] = fma((double)v.x, (double)v.x, acc[0]);
+      acc[1] = fma((double)v.y, (double)v.y, acc[1]);
+      acc[2] = fma((double)v.z, (double)v.z, acc[2]);
+      acc[3] = fma((double)v.w, (double)v.w, acc[3]);
     }
   } else {
 #pragma unroll

@@ -405,11 +405,13 @@ def test_sic_parity_large_codes(device, bits):
 
 def test_entropy_at_the_per_thread_tally_limit(device):
     """A layer large enough that the histogram launch gives each thread its maximum share of
-    codes (the 8-bit register tallies must not wrap), all in the tallied range [-7, 8]."""
-    n = 256 * 2048 * 250  # more codes than 2048 workgroups cover at 128 per thread
+    codes, nearly all of them the same code, so one 8-bit register tally per thread comes close to
+    its limit (it must not wrap); the rest at both ends of the tallied range [-7, 7]."""
+    n = 512 * 2048 * 250  # more codes than 2048 workgroups of 512 threads cover at 128 per thread
     say(f"[entropy] per-thread limit: {n} codes")
     i = torch.arange(n, device=device, dtype=torch.int64)
-    q = torch.where(i % 3 == 0, 1, torch.where(i % 7 == 0, -7, 0)).to(torch.int32).view(-1, 1024)
+    q = torch.where(i % 101 == 0, 7, torch.where(i % 103 == 0, -7, 0)).to(torch.int32).view(-1, 1024)
+    del i
     counts = torch.bincount((q.view(-1).to(torch.int64) + 7)).cpu().numpy()
     p = counts[counts > 0].astype(np.float64) / n
     expect = float(-(p * np.log2(p)).sum())
