@@ -112,8 +112,22 @@ int launch_gemm_y(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int
                   const double* B, int64_t ldb, double* C, int64_t ldc, double work, hipStream_t st);
 
 // covariance
+// The tiles of the last, partial round of the covariance launch (the tile count is rarely a
+// multiple of the CU count) are split along K into `pieces` workgroups each, which write their
+// partial sums to a slot each in the workspace; a second launch adds them up. `full` tiles are
+// computed whole.
+constexpr int SPLIT_SLOTS = 256;     // workgroups the partial round is spread over
+constexpr int SPLIT_MAX_PIECES = 16;
+struct SyrkSplit {
+  int64_t full;   // tiles computed whole
+  int pieces;     // workgroups per split tile
+  int64_t tail;   // split tiles
+};
+SyrkSplit syrk_split(int64_t n);
+size_t syrk_split_bytes(int64_t n);  // workspace of the split (0: none)
 int launch_syrk(const void* X, int dtype, int64_t rows, int64_t n, int64_t ldx, double alpha,
-                double beta, double* S, int64_t lds, hipStream_t st);
+                double beta, double* S, int64_t lds, void* split_ws, size_t split_ws_bytes,
+                hipStream_t st);
 int launch_mirror_upper(double* S, int64_t n, int64_t lds, hipStream_t st);
 int launch_diag_check(const double* S, int64_t n, int64_t lds, int* flags, hipStream_t st);
 

@@ -378,6 +378,7 @@ size_t ws_bytes_for(int op, int64_t n_out, int64_t n_in) {
   switch (op) {
     case WSIC_OP_COVARIANCE:
       cv.take<int>(FLAGS_BYTES / sizeof(int));
+      cv.take<char>(syrk_split_bytes(n_in));  // K-split of the launch's last partial round
       break;
     case WSIC_OP_CHOLESKY:
       cv.take<int>(FLAGS_BYTES / sizeof(int));
@@ -1020,9 +1021,13 @@ int wsic_covariance(const void* X, int dtype, int64_t rows, int64_t n_in, int64_
     }
     WSIC_TRY(check_ws(WSIC_OP_COVARIANCE, 0, n_in, ws, ws_bytes));
     hipStream_t st = (hipStream_t)stream;
-    int* flags = (int*)ws;
+    Carve cv(ws);
+    int* flags = cv.take<int>(FLAGS_BYTES / sizeof(int));
+    const size_t split_bytes = syrk_split_bytes(n_in);
+    void* split_ws = cv.take<char>(split_bytes);
     WSIC_TRY(launch_fill_zero(flags, FLAGS_BYTES, st));
-    WSIC_TRY(launch_syrk(X, dtype, rows, n_in, ldx, alpha, beta, Sigma, lds, st));
+    WSIC_TRY(launch_syrk(X, dtype, rows, n_in, ldx, alpha, beta, Sigma, lds, split_ws, split_bytes,
+                         st));
     WSIC_TRY(launch_mirror_upper(Sigma, n_in, lds, st));
     WSIC_TRY(launch_diag_check(Sigma, n_in, lds, flags, st));
     int f = 0;
