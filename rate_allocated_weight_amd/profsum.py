@@ -7,6 +7,8 @@ Reads the CSV files rocprofv3 writes (`--output-format csv`) for
   (`*_counter_collection.csv`, KiB per dispatch),
 * the same two counters for a plain device copy of known size (`bench.py
   --copy-calibration-mib M`), which turns the counter readings into bytes,
+* optionally a `--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE` run: the matrix-core busy
+  fraction per kernel, SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs),
 
 and writes, for one workload:
 
@@ -166,8 +168,20 @@ def trace_md(title: str, cmd: str, stats: list[dict], top: int = 24) -> str:
     return "\n".join(lines) + "\n"
 
 
+def mfma_busy(d: str) -> dict[str, float]:
+    """Per kernel: matrix-core busy fraction, averaged over its dispatches."""
+    busy = read_counters(d, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = read_counters(d, "GRBM_GUI_ACTIVE")
+    out = {}
+    for k, b in busy.items():
+        g = gui.get(k, [])
+        if len(g) == len(b) and sum(g) > 0:
+            out[k] = sum(b) / (sum(g) / 8.0 * 1024.0)
+    return out
+
+
 def counters_md(title: str, cmds: list[str], fetch: dict, write: dict, s_read: float,
-                s_write: float, calib_mib: int, top: int = 20) -> str:
+                s_write: float, calib_mib: int, top: int = 20, busy: dict | None = None) -> str:
     rows = []
     for k, rd in fetch.items():
         wr = write.get(k, [])
@@ -183,6 +197,12 @@ def counters_md(title: str, cmds: list[str], fetch: dict, write: dict, s_read: f
              "", "| kernel | launches | read MiB/launch | write MiB/launch |", "|---|---:|---:|---:|"]
     for _, k, n, r, w in rows[:top]:
         lines.append(f"| `{k}` | {n} | {r:.3f} | {w:.3f} |")
+    if busy:
+        lines += ["", "Matrix cores: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs).",
+                  "", "| kernel | MFMA busy |", "|---|---:|"]
+        for k, v in sorted(busy.items(), key=lambda t: -t[1]):
+            if v >= 0.001:
+                lines.append(f"| `{k}` | {v:.3f} |")
     return "\n".join(lines) + "\n"
 
 
@@ -197,6 +217,7 @@ def main(argv=None):
     ap.add_argument("--calib-fetch", required=True)
     ap.add_argument("--calib-write", required=True)
     ap.add_argument("--calib-mib", type=int, default=1024)
+    ap.add_argument("--mfma", help="rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE folder")
     ap.add_argument("--cmd", action="append", default=[],
                     help="command lines that made the runs (trace first, if any)")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
@@ -215,7 +236,8 @@ def main(argv=None):
         fh.write("\n")
     pmc_cmds = [c for c in a.cmd if "--kernel-trace" not in c]
     with open(os.path.join(a.out, f"{a.name}_counters.md"), "w") as fh:
-        fh.write(counters_md(title, pmc_cmds, fetch, write, s_read, s_write, a.calib_mib))
+        fh.write(counters_md(title, pmc_cmds, fetch, write, s_read, s_write, a.calib_mib,
+                             busy=mfma_busy(a.mfma) if a.mfma else None))
     if a.trace:
         tcmd = next((c for c in a.cmd if "--kernel-trace" in c), "")
         with open(os.path.join(a.out, f"{a.name}_kernel_trace.md"), "w") as fh:
