@@ -77,36 +77,53 @@ __global__ void k_limb_digits(const double* __restrict__ U, int64_t ldu, int64_t
 
 // C[M x N] (+)= F, F(m, n) = escale[n] * sum_l 256^(NL-1-l) sum_k A8(m,k) D_l(n,k).
 //
-// Tile 128 x 64, K-step 64; 4 waves in 2 x 2, each 64 x 32 = two 32x32 fragments, every
-// fragment with NL int32 accumulators. Operands go from global memory straight into LDS
-// (global_load_lds_dwordx4: each instruction of a wave fills 1 KiB, lane l at byte 16 l) through
-// a ring of STAGES buffers, so STAGES - 1 K-steps are in flight while one is multiplied, and no
-// registers are spent on staging. Each 64-byte LDS row holds four 16-byte chunks; chunk c of
-// row r sits in slot c ^ swz(r), which spreads the 32 rows one MFMA operand read touches over
-// all LDS banks. When beta != 0 the C tile is loaded into registers before the first operand
-// load, so its latency hides behind the whole K loop.
+// Tile TM x 64, K-step 64; NW waves in (TM/64) x 2, each 64 x 32 = two 32x32 fragments, every
+// fragment with NL int32 accumulators. Two shapes: 128 x 64 with 4 waves, and 256 x 64 with 8
+// waves (two per SIMD) for the large products, where it reads 36 KiB of operands per K-step for
+// twice the multiply-adds of the 28 KiB small tile (the product is bound by the operand traffic
+// from L2: each digit plane is read once per 64-row strip of codes). Operands go from global
+// memory straight into LDS (global_load_lds_dwordx4: each instruction of a wave fills 1 KiB, lane
+// l at byte 16 l) through a ring of STAGES buffers, so STAGES - 1 K-steps are in flight while one
+// is multiplied, and no registers are spent on staging. A stage's 1 KiB loads are dealt to the
+// waves round-robin (so with 36 of them, waves 0-3 issue 5 and waves 4-7 issue 4, and each waits
+// on its own count). Each 64-byte LDS row holds four 16-byte chunks; chunk c of row r sits in slot
+// c ^ swz(r), which spreads the 32 rows one MFMA operand read touches over all LDS banks. When
+// beta != 0 the C tile is loaded into registers before the first operand load, so its latency
+// hides behind the whole K loop.
 //
 // Reads are whole 64-byte K-steps: A8 and D must hold zeros in columns [K, roundup(K, 64)).
 // Rows past M or N load a clamped (valid) row whose results are never stored.
-constexpr int TM = 128, TN = 64, TKB = 64;
+constexpr int TN = 64, TKB = 64;
 constexpr int STAGES = 3;
-constexpr int A_BYTES = TM * TKB;          // 8 KiB
-constexpr int B_BYTES = NL * TN * TKB;     // 20 KiB
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int A_INSTR = A_BYTES / 1024 / 4;  // DMA instructions per wave per stage
-constexpr int B_INSTR = B_BYTES / 1024 / 4;
-constexpr int DMA_PER_STAGE = A_INSTR + B_INSTR;
-static_assert(A_INSTR * 4096 == A_BYTES && B_INSTR * 4096 == B_BYTES, "whole DMA rounds");
+
+template <int TM_, int NW_>
+struct I8Tile {
+  static constexpr int TM = TM_, NW = NW_;
+  static constexpr int A_BYTES = TM * TKB;
+  static constexpr int B_BYTES = NL * TN * TKB;  // 20 KiB
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_INS = A_BYTES / 1024, INS = STAGE_BYTES / 1024;  // 1 KiB loads per stage
+  static constexpr int DMA_MAX = (INS + NW - 1) / NW;                     // per wave (at most)
+  // the C tile goes into registers before the K loop when the registers allow (the large tile's
+  // 160 accumulator registers per lane leave no room: it loads C after the loop)
+  static constexpr bool C_FIRST = NW == 4;
+  static_assert(TM == 64 * (NW / 2) && NW % 2 == 0, "waves in (TM/64) x 2");
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 4096 == 0, "whole 1 KiB loads");
+};
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
-__global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K,
-                                                 const int8_t* __restrict__ A8, int64_t lda,
-                                                 const int8_t* __restrict__ D, int64_t ldd,
-                                                 int64_t plane, const double* __restrict__ escale,
-                                                 double* __restrict__ C, int64_t ldc, double beta,
-                                                 int tiles_n) {
+template <class Cfg>
+__global__ __launch_bounds__(64 * Cfg::NW) void k_gemm_i8(int64_t M, int64_t N, int64_t K,
+                                                          const int8_t* __restrict__ A8,
+                                                          int64_t lda,
+                                                          const int8_t* __restrict__ D,
+                                                          int64_t ldd, int64_t plane,
+                                                          const double* __restrict__ escale,
+                                                          double* __restrict__ C, int64_t ldc,
+                                                          double beta, int tiles_n) {
+  constexpr int TM = Cfg::TM, NW = Cfg::NW, A_BYTES = Cfg::A_BYTES, A_INS = Cfg::A_INS;
+  constexpr int INS = Cfg::INS, DMA_MAX = Cfg::DMA_MAX, STAGE_BYTES = Cfg::STAGE_BYTES;
   __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * STAGE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
@@ -117,7 +134,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K
   const int64_t ncol = n0 + wn * 32 + (lane & 31);
   const bool ncol_ok = ncol < N;
   double cold[2][16];
-  if (beta != 0.0) {
+  auto load_c = [&]() {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -125,40 +142,38 @@ __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K
         const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         cold[i][r] = (m < M && ncol_ok) ? C[m * ldc + ncol] : 0.0;
       }
-  }
+  };
+  if (Cfg::C_FIRST && beta != 0.0) load_c();
 
-  // DMA sources of this lane: A instruction h of this wave covers rows 16 (A_INSTR w + h) + l/4,
-  // B instruction h covers limb / row (B_INSTR w + h) as 4 instructions per limb plane.
-  const int8_t* asrc[A_INSTR];
-  const int8_t* bsrc[B_INSTR];
-  int aoff[A_INSTR], boff[B_INSTR];
+  // DMA sources of this lane: load g = wave + NW h of a stage; g < A_INS covers rows 16 g + l/4
+  // of the codes, the rest limb plane (g - A_INS) / 4, rows 16 ((g - A_INS) % 4) + l/4 of D
+  const int8_t* src[DMA_MAX];
+  int off[DMA_MAX];
 #pragma unroll
-  for (int h = 0; h < A_INSTR; ++h) {
-    const int ins = A_INSTR * wave + h;
-    const int r = 16 * ins + (lane >> 2);
-    const int c = (lane & 3) ^ swz(r);
-    const int64_t m = (m0 + r < M) ? m0 + r : M - 1;
-    asrc[h] = A8 + m * lda + 16 * c;
-    aoff[h] = 1024 * ins;
+  for (int h = 0; h < DMA_MAX; ++h) {
+    int g = wave + NW * h;
+    g = g < INS ? g : INS - 1;  // (not issued: see `mine` below)
+    if (g < A_INS) {
+      const int r = 16 * g + (lane >> 2);
+      const int c = (lane & 3) ^ swz(r);
+      const int64_t m = (m0 + r < M) ? m0 + r : M - 1;
+      src[h] = A8 + m * lda + 16 * c;
+    } else {
+      const int bi = g - A_INS;
+      const int l = bi >> 2, r = 16 * (bi & 3) + (lane >> 2);
+      const int c = (lane & 3) ^ swz(r);
+      const int64_t n = (n0 + r < N) ? n0 + r : N - 1;
+      src[h] = D + l * plane + n * ldd + 16 * c;
+    }
+    off[h] = 1024 * g;
   }
-#pragma unroll
-  for (int h = 0; h < B_INSTR; ++h) {
-    const int ins = B_INSTR * wave + h;
-    const int l = ins >> 2, r = 16 * (ins & 3) + (lane >> 2);
-    const int c = (lane & 3) ^ swz(r);
-    const int64_t n = (n0 + r < N) ? n0 + r : N - 1;
-    bsrc[h] = D + l * plane + n * ldd + 16 * c;
-    boff[h] = A_BYTES + 1024 * ins;
-  }
+  const int mine = (INS - wave + NW - 1) / NW;  // loads this wave issues per stage (uniform)
   auto issue = [&](int64_t kstep, int buf) {
     int8_t* base = smem + buf * STAGE_BYTES;
     const int64_t k0 = kstep * TKB;
 #pragma unroll
-    for (int h = 0; h < A_INSTR; ++h)
-      pipe::dma16(asrc[h] + k0, base + aoff[h]);
-#pragma unroll
-    for (int h = 0; h < B_INSTR; ++h)
-      pipe::dma16(bsrc[h] + k0, base + boff[h]);
+    for (int h = 0; h < DMA_MAX; ++h)
+      if (h < mine) pipe::dma16(src[h] + k0, base + off[h]);
   };
 
   v16i acc[2][NL];
@@ -177,7 +192,11 @@ __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K
     if (st < nk) issue(st, st);
   int cur = 0;  // buffer of step t; step t + STAGES - 1 goes into the one before it
   for (int t = 0; t < nk; ++t) {
-    pipe::wait_ahead<DMA_PER_STAGE, STAGES - 2>(min(STAGES - 2, nk - 1 - t));
+    const int ahead = min(STAGES - 2, nk - 1 - t);
+    if (mine == DMA_MAX)
+      pipe::wait_ahead<DMA_MAX, STAGES - 2>(ahead);
+    else
+      pipe::wait_ahead<(DMA_MAX > 1 ? DMA_MAX - 1 : 1), STAGES - 2>(ahead);
     pipe::barrier_lds();  // step t is in LDS for every wave; every wave is done with step t - 1
     if (t + STAGES - 1 < nk) issue(t + STAGES - 1, cur == 0 ? STAGES - 1 : cur - 1);
     const int8_t* As = smem + cur * STAGE_BYTES;
@@ -203,6 +222,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K
     }
   }
 
+  if (!Cfg::C_FIRST && beta != 0.0) load_c();
   if (!ncol_ok) return;
   const double es = escale[ncol];
 #pragma unroll
@@ -219,6 +239,10 @@ __global__ __launch_bounds__(256) void k_gemm_i8(int64_t M, int64_t N, int64_t K
       }
     }
 }
+
+using I8Small = I8Tile<128, 4>;
+using I8Large = I8Tile<256, 8>;
+constexpr int64_t I8_LARGE_MIN_TILES = 256;  // the CU count of the chip
 
 }  // namespace
 
@@ -245,11 +269,21 @@ int launch_gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t* A8, int64_t ld
     set_error("internal: int8 operands shorter than whole K-steps");
     return WSIC_E_INVAL;
   }
-  const int64_t tiles_n = (N + TN - 1) / TN, tiles = ((M + TM - 1) / TM) * tiles_n;
+  const int64_t tiles_n = (N + TN - 1) / TN;
   // algorithmic int8 ops: NL digit products per multiply-add
   const double work = 2.0 * NL * (double)M * (double)N * (double)K;
-  WSIC_LAUNCH("gemm_trail_i8", work, st, k_gemm_i8, dim3((unsigned)tiles), dim3(256), 0, M, N, K,
-              A8, lda, D, ldd, plane, escale, C, ldc, beta, (int)tiles_n);
+  // the large tile when it still gives every CU a workgroup
+  const int64_t tiles_large = ((M + I8Large::TM - 1) / I8Large::TM) * tiles_n;
+  if (tiles_large >= I8_LARGE_MIN_TILES) {
+    WSIC_LAUNCH("gemm_trail_i8", work, st, k_gemm_i8<I8Large>, dim3((unsigned)tiles_large),
+                dim3(64 * I8Large::NW), 0, M, N, K, A8, lda, D, ldd, plane, escale, C, ldc, beta,
+                (int)tiles_n);
+  } else {
+    const int64_t tiles = ((M + I8Small::TM - 1) / I8Small::TM) * tiles_n;
+    WSIC_LAUNCH("gemm_trail_i8", work, st, k_gemm_i8<I8Small>, dim3((unsigned)tiles),
+                dim3(64 * I8Small::NW), 0, M, N, K, A8, lda, D, ldd, plane, escale, C, ldc, beta,
+                (int)tiles_n);
+  }
   return WSIC_OK;
 }
 
