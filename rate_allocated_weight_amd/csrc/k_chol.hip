@@ -120,9 +120,15 @@ __device__ __forceinline__ void panel_factor(double (&a)[RPW], double (&sl)[RPW]
         if (k0 + t < nbk) {  // uniform
           const double ut = pl->u[par][t][j];
           const double xt = pl->x[par][t][j];
+          // U(k0 + t, RPW w .. RPW w + RPW - 1): the same 64 bytes for every lane, read as
+          // 16-byte pairs (one LDS read per pair instead of per entry)
+          const double2* row = reinterpret_cast<const double2*>(&pl->u[par][t][RPW * w]);
+          double2 q[RPW / 2];
+#pragma unroll
+          for (int h = 0; h < RPW / 2; ++h) q[h] = row[h];
 #pragma unroll
           for (int s = 0; s < RPW; ++s) {
-            const double uis = pl->u[par][t][RPW * w + s];  // U(k0 + t, RPW w + s)
+            const double uis = (s & 1) ? q[s >> 1].y : q[s >> 1].x;
             a[s] = fma(-uis, ut, a[s]);
             sl[s] = fma(-uis, xt, sl[s]);
           }
