@@ -56,6 +56,27 @@ def test_covariance_parity(device, name):
     assert err <= tol
 
 
+@pytest.mark.parametrize("n_in,rows", [(3072, 1000), (3000, 777)])
+def test_covariance_split_tail_round(device, n_in, rows):
+    """Widths whose tile count is not a multiple of the CU count: the tiles of the last, partial
+    round are split along the calibration rows (here into pieces of a few 96-row steps, the last
+    one ragged) and their partial sums added by a second launch. Also the streaming form
+    (beta != 0) through the same path."""
+    layer = workloads.make_layer("ar1", 8, n_in, rows, seed=11, name=f"split_{n_in}")
+    say(f"[covariance-split] rows={rows} n_in={n_in}")
+    X = x_tensors(layer)
+    sig_gpu = lib.covariance_chunks(X).cpu().numpy()
+    sig_or = _sigma_oracle(layer)
+    scale = np.sqrt(np.outer(np.diag(sig_or), np.diag(sig_or)))
+    err = np.max(np.abs(sig_gpu - sig_or) / scale)
+    say(f"  max normalized |dSigma| = {err:.3e}")
+    assert np.array_equal(sig_gpu, sig_gpu.T)
+    assert err <= 1e-6
+    s1 = lib.covariance(X[0], alpha=0.5)
+    s2 = lib.covariance(X[0], sigma=s1.clone(), alpha=0.25, beta=2.0)
+    assert torch.allclose(s2, s1 * 2.5, rtol=1e-12, atol=0)
+
+
 def test_covariance_streaming_beta(device):
     layer = _layer("spiked_300x333")
     X = x_tensors(layer)[0]
