@@ -2,6 +2,8 @@
 it must return what wsic_distortion returns on the same inputs, on consecutive calls that share
 the static scratch (the second on a smaller layer, so stale partials of the first would show),
 in both distortion modes, with the dequantized weights; and it must allocate nothing."""
+import gc
+
 import numpy as np
 import pytest
 import torch
@@ -35,12 +37,20 @@ def test_noalloc_distortion_equals_workspace_call():
             d_ws, wh_ws = lib.distortion(Wt, codes, U, c, resid=resid if mode == "resid" else None, mode=mode,
                                          w_hat_dtype=torch.float32)
             wh = torch.full((n_out, n_in), float("nan"), dtype=torch.float32, device=DEV)
-            torch.cuda.synchronize()
-            before = torch.cuda.memory_allocated()
-            d_na = lib.distortion_noalloc(Wt, codes, U, c, resid=resid if mode == "resid" else None, mode=mode,
-                                          w_hat=wh)
-            torch.cuda.synchronize()
-            assert torch.cuda.memory_allocated() == before
+            # the garbage collector must not free tensors of earlier tests inside the measured
+            # call (a drop of the count is no allocation, but it would hide one)
+            gc.collect()
+            gc.disable()
+            try:
+                torch.cuda.synchronize()
+                before = torch.cuda.memory_allocated()
+                d_na = lib.distortion_noalloc(Wt, codes, U, c, resid=resid if mode == "resid" else None,
+                                              mode=mode, w_hat=wh)
+                torch.cuda.synchronize()
+                after = torch.cuda.memory_allocated()
+            finally:
+                gc.enable()
+            assert after == before
             say(f"[noalloc] {recipe} {n_out}x{n_in} {mode}: workspace call {d_ws!r}, static scratch {d_na!r}")
             assert d_na == d_ws
             assert torch.equal(wh, wh_ws)
