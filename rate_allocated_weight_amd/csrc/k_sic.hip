@@ -17,8 +17,10 @@
 //
 // B's diagonal blocks are packed once per factor U (they do not depend on c): column j of a
 // block keeps rows 0 .. 16*(j/16+1)-1, zero from row j on, so that in step j every lane reads
-// its entries unconditionally (a zero leaves finished targets unchanged). Column j = 16a + r
-// starts at 16 (a+1)(8a + r); a block holds 9216 doubles (72 KiB, two workgroups per CU).
+// its entries unconditionally (a zero leaves finished targets unchanged). Columns go in pairs
+// (2m+1, 2m), which share their row count: the pair starts at 16 (a+1)(8a + r) for its even
+// column 2m = 16a + r, and row i of the pair holds the odd column's entry then the even one's,
+// so one 16-byte LDS read serves two steps. A block holds 9216 doubles (72 KiB).
 #include <type_traits>
 
 #include "common.h"
@@ -55,20 +57,26 @@ __device__ __forceinline__ float f32_up(double x) {
   return ((double)f < x) ? __int_as_float(__float_as_int(f) + 1) : f;
 }
 
-// Step J of the in-block recursion (J = 127 ... 0), then the remaining ones. Columns past the
-// end of a ragged last block hold z = 0 and all-zero B entries, so their steps change nothing
-// and need no branch. A column's target is final once its own step has run (later steps only
-// touch columns left of it), so rounding decisions can be checked after the block.
+// Steps 2M+1 and 2M of the in-block recursion (M = 63 ... 0), then the remaining ones. Columns
+// past the end of a ragged last block hold z = 0 and all-zero B entries, so their steps change
+// nothing and need no branch. A column's target is final once its own step has run (later steps
+// only touch columns left of it), so rounding decisions can be checked after the block.
 //
-// The B entries of a step are read from LDS two steps ahead (b0: this step, b1: the next one),
-// and the target the next step rounds is updated first, so the sequential chain per column is
-// round -> broadcast -> one FMA.
-template <int J>
-__device__ __forceinline__ void load_b(double (&b)[8], const double* __restrict__ bl) {
-  if constexpr (J >= 0) {
-    constexpr int a = J >> 4, off = pack_off(J);
+// The B entries of a pair are read from LDS one pair ahead (bo, be: this pair's odd and even
+// column, no, ne: the next pair's), and the target the next step rounds is updated first, so the
+// sequential chain per column is round -> broadcast -> one FMA. bl points at the lane's first
+// entry (two doubles per row and pair).
+template <int M>
+__device__ __forceinline__ void load_pair(double (&bo)[8], double (&be)[8],
+                                          const double* __restrict__ bl) {
+  if constexpr (M >= 0) {
+    constexpr int a = (2 * M) >> 4, off = pack_off(2 * M);
 #pragma unroll
-    for (int sp = 0; sp <= a; ++sp) b[sp] = bl[off + 16 * sp];
+    for (int sp = 0; sp <= a; ++sp) {
+      const double2 v = *reinterpret_cast<const double2*>(bl + off + 32 * sp);
+      bo[sp] = v.x;
+      be[sp] = v.y;
+    }
   }
 }
 
@@ -79,38 +87,45 @@ struct NoHook {
   __device__ __forceinline__ void operator()(T) const {}
 };
 
-template <int J>
-struct Steps {
+// step J with B entries b (column J of the block)
+template <int J, class H>
+__device__ __forceinline__ void sic_step(double (&z)[8], const double (&b)[8], H& hook) {
+  hook(std::integral_constant<int, J>{});
+  constexpr int a = J >> 4, l = J & 15;
+  constexpr int an = (J - 1) >> 4;  // group of the next step's target (a or a - 1)
+  const double qb = bcast_row<l>(rint(z[a]));
+  if constexpr (J > 0) z[an] = fma(-b[an], qb, z[an]);
+#pragma unroll
+  for (int sp = 0; sp <= a; ++sp)
+    if (J == 0 || sp != an) z[sp] = fma(-b[sp], qb, z[sp]);
+}
+
+template <int M>
+struct Pairs {
   template <class H>
   static __device__ __forceinline__ void run(double (&z)[8], const double* __restrict__ bl,
-                                             const double (&b0)[8], const double (&b1)[8], H& hook) {
-    hook(std::integral_constant<int, J>{});
-    constexpr int a = J >> 4, l = J & 15;
-    constexpr int an = (J - 1) >> 4;  // group of the next step's target (a or a - 1)
-    double b2[8];
-    load_b<J - 2>(b2, bl);
-    const double qb = bcast_row<l>(rint(z[a]));
-    if constexpr (J > 0) z[an] = fma(-b0[an], qb, z[an]);
-#pragma unroll
-    for (int sp = 0; sp <= a; ++sp)
-      if (J == 0 || sp != an) z[sp] = fma(-b0[sp], qb, z[sp]);
-    Steps<J - 1>::run(z, bl, b1, b2, hook);
+                                             const double (&bo)[8], const double (&be)[8], H& hook) {
+    double no[8], ne[8];
+    load_pair<M - 1>(no, ne, bl);
+    sic_step<2 * M + 1>(z, bo, hook);
+    sic_step<2 * M>(z, be, hook);
+    Pairs<M - 1>::run(z, bl, no, ne, hook);
   }
 };
 template <>
-struct Steps<-1> {
+struct Pairs<-1> {
   template <class H>
   static __device__ __forceinline__ void run(double (&)[8], const double*, const double (&)[8],
                                              const double (&)[8], H&) {}
 };
 
+// bl: the block's packed B plus 2 * (lane within its DPP row)
 template <class H = NoHook>
 __device__ __forceinline__ void run_block(double (&z)[8], const double* __restrict__ bl,
                                           H&& hook = H{}) {
-  double b0[8], b1[8];
-  load_b<BW - 1>(b0, bl);
-  load_b<BW - 2>(b1, bl);
-  Steps<BW - 1>::run(z, bl, b0, b1, hook);
+  double bo[8], be[8];
+  load_pair<BW / 2 - 1>(bo, be, bl);
+  Pairs<BW / 2 - 1>::run(z, bl, bo, be, hook);
 }
 
 // I8 = the interference G came from the int8 limb product (k_limb.hip): then the leaf also
@@ -242,7 +257,7 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
   for (int s = 0; s < 8; ++s) gin[s] = yv[s] * p.invc - z[s];
   __syncthreads();
 
-  run_block(z, Bs + l16);
+  run_block(z, Bs + 2 * l16);
   if (I8 && GIN) {
     // A rounding decision closer to a boundary than the error bound of the int8 product is
     // first re-checked on its own: the workgroup forms that decision's exact fp64 interference
@@ -339,7 +354,7 @@ __global__ __launch_bounds__(256) void k_sic_leaf(LeafArgs p) {
         z[s] = (active && j < w) ? yv[s] * p.invc - acc[s] : 0.0;
       }
       if (tid == 0) atomicAdd(p.flags + 1, 1);  // count of exact re-derivations
-      run_block(z, Bs + l16);
+      run_block(z, Bs + 2 * l16);
     }
   }
 
@@ -736,7 +751,7 @@ __global__ __launch_bounds__(256) void k_sic_super(LeafArgs p) {
 
     // the lane's offset is made opaque here so that the block's LDS addresses are formed inside
     // the loop (immediate offsets) instead of being hoisted into hundreds of live registers
-    int lb = l16;
+    int lb = 2 * l16;
     asm volatile("" : "+v"(lb));
     run_block(z, Bcur + lb, hook);
 
@@ -920,7 +935,7 @@ __global__ void k_pack_blocks(const double* __restrict__ U, int64_t ldu, int64_t
   const int64_t j0 = blk * BW;
   double v = 0.0;
   if (i < j && j0 + j < n) v = U[(j0 + i) * ldu + j0 + j] * invd[j0 + j];
-  Bpk[blk * PACK + pack_off(j) + i] = v;
+  Bpk[blk * PACK + pack_off(j & ~1) + 2 * i + (1 - (j & 1))] = v;  // odd column first
 }
 
 __global__ void k_prep(const double* U, int64_t ldu, int64_t n, double* invd, int* flags) {
