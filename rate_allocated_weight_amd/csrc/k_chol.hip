@@ -29,15 +29,6 @@ constexpr int NB = 64;
 constexpr int PANEL_WAVES = 8;
 constexpr int RPW = NB / PANEL_WAVES;  // rows per wave
 
-// 1/sqrt(p) to ~1 ulp: hardware estimate refined by two Newton steps
-__device__ __forceinline__ double rsqrt_f64(double p) {
-  double y = __builtin_amdgcn_rsq(p);
-  const double h = 0.5 * p;
-  y = y * fma(-h * y, y, 1.5);
-  y = y * fma(-h * y, y, 1.5);
-  return y;
-}
-
 // Rows published by the owner of a pivot group: the group's rows of U and of the solved slab X,
 // double-buffered by the parity of the group, and the group's first failing pivot (0: none).
 struct PanelLds {
@@ -84,13 +75,18 @@ __device__ __forceinline__ void panel_factor(double (&a)[RPW], double (&sl)[RPW]
       for (int sk = 0; sk < RPW; ++sk) {
         const int k = k0 + sk;
         if (k < nbk) {  // uniform
-          const double p0 = lane_bcast(a[sk], k);
-          const bool ok = (p0 > 0.0) && isfinite(p0);
-          bad = (bad == 0 && !ok) ? k + 1 : bad;
-          const double p = ok ? p0 : 1.0;
-          const double inv = rsqrt_f64(p);
-          const double u = (j == k) ? p * inv : a[sk] * inv;  // U(k, j), j >= k
-          const double x = sl[sk] * inv;                      // X(k, c)
+          const double p = lane_bcast(a[sk], k);
+          const bool ok = (p > 0.0) && isfinite(p);
+          bad = (bad == 0 && !ok) ? k + 1 : bad;  // a failed pivot ends the factorization below
+          // U(k, j) = a(k, j) / sqrt(p) (lane k: sqrt(p)) and X(k, c), with 1/sqrt(p) from the
+          // hardware estimate y0 and two Newton steps y1 = y0 f1, y2 = y1 f2, f = 1.5 - (p/2) y^2;
+          // the last factor is applied to a y1 and sl y1 so that it is not a step of its own
+          const double h = 0.5 * p;
+          const double y0 = __builtin_amdgcn_rsq(p);
+          const double y1 = y0 * fma(-h * y0, y0, 1.5);
+          const double f2 = fma(-h * y1, y1, 1.5);
+          const double u = (a[sk] * y1) * f2;
+          const double x = (sl[sk] * y1) * f2;
           a[sk] = (j >= k) ? u : 0.0;
           sl[sk] = x;
 #pragma unroll
