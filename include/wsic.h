@@ -383,6 +383,9 @@ int wsic_distortion_noalloc(const void* W, int dtype, int64_t n_out, int64_t n_i
  *   WSIC_DBG_CHOL_FUSED     0: Cholesky update and next panel as separate launches (default 1)
  *   WSIC_DBG_LOGITS_GENERIC 1: fp64 VALU logits for bf16 curvature inputs too (default 0)
  *   WSIC_DBG_TRACE          1: one line per SIC pass of the rate controller on stderr (default 0)
+ *   WSIC_DBG_PROBE          0: the secant controller starts from its rate model alone, without
+ *                              the probe pass of several grid scales on sampled rows (default 1);
+ *                              the accepted c then differs within the controller's tolerance
  * wsic_debug_set returns WSIC_E_INVAL for an unknown knob or a value out of range;
  * wsic_debug_get writes the current value to *value (host); wsic_debug_reset restores every
  * default.
@@ -393,7 +396,8 @@ enum wsic_debug_knob {
   WSIC_DBG_GUARD_SCALE = 2,
   WSIC_DBG_CHOL_FUSED = 3,
   WSIC_DBG_LOGITS_GENERIC = 4,
-  WSIC_DBG_TRACE = 5
+  WSIC_DBG_TRACE = 5,
+  WSIC_DBG_PROBE = 6
 };
 int wsic_debug_set(int knob, double value);
 int wsic_debug_get(int knob, double* value);

@@ -29,7 +29,7 @@ D_RESID, D_DIRECT = 0, 1
 WF_AUTO, WF_SECANT, WF_BISECT = 0, 1, 2
 # diagnostic switches (wsic_debug_set)
 DEBUG_KNOBS = {"fp64_product": 0, "super_blocks": 1, "guard_scale": 2, "chol_fused": 3,
-               "logits_generic": 4, "trace": 5}
+               "logits_generic": 4, "trace": 5, "probe": 6}
 
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p

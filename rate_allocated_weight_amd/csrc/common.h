@@ -300,6 +300,14 @@ int launch_row_sqrt(const double* lam, int64_t n, double* s, int* flags, hipStre
 // Y[r, :] *= s[r]
 int launch_scale_rows(double* Y, int64_t n_out, int64_t n_in, int64_t ldy, const double* s,
                       hipStream_t st);
+// the rate controller's probe layer: K groups of S evenly spaced rows of Y, group g scaled by
+// fac.v[g] (S * K <= 65535, S <= n_out, K <= PROBE_MAX)
+constexpr int PROBE_MAX = 8;
+struct ProbeFactors {
+  double v[PROBE_MAX];
+};
+int launch_probe_rows(const double* Y, int64_t ldy, int64_t n_out, int64_t n_in, int S, int K,
+                      const ProbeFactors& fac, double* Yp, int64_t ldp, hipStream_t st);
 int launch_sum_partials(const double* partial, int64_t n, double* out, hipStream_t st);
 
 }  // namespace wsic

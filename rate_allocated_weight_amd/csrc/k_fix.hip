@@ -126,6 +126,16 @@ __global__ void k_scatter_codes(const int32_t* __restrict__ ql, int64_t ldql,
   }
 }
 
+// Rows of the rate controller's probe layer: row g * S + i is row r_i = floor((2 i + 1) n_out /
+// (2 S)) of Y times fac.v[g] (the probe's grid scale c_g enters as Y / c_g = (Y c / c_g) / c).
+__global__ void k_probe_rows(const double* __restrict__ Y, int64_t ldy, int64_t n_out, int64_t n_in,
+                             int S, ProbeFactors fac, double* __restrict__ Yp, int64_t ldp) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int v = blockIdx.y, g = v / S, i = v - g * S;
+  const int64_t r = ((2 * (int64_t)i + 1) * n_out) / (2 * (int64_t)S);
+  if (j < n_in) Yp[(int64_t)v * ldp + j] = Y[r * ldy + j] * fac.v[g];
+}
+
 }  // namespace
 
 int launch_lmmse_rows(const double* Y, int64_t ldy, const float* R, int64_t ldr, const double* U,
@@ -175,6 +185,15 @@ int launch_scatter_codes(const int32_t* ql, int64_t ldql, const int32_t* pos, in
     WSIC_LAUNCH("scatter", 12.0 * (double)nr * n_in, st, k_scatter_codes, dim3(gx, (unsigned)nr),
                 dim3(256), 0, ql + r0 * ldql, ldql, pos, n_in, q + r0 * ldq, ldq);
   }
+  return WSIC_OK;
+}
+
+int launch_probe_rows(const double* Y, int64_t ldy, int64_t n_out, int64_t n_in, int S, int K,
+                      const ProbeFactors& fac, double* Yp, int64_t ldp, hipStream_t st) {
+  if (S <= 0 || K <= 0 || K > PROBE_MAX || (int64_t)S * K > 65535 || S > n_out) return WSIC_E_INVAL;
+  const unsigned gx = (unsigned)((n_in + 255) / 256);
+  WSIC_LAUNCH("probe_rows", 16.0 * (double)S * K * n_in, st, k_probe_rows,
+              dim3(gx, (unsigned)(S * K)), dim3(256), 0, Y, ldy, n_out, n_in, S, fac, Yp, ldp);
   return WSIC_OK;
 }
 

@@ -235,6 +235,15 @@ ColHistWs carve_colhist(Carve& cv, int64_t n_in) {
   return h;
 }
 
+// The secant controller's probe: PROBE_K grid scales tried at once on a layer of PROBE_K groups
+// of probe_rows(n_out) evenly spaced rows (0: no probe for this shape). It reuses the pass
+// buffers of the real layer, so it needs at most n_out rows.
+constexpr int PROBE_K = PROBE_MAX;
+int probe_rows(int64_t n_out) {
+  if (n_out < 64 * PROBE_K) return 0;
+  return (int)std::min<int64_t>(512, n_out / PROBE_K);
+}
+
 struct WfWs {
   SicWs sic;
   int32_t* codes2;
@@ -243,7 +252,11 @@ struct WfWs {
   double* diag;
   HistWs hist;
   ColHistWs col;
+  double* Yp;                  // the probe layer's Y (PROBE_K * probe_rows x n_in)
+  unsigned long long* pbins;   // one histogram (and its overflow count) per probe group
+  EntropyResult* pres;
 };
+constexpr size_t PROBE_BIN_STRIDE = HIST_BINS + 32;
 WfWs carve_wf(Carve& cv, int64_t n_out, int64_t n_in) {
   WfWs w;
   w.sic = carve_sic(cv, n_out, n_in);
@@ -253,6 +266,10 @@ WfWs carve_wf(Carve& cv, int64_t n_out, int64_t n_in) {
   w.diag = cv.take<double>((size_t)n_in);
   w.hist = carve_hist(cv);
   w.col = carve_colhist(cv, n_in);
+  const int S = probe_rows(n_out);
+  w.Yp = S ? cv.take<double>((size_t)PROBE_K * S * n_in) : nullptr;
+  w.pbins = S ? cv.take<unsigned long long>(PROBE_K * PROBE_BIN_STRIDE) : nullptr;
+  w.pres = S ? cv.take<EntropyResult>(PROBE_K) : nullptr;
   return w;
 }
 
@@ -598,6 +615,7 @@ struct DebugKnobs {
   std::atomic<bool> chol_fused{true};
   std::atomic<bool> logits_generic{false};
   std::atomic<bool> trace{false};
+  std::atomic<bool> probe{true};
 };
 DebugKnobs g_dbg;
 
@@ -949,6 +967,7 @@ int wsic_debug_set(int knob, double v) {
     case WSIC_DBG_CHOL_FUSED: g_dbg.chol_fused = on; return WSIC_OK;
     case WSIC_DBG_LOGITS_GENERIC: g_dbg.logits_generic = on; return WSIC_OK;
     case WSIC_DBG_TRACE: g_dbg.trace = on; return WSIC_OK;
+    case WSIC_DBG_PROBE: g_dbg.probe = on; return WSIC_OK;
     default:
       wsic::set_error("debug_set: unknown knob %d", knob);
       return WSIC_E_INVAL;
@@ -969,6 +988,7 @@ int wsic_debug_get(int knob, double* v) {
     case WSIC_DBG_CHOL_FUSED: *v = g_dbg.chol_fused.load(); return WSIC_OK;
     case WSIC_DBG_LOGITS_GENERIC: *v = g_dbg.logits_generic.load(); return WSIC_OK;
     case WSIC_DBG_TRACE: *v = g_dbg.trace.load(); return WSIC_OK;
+    case WSIC_DBG_PROBE: *v = g_dbg.probe.load(); return WSIC_OK;
     default:
       wsic::set_error("debug_get: unknown knob %d", knob);
       return WSIC_E_INVAL;
@@ -983,6 +1003,7 @@ void wsic_debug_reset(void) {
   g_dbg.chol_fused = true;
   g_dbg.logits_generic = false;
   g_dbg.trace = false;
+  g_dbg.probe = true;
 }
 
 const char* wsic_last_error(void) { return wsic::last_error(); }
@@ -1324,6 +1345,71 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
       constexpr double SLOPE_DX = 1.0 / 1024;
       const double Rt = R - 0.5 * o.rate_tol;
       auto accept = [&]() { return have_hi && h_hi > R - o.rate_tol; };
+      // Probe (pooled rate): one pass over PROBE_K copies of S evenly spaced rows, copy g at the
+      // grid scale c0 2^off[g] (rows are independent, so each copy quantizes exactly as its rows
+      // would in the whole layer at that scale). The PROBE_K rates measure H(log2 c) around the
+      // model's start; the first full pass goes to their crossing of Rt, and their local slope
+      // replaces the model's. The sample's rate differs from the layer's by a near-constant
+      // offset (~1e-3 bit at 512 x 4096 codes), which the first full pass measures and the
+      // slope then removes.
+      double probe_slope = 0.0;  // 0: no probe
+      const int S = probe_rows(n_out);
+      if (!cols && S > 0 && wf.Yp && g_dbg.probe.load() && passes < o.max_passes) {
+        static const double off[PROBE_K] = {-0.16, -0.08, -0.04, -0.015, 0.015, 0.04, 0.08, 0.16};
+        const double x0 = std::log2(c0);
+        ProbeFactors fac{};
+        for (int g = 0; g < PROBE_K; ++g) fac.v[g] = std::exp2(-off[g]);  // Y / c_g = (Y fac) / c0
+        ++passes;
+        WSIC_TRY(launch_probe_rows(x.ws.Y, n_in, n_out, n_in, S, PROBE_K, fac, wf.Yp, n_in, st));
+        SicCtx xp = x;  // the probe layer shares U's operands and the pass buffers (S K <= n_out)
+        xp.n_out = (int64_t)PROBE_K * S;
+        xp.ws.Y = wf.Yp;
+        WSIC_TRY(sic_pass_once(xp, c0, wf.codes2, n_in, nullptr, 0));
+        WSIC_TRY(launch_fill_zero(wf.pbins, PROBE_K * PROBE_BIN_STRIDE * sizeof(unsigned long long),
+                                  st));
+        for (int g = 0; g < PROBE_K; ++g) {
+          unsigned long long* bins = wf.pbins + g * PROBE_BIN_STRIDE;
+          unsigned int* novf = reinterpret_cast<unsigned int*>(bins + HIST_BINS);
+          WSIC_TRY(launch_hist(wf.codes2 + (size_t)g * S * n_in, S, n_in, n_in, bins, wf.hist.ovf,
+                               novf, st));
+          WSIC_TRY(launch_entropy_reduce(bins, novf, g == 0 ? x.ws.pflags : nullptr, wf.pres + g,
+                                         st));
+        }
+        EntropyResult pr[PROBE_K];
+        const ReadPiece rp{pr, wf.pres, sizeof pr};
+        WSIC_TRY(read_back(&rp, 1, st));
+        // a row whose list of large codes overflowed, or codes beyond the histogram's window:
+        // the probe is dropped (the full passes handle both exactly)
+        bool ok = !(pr[0].flags & FLAG_OVERFLOW_LIST);
+        if (ok) WSIC_TRY(flags_status(pr[0].flags, "waterfill"));
+        double xg[PROBE_K], hg[PROBE_K];
+        const double Np = (double)S * (double)n_in;
+        for (int g = 0; g < PROBE_K; ++g) {
+          ok = ok && pr[g].ovf_count == 0;
+          xg[g] = x0 + off[g];
+          hg[g] = std::log2(Np) - pr[g].sum_nlogn / Np;
+        }
+        // the crossing of Rt on the piecewise-linear H(x) through the probes (H falls with x);
+        // outside the probed range the end segment is extended
+        int k = -1;
+        for (int g = 0; g + 1 < PROBE_K && k < 0; ++g)
+          if (hg[g] >= Rt && hg[g + 1] <= Rt) k = g;
+        if (k < 0) k = (hg[PROBE_K - 1] > Rt) ? PROBE_K - 2 : 0;
+        const double sl = (hg[k + 1] - hg[k]) / (xg[k + 1] - xg[k]);
+        if (ok && sl < -0.25 && sl > -4.0) {
+          const double x1 = std::min(x0 + 2.0, std::max(x0 - 2.0, xg[k] + (Rt - hg[k]) / sl));
+          if (std::isfinite(x1)) {
+            c0 = std::exp2(x1);
+            probe_slope = sl;
+          }
+        }
+        if (trace)
+          std::fprintf(stderr,
+                       "wsic waterfill pass %d: probe of %d scales on %d rows, H(c0 2^%.3f) = "
+                       "%.6f ... H(c0 2^%.3f) = %.6f, slope %.5f, next c=%.17g%s\n",
+                       passes, PROBE_K, S, off[0], hg[0], off[PROBE_K - 1], hg[PROBE_K - 1], sl,
+                       c0, probe_slope != 0.0 ? "" : " (probe not used)");
+      }
       std::vector<double> xs, hs;
       double xb = std::log2(c0), hb = 0.0;
       int b = free_buf();
@@ -1341,8 +1427,8 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
           xh = std::log2(c_hi);
           if (xh - xl <= o.bracket_log2) break;
         }
-        double slope = -1.0;
-        if (xs.size() == 1 && !gq.empty()) {  // one evaluation: the rate model's local slope
+        double slope = probe_slope != 0.0 ? probe_slope : -1.0;
+        if (xs.size() == 1 && !gq.empty() && probe_slope == 0.0) {  // the rate model's slope
           const double dx = std::min(2.0, std::max(-2.0, hb - Rt));  // the step at slope -1
           if (std::fabs(dx) > 1e-9) {
             const double sl = (gauss_mix_entropy(gq, std::exp2(xb + dx), !cols) -
@@ -1350,8 +1436,11 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
             if (sl < -0.25 && sl > -4.0) slope = sl;
           }
         }
-        for (size_t i = xs.size() - 1; i-- > 0;) {  // the latest evaluation far enough back
-          if (std::fabs(xb - xs[i]) >= SLOPE_DX) {
+        // the latest evaluation far enough back (after a probe, whose slope rests on far more
+        // codes than two nearby full passes resolve, only one much farther back)
+        const double min_dx = probe_slope != 0.0 ? 1.0 / 64 : SLOPE_DX;
+        for (size_t i = xs.size() - 1; i-- > 0;) {
+          if (std::fabs(xb - xs[i]) >= min_dx) {
             const double sl = (hb - hs[i]) / (xb - xs[i]);
             if (sl < -0.25 && sl > -4.0) slope = sl;
             break;
