@@ -152,7 +152,10 @@ typedef struct wsic_wf_opts {
                           bracket_log2 -- the reference search, whose sequence of grid
                           scales is fully determined by the code entropies it sees;
                           WSIC_WF_SECANT: safeguarded regula falsi (Illinois) on log2 c,
-                          far fewer passes once H(c) is smooth (large layers);
+                          far fewer passes once H(c) is smooth (large layers); on layers
+                          of at least 16384 rows its first pass is a probe of 8 grid scales
+                          on 512 evenly spaced rows (counted in passes_out), which gives the
+                          start and the slope;
                           WSIC_WF_AUTO (default): BISECT below WSIC_WF_AUTO_PARAMS weights,
                           where H(c) moves in visible non-monotone steps, else SECANT     */
   double c_init;       /* > 0: first grid scale tried; 0: high-rate estimate
@@ -384,8 +387,9 @@ int wsic_distortion_noalloc(const void* W, int dtype, int64_t n_out, int64_t n_i
  *   WSIC_DBG_LOGITS_GENERIC 1: fp64 VALU logits for bf16 curvature inputs too (default 0)
  *   WSIC_DBG_TRACE          1: one line per SIC pass of the rate controller on stderr (default 0)
  *   WSIC_DBG_PROBE          0: the secant controller starts from its rate model alone, without
- *                              the probe pass of several grid scales on sampled rows (default 1);
- *                              the accepted c then differs within the controller's tolerance
+ *                              the probe pass (8 grid scales on 512 sampled rows, layers of at
+ *                              least 16384 rows; default 1); the accepted c then differs within
+ *                              the controller's tolerance
  * wsic_debug_set returns WSIC_E_INVAL for an unknown knob or a value out of range;
  * wsic_debug_get writes the current value to *value (host); wsic_debug_reset restores every
  * default.

@@ -237,11 +237,15 @@ ColHistWs carve_colhist(Carve& cv, int64_t n_in) {
 
 // The secant controller's probe: PROBE_K grid scales tried at once on a layer of PROBE_K groups
 // of probe_rows(n_out) evenly spaced rows (0: no probe for this shape). It reuses the pass
-// buffers of the real layer, so it needs at most n_out rows.
+// buffers of the real layer, so it needs at most n_out rows. A pass is bound by the latency of
+// its workgroups (16 rows each, one per CU) up to 4096 rows, so the probe's 4096 rows cost as
+// much as a whole pass of a layer that small; it runs only where it costs at most a quarter of
+// a pass. (On 4096- to 11008-row layers, measured with it: 34 passes over 6 targets against 32.)
 constexpr int PROBE_K = PROBE_MAX;
+constexpr int64_t PROBE_MIN_ROWS = 16384;
 int probe_rows(int64_t n_out) {
-  if (n_out < 64 * PROBE_K) return 0;
-  return (int)std::min<int64_t>(512, n_out / PROBE_K);
+  if (n_out < PROBE_MIN_ROWS) return 0;
+  return 512;
 }
 
 struct WfWs {

@@ -1,0 +1,75 @@
+"""The secant rate controller with its probe pass (layers of at least 16384 rows): a first pass
+over 8 copies of 512 evenly spaced rows, each copy at its own grid scale, gives the start and
+the slope of H(log2 c). Whatever the probe says, the result must meet the same bar as without
+it: the rate inside the acceptance window, c and the rate next to the reference search's
+(bisection, which replays the oracle's sequence), and the oracle's codes at the returned c on
+every row (WaterSIC page, Sommario tecnico §2 items 1-2)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import DEV, RATE_TOL, REL_TOL, assert_codes_parity, say, w_tensor
+from rate_allocated_weight_amd import _lib as lib
+from rate_allocated_weight_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+WINDOW = 8e-5  # the controller's default acceptance window below the target
+
+
+@pytest.fixture(scope="module")
+def layer_on_device():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    layer = workloads.make_layer("spiked", 16384, 256, 1024, seed=3, dtype="bf16", rank=16,
+                                 name="spiked_16384x256")
+    L, info = oracle.cholesky_lower(oracle.covariance(layer.x_chunks))
+    assert info == 0
+    U = torch.from_numpy(np.ascontiguousarray(L.T)).to(DEV)
+    return layer, L, U
+
+
+@pytest.mark.parametrize("R", [1.5, 3.0])
+def test_probe_secant_meets_the_bar(layer_on_device, capfd, R):
+    layer, L, U = layer_on_device
+    W = w_tensor(layer)
+    try:
+        lib.debug_set("trace", 1)
+        wf = lib.waterfill(W, U, R, mode="secant")
+    finally:
+        lib.debug_reset()
+    err = capfd.readouterr().err
+    assert "probe of 8 scales on 512 rows" in err, "the probe pass did not run"
+    assert "(probe not used)" not in err
+    lib.debug_set("probe", 0)
+    try:
+        plain = lib.waterfill(W, U, R, mode="secant")
+    finally:
+        lib.debug_reset()
+    ref = lib.waterfill(W, U, R, mode="bisect")
+    say(f"[probe] {layer.name} R={R}: probe c={wf['c']:.9g} H={wf['rate']:.7f} passes={wf['passes']}; "
+        f"plain c={plain['c']:.9g} H={plain['rate']:.7f} passes={plain['passes']}; "
+        f"bisect c={ref['c']:.9g} H={ref['rate']:.7f} passes={ref['passes']}")
+    for r in (wf, plain):
+        assert R - WINDOW < r["rate"] <= R
+        assert abs(r["rate"] - ref["rate"]) <= RATE_TOL
+        assert abs(r["c"] / ref["c"] - 1.0) <= REL_TOL
+    sic = oracle.sic_quantize(layer.w, L, wf["c"])
+    assert_codes_parity(wf["codes"].cpu().numpy(), sic, label=f"probe R={R}")
+    assert wf["rate"] == pytest.approx(oracle.entropy_bits(sic["q"]), abs=1e-12)
+
+
+def test_no_probe_below_16384_rows(capfd):
+    """Layers under 16384 rows run the plain secant (the probe would cost a whole pass)."""
+    layer = workloads.make_layer("spiked", 4096, 128, 600, seed=4, dtype="bf16", rank=8)
+    L, info = oracle.cholesky_lower(oracle.covariance(layer.x_chunks))
+    assert info == 0
+    U = torch.from_numpy(np.ascontiguousarray(L.T)).to(DEV)
+    try:
+        lib.debug_set("trace", 1)
+        wf = lib.waterfill(w_tensor(layer), U, 2.0, mode="secant")
+    finally:
+        lib.debug_reset()
+    err = capfd.readouterr().err
+    assert "probe" not in err
+    assert 2.0 - WINDOW < wf["rate"] <= 2.0
