@@ -210,7 +210,7 @@ int launch_gemm_i8(int64_t M, int64_t N, int64_t K, const int8_t* A8, int64_t ld
                    int64_t ldd, int64_t plane, const double* escale, double* C, int64_t ldc,
                    double beta, hipStream_t st);
 int colstats_doubles(int64_t n_out, int64_t n_in);
-// column variances of diag(rs) W (rs nullable: W itself)
+// column variances of diag(rs) W (rs nullable: W itself); part (colstats_doubles, 16-byte aligned)
 int launch_colstats(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
                     double* part, double* colvar, hipStream_t st, const double* rs = nullptr);
 

@@ -53,26 +53,39 @@ __global__ __launch_bounds__(256) void k_row_scale(const double* __restrict__ U,
 }
 
 // Digit planes: D[l][j][k] for k > j, zero elsewhere (including the padding k in [n, ldd)).
+// Four adjacent k per thread (ldd is a multiple of 128), one 4-byte store per plane; x - d is a
+// multiple of 256, so the shift is the exact division.
 __global__ void k_limb_digits(const double* __restrict__ U, int64_t ldu, int64_t n,
                               const double* __restrict__ invd, const double* __restrict__ escale,
                               int8_t* __restrict__ D, int64_t ldd) {
   const int64_t j = blockIdx.y;
-  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= ldd) return;
-  long long x = 0;
-  if (k > j && k < n) {
-    // B_jk * 2^(P - e_j): exact power-of-two scaling, then one rounding
-    const double v = (U[j * ldu + k] * invd[k]) / escale[j];
-    x = (long long)rint(v);
+  const int64_t k0 = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (k0 >= ldd) return;
+  const double ies = 1.0 / escale[j];  // exact: escale is a power of two
+  uint32_t w[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l) w[l] = 0u;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int64_t k = k0 + c;
+    long long x = 0;
+    if (k > j && k < n) {
+      // B_jk * 2^(P - e_j): exact power-of-two scaling, then one rounding
+      const double v = (U[j * ldu + k] * invd[k]) * ies;
+      x = (long long)rint(v);
+    }
+#pragma unroll
+    for (int l = NL - 1; l >= 0; --l) {
+      long long d = x & 255;  // balanced digit in [-128, 127]
+      if (d >= 128) d -= 256;
+      x = (x - d) >> 8;
+      w[l] |= ((uint32_t)(d & 255)) << (8 * c);
+    }
   }
   const int64_t plane = n * ldd;
 #pragma unroll
-  for (int l = NL - 1; l >= 0; --l) {
-    long long d = x & 255;  // balanced digit in [-128, 127]
-    if (d >= 128) d -= 256;
-    x = (x - d) / 256;
-    D[(int64_t)l * plane + j * ldd + k] = (int8_t)d;
-  }
+  for (int l = 0; l < NL; ++l)
+    *reinterpret_cast<uint32_t*>(D + (int64_t)l * plane + j * ldd + k0) = w[l];
 }
 
 // C[M x N] (+)= F, F(m, n) = escale[n] * sum_l 256^(NL-1-l) sum_k A8(m,k) D_l(n,k).
@@ -250,8 +263,12 @@ int launch_limb_pack(const double* U, int64_t ldu, int64_t n, const double* invd
                      double* bscale, int8_t* D, int64_t ldd, hipStream_t st) {
   WSIC_LAUNCH("limb_scale", 8.0 * n * n / 2, st, k_row_scale, dim3((unsigned)n), dim3(256), 0, U,
               ldu, n, invd, escale, bscale);
+  if (ldd % 4 != 0 || (((uintptr_t)D) & 3) != 0) {
+    set_error("internal: digit plane layout");
+    return WSIC_E_INVAL;
+  }
   WSIC_LAUNCH("limb_digits", (double)n * ldd * (4.0 + NL), st, k_limb_digits,
-              dim3((unsigned)((ldd + 255) / 256), (unsigned)n), dim3(256), 0, U, ldu, n, invd,
+              dim3((unsigned)((ldd / 4 + 255) / 256), (unsigned)n), dim3(256), 0, U, ldu, n, invd,
               escale, D, ldd);
   return WSIC_OK;
 }

@@ -21,6 +21,7 @@
 // (2m+1, 2m), which share their row count: the pair starts at 16 (a+1)(8a + r) for its even
 // column 2m = 16a + r, and row i of the pair holds the odd column's entry then the even one's,
 // so one 16-byte LDS read serves two steps. A block holds 9216 doubles (72 KiB).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -971,46 +972,124 @@ __device__ __forceinline__ float elem<uint16_t>(const uint16_t* p, int64_t i) {
   return bf16_to_f32(p[i]);
 }
 
+// a 32-bit word of two bf16 / one fp32 holds a NaN or Inf (all exponent bits set)
 template <typename T>
-__global__ void k_check_finite(const T* W, int64_t n_out, int64_t n_in, int64_t ldw, int* flags) {
-  int bad = 0;
-  const int64_t total = n_out * n_in;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = e / n_in, j = e % n_in;
-    if (!isfinite(elem<T>(W, r * ldw + j))) bad = 1;
+__device__ __forceinline__ bool word_nonfinite(uint32_t w);
+template <>
+__device__ __forceinline__ bool word_nonfinite<uint16_t>(uint32_t w) {
+  return (w & 0x7F80u) == 0x7F80u || (w & 0x7F800000u) == 0x7F800000u;
+}
+template <>
+__device__ __forceinline__ bool word_nonfinite<float>(uint32_t w) {
+  return (w & 0x7F800000u) == 0x7F800000u;
+}
+
+// Rows over the y dimension of the grid, each row's 16-byte chunks over x (VEC: rows start
+// 16-byte aligned, checked by the launcher), the row's tail element by element.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void k_check_finite(const T* W, int64_t n_out, int64_t n_in,
+                                                      int64_t ldw, int* flags) {
+  constexpr int E = 16 / (int)sizeof(T);
+  bool bad = false;
+  const int64_t x0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t xs = (int64_t)gridDim.x * blockDim.x;
+  const int64_t nv = VEC ? n_in / E : 0;
+  for (int64_t r = blockIdx.y; r < n_out; r += gridDim.y) {
+    const T* wr = W + r * ldw;
+    if (VEC) {
+      const uint4* v4 = reinterpret_cast<const uint4*>(wr);
+      for (int64_t c = x0; c < nv; c += xs) {
+        const uint4 v = v4[c];
+        bad = bad || word_nonfinite<T>(v.x) || word_nonfinite<T>(v.y) ||
+              word_nonfinite<T>(v.z) || word_nonfinite<T>(v.w);
+      }
+    }
+    for (int64_t j = nv * E + x0; j < n_in; j += xs)
+      if (!isfinite(elem<T>(wr, j))) bad = true;
   }
   if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flags, FLAG_NONFINITE);
 }
 
-// Column sums of W and W^2 over a slab of COLSTAT_ROWS rows: 64 columns x 4 row lanes per
-// workgroup, one partial pair per (slab, column); k_colstats_finish reduces the slabs in order.
-constexpr int COLSTAT_ROWS = 256;
+// Column sums of W and W^2 over a slab of COLSTAT_ROWS rows: 256 columns (4 adjacent ones per
+// thread, one 8- or 16-byte load per row when VEC) x 4 row lanes per workgroup, one partial pair
+// per (slab, column); k_colstats_finish reduces the slabs in order. Every column's terms are
+// summed in the same order whatever the load width.
+constexpr int COLSTAT_ROWS = 64;
 template <typename T>
+struct Quad;
+template <>
+struct Quad<uint16_t> {
+  typedef uint2 type;
+  static __device__ __forceinline__ void get(const uint16_t* p, float (&v)[4]) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(q.x << 16);
+    v[1] = __uint_as_float(q.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(q.y << 16);
+    v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+  }
+};
+template <>
+struct Quad<float> {
+  static __device__ __forceinline__ void get(const float* p, float (&v)[4]) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x;
+    v[1] = q.y;
+    v[2] = q.z;
+    v[3] = q.w;
+  }
+};
+template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void k_colstats(const T* W, int64_t n_out, int64_t n_in,
                                                   int64_t ldw, double* part,
                                                   const double* __restrict__ rs) {
-  __shared__ double s1[4][64], s2[4][64];
+  __shared__ double s1[4][256], s2[4][256];
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const int64_t j = (int64_t)blockIdx.x * 64 + tx;
+  const int64_t j = (int64_t)blockIdx.x * 256 + 4 * tx;
   const int64_t r0 = (int64_t)blockIdx.y * COLSTAT_ROWS;
-  double a = 0.0, b = 0.0;
-  if (j < n_in) {
-    const int64_t r1 = (r0 + COLSTAT_ROWS < n_out) ? r0 + COLSTAT_ROWS : n_out;
+  double a[4] = {0.0, 0.0, 0.0, 0.0}, b[4] = {0.0, 0.0, 0.0, 0.0};
+  const int64_t r1 = (r0 + COLSTAT_ROWS < n_out) ? r0 + COLSTAT_ROWS : n_out;
+  if (VEC && j + 3 < n_in) {
     for (int64_t r = r0 + ty; r < r1; r += 4) {
-      const double v = rs ? (double)elem<T>(W, r * ldw + j) * rs[r] : (double)elem<T>(W, r * ldw + j);
-      a += v;
-      b = fma(v, v, b);
+      float v[4];
+      Quad<T>::get(W + r * ldw + j, v);
+      const double sc = rs ? rs[r] : 1.0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const double x = rs ? (double)v[c] * sc : (double)v[c];
+        a[c] += x;
+        b[c] = fma(x, x, b[c]);
+      }
+    }
+  } else {
+    for (int64_t r = r0 + ty; r < r1; r += 4) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (j + c < n_in) {
+          const double x = rs ? (double)elem<T>(W, r * ldw + j + c) * rs[r]
+                              : (double)elem<T>(W, r * ldw + j + c);
+          a[c] += x;
+          b[c] = fma(x, x, b[c]);
+        }
+      }
     }
   }
-  s1[ty][tx] = a;
-  s2[ty][tx] = b;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    s1[ty][4 * tx + c] = a[c];
+    s2[ty][4 * tx + c] = b[c];
+  }
   __syncthreads();
-  if (ty == 0 && j < n_in) {
-    const double sa = (s1[0][tx] + s1[1][tx]) + (s1[2][tx] + s1[3][tx]);
-    const double sb = (s2[0][tx] + s2[1][tx]) + (s2[2][tx] + s2[3][tx]);
-    part[((int64_t)blockIdx.y * n_in + j) * 2 + 0] = sa;
-    part[((int64_t)blockIdx.y * n_in + j) * 2 + 1] = sb;
+  if (ty == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int t = 4 * tx + c;
+      if (j + c < n_in) {
+        const double sa = (s1[0][t] + s1[1][t]) + (s1[2][t] + s1[3][t]);
+        const double sb = (s2[0][t] + s2[1][t]) + (s2[2][t] + s2[3][t]);
+        part[((int64_t)blockIdx.y * n_in + j + c) * 2 + 0] = sa;
+        part[((int64_t)blockIdx.y * n_in + j + c) * 2 + 1] = sb;
+      }
+    }
   }
 }
 
@@ -1018,10 +1097,24 @@ __global__ void k_colstats_finish(const double* part, int64_t n_out, int64_t n_i
                                   double* colvar) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n_in) return;
+  // slabs in order, their loads issued eight at a time
   double a = 0.0, b = 0.0;
-  for (int s = 0; s < nslab; ++s) {
-    a += part[((int64_t)s * n_in + j) * 2 + 0];
-    b += part[((int64_t)s * n_in + j) * 2 + 1];
+  const double2* p2 = reinterpret_cast<const double2*>(part) + j;
+  int s = 0;
+  for (; s + 8 <= nslab; s += 8) {
+    double2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p2[(int64_t)(s + u) * n_in];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a += v[u].x;
+      b += v[u].y;
+    }
+  }
+  for (; s < nslab; ++s) {
+    const double2 v = p2[(int64_t)s * n_in];
+    a += v.x;
+    b += v.y;
   }
   const double mean = a / (double)n_out;
   const double v = b / (double)n_out - mean * mean;
@@ -1125,31 +1218,59 @@ int launch_delta(const double* U, int64_t ldu, int64_t n, double c, double* delt
 
 int launch_check_finite(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
                         int* flags, hipStream_t st) {
-  const int64_t total = n_out * n_in;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  if (blocks < 1) blocks = 1;
-  const double work = (double)total * (dtype == WSIC_BF16 ? 2.0 : 4.0);
-  if (dtype == WSIC_BF16)
-    WSIC_LAUNCH("check_finite", work, st, k_check_finite<uint16_t>, dim3((unsigned)blocks),
-                dim3(256), 0, (const uint16_t*)W, n_out, n_in, ldw, flags);
-  else
-    WSIC_LAUNCH("check_finite", work, st, k_check_finite<float>, dim3((unsigned)blocks), dim3(256),
-                0, (const float*)W, n_out, n_in, ldw, flags);
+  if (n_out <= 0 || n_in <= 0) return WSIC_OK;
+  const int64_t esz = dtype == WSIC_BF16 ? 2 : 4;
+  const bool vec = (((uintptr_t)W) & 15) == 0 && (ldw * esz) % 16 == 0;
+  const int64_t per_row = vec ? (n_in * esz + 15) / 16 : n_in;  // work items of a row
+  const int64_t gx = std::min<int64_t>(std::max<int64_t>((per_row + 255) / 256, 1), 64);
+  const int64_t gy = std::min<int64_t>(std::max<int64_t>(2048 / gx, 1), std::min<int64_t>(n_out, 65535));
+  const dim3 grid((unsigned)gx, (unsigned)gy);
+  const double work = (double)n_out * n_in * esz;
+  if (dtype == WSIC_BF16) {
+    if (vec)
+      WSIC_LAUNCH("check_finite", work, st, (k_check_finite<uint16_t, true>), grid, dim3(256), 0,
+                  (const uint16_t*)W, n_out, n_in, ldw, flags);
+    else
+      WSIC_LAUNCH("check_finite", work, st, (k_check_finite<uint16_t, false>), grid, dim3(256), 0,
+                  (const uint16_t*)W, n_out, n_in, ldw, flags);
+  } else {
+    if (vec)
+      WSIC_LAUNCH("check_finite", work, st, (k_check_finite<float, true>), grid, dim3(256), 0,
+                  (const float*)W, n_out, n_in, ldw, flags);
+    else
+      WSIC_LAUNCH("check_finite", work, st, (k_check_finite<float, false>), grid, dim3(256), 0,
+                  (const float*)W, n_out, n_in, ldw, flags);
+  }
   return WSIC_OK;
 }
 
 int launch_colstats(const void* W, int dtype, int64_t n_out, int64_t n_in, int64_t ldw,
                     double* part, double* colvar, hipStream_t st, const double* rs) {
-  const unsigned gx = (unsigned)((n_in + 63) / 64);
+  if ((((uintptr_t)part) & 15) != 0) {
+    set_error("internal: column partial sums not 16-byte aligned");
+    return WSIC_E_INVAL;
+  }
+  const unsigned gx = (unsigned)((n_in + 255) / 256);
   const unsigned gy = (unsigned)((n_out + COLSTAT_ROWS - 1) / COLSTAT_ROWS);
-  const double work = (double)n_out * n_in * (dtype == WSIC_BF16 ? 2.0 : 4.0);
-  if (dtype == WSIC_BF16)
-    WSIC_LAUNCH("colstats", work, st, k_colstats<uint16_t>, dim3(gx, gy), dim3(256), 0,
-                (const uint16_t*)W, n_out, n_in, ldw, part, rs);
-  else
-    WSIC_LAUNCH("colstats", work, st, k_colstats<float>, dim3(gx, gy), dim3(256), 0,
-                (const float*)W, n_out, n_in, ldw, part, rs);
+  const int64_t esz = dtype == WSIC_BF16 ? 2 : 4;
+  // 4-column loads need every row start aligned to 4 elements
+  const bool vec = (((uintptr_t)W) & (4 * esz - 1)) == 0 && ldw % 4 == 0;
+  const double work = (double)n_out * n_in * esz;
+  if (dtype == WSIC_BF16) {
+    if (vec)
+      WSIC_LAUNCH("colstats", work, st, (k_colstats<uint16_t, true>), dim3(gx, gy), dim3(256), 0,
+                  (const uint16_t*)W, n_out, n_in, ldw, part, rs);
+    else
+      WSIC_LAUNCH("colstats", work, st, (k_colstats<uint16_t, false>), dim3(gx, gy), dim3(256), 0,
+                  (const uint16_t*)W, n_out, n_in, ldw, part, rs);
+  } else {
+    if (vec)
+      WSIC_LAUNCH("colstats", work, st, (k_colstats<float, true>), dim3(gx, gy), dim3(256), 0,
+                  (const float*)W, n_out, n_in, ldw, part, rs);
+    else
+      WSIC_LAUNCH("colstats", work, st, (k_colstats<float, false>), dim3(gx, gy), dim3(256), 0,
+                  (const float*)W, n_out, n_in, ldw, part, rs);
+  }
   WSIC_LAUNCH("colstats", 16.0 * gy * n_in, st, k_colstats_finish,
               dim3((unsigned)((n_in + 255) / 256)), dim3(256), 0, part, n_out, n_in, (int)gy, colvar);
   return WSIC_OK;

@@ -266,7 +266,8 @@ WfWs carve_wf(Carve& cv, int64_t n_out, int64_t n_in) {
   w.sic = carve_sic(cv, n_out, n_in);
   w.codes2 = cv.take<int32_t>((size_t)n_out * n_in);
   w.resid2 = cv.take<float>((size_t)n_out * n_in);
-  w.colvar = cv.take<double>((size_t)colstats_doubles(n_out, n_in) + n_in);
+  // column variances (n_in), then the partial sums from an even offset (16-byte aligned)
+  w.colvar = cv.take<double>((size_t)colstats_doubles(n_out, n_in) + n_in + 1);
   w.diag = cv.take<double>((size_t)n_in);
   w.hist = carve_hist(cv);
   w.col = carve_colhist(cv, n_in);
@@ -1213,7 +1214,8 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
     std::vector<double> gq;  // quantiles of std(W_:,j) U_jj for the secant's rate model
     int setup_flags = 0;
     if (!(c0 > 0.0)) {
-      WSIC_TRY(launch_colstats(W, dtype, n_out, n_in, ldw, wf.colvar + n_in, wf.colvar, st, x.rs));
+      WSIC_TRY(launch_colstats(W, dtype, n_out, n_in, ldw, wf.colvar + (n_in + 1) / 2 * 2, wf.colvar,
+                               st, x.rs));
       WSIC_TRY(launch_delta(U, ldu, n_in, 1.0, nullptr, wf.diag, st));
       std::vector<double> var(n_in), diag(n_in);
       const ReadPiece pv[2] = {{var.data(), wf.colvar, n_in * sizeof(double)},
