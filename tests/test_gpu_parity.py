@@ -363,6 +363,36 @@ def test_nonfinite_weight_is_reported(device):
     assert ei.value.status == lib.E_NONFINITE
 
 
+@pytest.mark.parametrize("dtype,n_out,n_in,pad", [("bf16", 40, 256, 0), ("bf16", 40, 333, 0),
+                                                  ("bf16", 40, 256, 8), ("f32", 24, 260, 0),
+                                                  ("f32", 24, 258, 0), ("f32", 24, 256, 4)])
+def test_nonfinite_weight_any_position(device, dtype, n_out, n_in, pad):
+    """The finiteness check of W reads rows in 16-byte chunks when rows are aligned and element
+    by element otherwise (and for a row's tail): a NaN or an Inf anywhere, in either path, is
+    reported; a clean layer is not."""
+    rng = np.random.default_rng(5)
+    full = torch.from_numpy(rng.normal(0, 0.02, (n_out, n_in + pad)).astype(np.float32)).to(device)
+    if dtype == "bf16":
+        full = full.to(torch.bfloat16)
+    W = full[:, :n_in]
+    sig = np.eye(n_in)
+    U = torch.from_numpy(sig).to(device)
+    lib.sic_quantize(W, U, 0.01)  # clean: no error
+    if pad:
+        full[:, n_in:] = float("nan")  # padding past n_in is not part of the layer
+        lib.sic_quantize(W, U, 0.01)
+        full[:, n_in:] = 0.0
+    for r, j, v in [(0, 0, float("nan")), (1, 9, float("inf")), (n_out // 2, n_in // 2, float("-inf")),
+                    (n_out - 1, n_in - 1, float("nan")), (n_out - 2, n_in - 3, float("inf"))]:
+        old = W[r, j].item()
+        W[r, j] = v
+        with pytest.raises(lib.WsicError) as ei:
+            lib.sic_quantize(W, U, 0.01)
+        assert ei.value.status == lib.E_NONFINITE, (r, j, v)
+        W[r, j] = old
+    lib.sic_quantize(W, U, 0.01)
+
+
 def test_nonfinite_activation_is_reported(device):
     layer = _layer("spiked_300x333")
     X = x_tensors(layer)[0]
