@@ -1360,7 +1360,8 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
       // slope then removes.
       double probe_slope = 0.0;  // 0: no probe
       const int S = probe_rows(n_out);
-      if (!cols && S > 0 && wf.Yp && g_dbg.probe.load() && passes < o.max_passes) {
+      // (only with room for at least one full pass after it)
+      if (!cols && S > 0 && wf.Yp && g_dbg.probe.load() && passes + 2 <= o.max_passes) {
         static const double off[PROBE_K] = {-0.16, -0.08, -0.04, -0.015, 0.015, 0.04, 0.08, 0.16};
         const double x0 = std::log2(c0);
         ProbeFactors fac{};
