@@ -1489,9 +1489,18 @@ static int waterfill_run(const double* lam, const void* W, int dtype, int64_t n_
     }
     // the accepted codes must end in the caller's buffers
     if (hi_buf == 1) {
-      WSIC_HIP_TRY(hipMemcpy2DAsync(codes, ldq * sizeof(int32_t), wf.codes2, n_in * sizeof(int32_t),
-                                    n_in * sizeof(int32_t), n_out, hipMemcpyDeviceToDevice, st));
-      if (resid)
+      // (dense rows: one linear copy, which the runtime runs faster than a 2-D one)
+      if (ldq == n_in)
+        WSIC_HIP_TRY(hipMemcpyAsync(codes, wf.codes2, (size_t)n_out * n_in * sizeof(int32_t),
+                                    hipMemcpyDeviceToDevice, st));
+      else
+        WSIC_HIP_TRY(hipMemcpy2DAsync(codes, ldq * sizeof(int32_t), wf.codes2,
+                                      n_in * sizeof(int32_t), n_in * sizeof(int32_t), n_out,
+                                      hipMemcpyDeviceToDevice, st));
+      if (resid && ldr == n_in)
+        WSIC_HIP_TRY(hipMemcpyAsync(resid, wf.resid2, (size_t)n_out * n_in * sizeof(float),
+                                    hipMemcpyDeviceToDevice, st));
+      else if (resid)
         WSIC_HIP_TRY(hipMemcpy2DAsync(resid, ldr * sizeof(float), wf.resid2, n_in * sizeof(float),
                                       n_in * sizeof(float), n_out, hipMemcpyDeviceToDevice, st));
       WSIC_HIP_TRY(hipStreamSynchronize(st));
