@@ -73,3 +73,34 @@ def test_no_probe_below_16384_rows(capfd):
     err = capfd.readouterr().err
     assert "probe" not in err
     assert 2.0 - WINDOW < wf["rate"] <= 2.0
+
+
+@pytest.mark.parametrize("which", ["waterfill", "softwater"])
+def test_probe_padded_outputs(layer_on_device, capfd, which):
+    """With the probe pass, codes and residuals written through row-padded views give the same
+    search and results as dense outputs, and the padding is never written (the probe's own codes
+    go to the workspace, whose rows are dense)."""
+    layer, L, U = layer_on_device
+    W = w_tensor(layer)
+    n_out, n_in = layer.n_out, layer.n_in
+    pad = 11
+    codes_big = torch.full((n_out, n_in + pad), -99, dtype=torch.int32, device=DEV)
+    resid_big = torch.full((n_out, n_in + pad), 1234.5, dtype=torch.float32, device=DEV)
+    if which == "waterfill":
+        run = lambda **kw: lib.waterfill(W, U, 2.0, mode="secant", **kw)
+    else:
+        lam = torch.from_numpy(np.linspace(0.05, 0.25, n_out)).to(DEV)
+        run = lambda **kw: lib.softwater_waterfill(W, U, lam, 2.0, mode="secant", **kw)
+    try:
+        lib.debug_set("trace", 1)
+        dense = run()
+        padded = run(codes=codes_big[:, :n_in], resid=resid_big[:, :n_in])
+    finally:
+        lib.debug_reset()
+    assert capfd.readouterr().err.count("probe of 8 scales") == 2
+    say(f"[probe-padded] {which}: c={dense['c']!r} passes={dense['passes']}; padded c={padded['c']!r}")
+    assert padded["c"] == dense["c"] and padded["rate"] == dense["rate"]
+    assert torch.equal(codes_big[:, :n_in], dense["codes"])
+    assert torch.equal(resid_big[:, :n_in], dense["resid"])
+    assert torch.all(codes_big[:, n_in:] == -99)
+    assert torch.all(resid_big[:, n_in:] == 1234.5)
