@@ -267,7 +267,9 @@ int wsic_scatter_codes(const int32_t* codes_live, int64_t n_out, int64_t ldql, c
  *   out_cap >= wsic_rans_bound(n, L) bytes; *out_bytes (host): bytes written. n < 2^31.
  *   Workspace: wsic_workspace_bytes(WSIC_OP_RANS_ENC, lane_symbols, n).
  * wsic_rans_decode: the n codes back (n must match the container); WSIC_E_INVAL for a container
- *   that is not one or does not decode to the encoder's start states.
+ *   that is not one, whose frequency table does not sum to 2^14, whose streams read past the
+ *   escapes or the payload, or that does not decode to the encoder's start states (a damaged
+ *   container never makes the decoder read or write outside its buffers).
  *   Workspace: wsic_workspace_bytes(WSIC_OP_RANS_DEC, 0, 1).
  * wsic_rans_decode_dequant: decodes an n_out x n_in layer straight to W_hat_ij = c q_ij / U_jj
  *   (w_hat_dtype f32 or bf16, contiguous). Workspace: wsic_workspace_bytes(WSIC_OP_RANS_DEC, 0, n_in).

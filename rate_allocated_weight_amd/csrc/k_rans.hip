@@ -10,13 +10,23 @@
 //     them (by step, then by lane among the lanes that read one), found with a wave ballot and a
 //     prefix popcount, so the decoder's word loads are contiguous too.
 //
-//   k_rans_esc_count  escapes per group (for the escape offsets, scanned before encoding)
-//   k_rans_encode     symbols in reverse order per lane; words written backwards into a per-group
-//                     area, escapes straight into the container
+//   k_rans_esc_count  escapes per group (for the escape offsets, scanned before encoding); one
+//                     workgroup per group, 16-byte loads
+//   k_rans_encode     symbols in reverse order per lane, the codes of the next 32 steps loading
+//                     while 32 steps run; words written backwards into a per-group area, escapes
+//                     straight into the container; xs / f through a per-symbol reciprocal in fp64
+//                     with one exact correction
 //   k_scan_u32        exclusive prefix sums (one workgroup): word and escape offsets
 //   k_rans_compact    each group's words into the container's payload
-//   k_rans_decode     one wave per group, a 2^14-entry slot -> symbol table in LDS; writes int32
-//                     codes, or dequantized weights c q / U_jj (float or bf16)
+//   k_rans_decode     eight groups (waves) per workgroup sharing two slot tables in LDS, built in
+//                     parallel (frequency sums by a scan, each symbol marking its first slot, a
+//                     prefix maximum spreading the marks): slot -> symbol, and slot -> (f, slot -
+//                     cum) so that one LDS read gives the state update; the payload words reach the
+//                     wave through a ring in LDS filled ahead of the decoder, so a step waits on LDS
+//                     only; writes int32 codes, or dequantized weights c q / U_jj (float or bf16)
+//                     with the column scales in LDS (n_in <= 4096) or loaded a block ahead
+#include <type_traits>
+
 #include "common.h"
 
 namespace wsic {
@@ -25,25 +35,84 @@ namespace {
 constexpr int RPROB = 14, RM = 1 << RPROB, RLANES = 64, RWIN = 2047;
 constexpr uint32_t RLOW = 1u << 16;
 
-__device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
+// ballots and the count of the set lanes below this one, straight from the lane masks
+__device__ __forceinline__ uint64_t ballot(bool b) { return __builtin_amdgcn_ballot_w64(b); }
+__device__ __forceinline__ uint32_t count_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
+__device__ __forceinline__ uint32_t is_escape(int v) { return (v < -RWIN || v > RWIN) ? 1u : 0u; }
+
+// Escapes per group: a group's L x 64 codes are contiguous, so one workgroup per group reads them
+// with 16-byte loads (VEC: the codes are 16-byte aligned, which makes every group start so), eight
+// loads in flight per thread, and sums the counts.
+template <bool VEC>
 __global__ __launch_bounds__(256) void k_rans_esc_count(const int32_t* __restrict__ q, int64_t N,
                                                         int L, int64_t G,
                                                         uint32_t* __restrict__ cnt) {
-  const int lane = threadIdx.x & 63;
-  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= G) return;
+  __shared__ uint32_t part[4];
+  const int64_t g = blockIdx.x;
+  const int64_t e0 = g * (int64_t)L * RLANES;
+  const int64_t e1 = e0 + (int64_t)L * RLANES < N ? e0 + (int64_t)L * RLANES : N;
   uint32_t c = 0;
-  for (int k = 0; k < L; ++k) {
-    const int64_t p = (g * L + k) * RLANES + lane;
-    if (p < N) {
-      const int v = q[p];
-      c += (v < -RWIN || v > RWIN) ? 1u : 0u;
+  const int64_t n4 = VEC && e1 > e0 ? (e1 - e0) / 4 : 0;
+  if (VEC) {
+    const int4* q4 = reinterpret_cast<const int4*>(q + e0);
+    for (int64_t i = threadIdx.x; i < n4; i += 256 * 8) {
+      int4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t ii = i + u * 256;
+        v[u] = q4[ii < n4 ? ii : n4 - 1];  // (clamped: counted only when in range)
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t m = (i + u * 256 < n4) ? 1u : 0u;
+        c += m * (is_escape(v[u].x) + is_escape(v[u].y) + is_escape(v[u].z) + is_escape(v[u].w));
+      }
     }
   }
+  for (int64_t e = e0 + n4 * 4 + threadIdx.x; e < e1; e += 256) c += is_escape(q[e]);
   for (int d = 1; d < 64; d <<= 1) c += __shfl_xor(c, d, 64);
-  if (lane == 0) cnt[g] = c;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) cnt[g] = (part[0] + part[1]) + (part[2] + part[3]);
 }
+
+// Exclusive prefix sums of the frequency table (nsym <= 4096) into sc, by a workgroup of NT threads
+// (4096 / NT consecutive symbols each, then a scan of the thread sums); returns the table's total.
+// Every thread of the workgroup calls it.
+template <int NT>
+__device__ uint32_t table_cum(const uint16_t* sf, uint16_t* sc, int nsym, uint32_t* wsum) {
+  constexpr int PER = 4096 / NT;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  uint32_t loc = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (t * PER + j < nsym) loc += sf[t * PER + j];
+  uint32_t inc = loc;
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  uint32_t c = inc - loc, total = 0;
+  for (int i = 0; i < NT / 64; ++i) {
+    if (i < w) c += wsum[i];
+    total += wsum[i];
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (t * PER + j < nsym) {
+      sc[t * PER + j] = (uint16_t)c;
+      c += sf[t * PER + j];
+    }
+  __syncthreads();
+  return total;
+}
+
+constexpr int EB = 32;  // encoder: the codes of the next EB steps are loaded while EB steps run
 
 __global__ __launch_bounds__(256) void k_rans_encode(const int32_t* __restrict__ q, int64_t N, int L,
                                                      int64_t G, int lo, int nsym,
@@ -54,16 +123,15 @@ __global__ __launch_bounds__(256) void k_rans_encode(const int32_t* __restrict__
                                                      uint32_t* __restrict__ gwords,
                                                      uint32_t* __restrict__ states) {
   __shared__ uint16_t sf[4096 + 8], sc[4096 + 8];
-  for (int s = threadIdx.x; s < nsym; s += 256) sf[s] = freq[s];
-  __syncthreads();
-  if (threadIdx.x == 0) {  // cumulative frequencies (nsym <= 4096)
-    uint32_t c = 0;
-    for (int s = 0; s < nsym; ++s) {
-      sc[s] = (uint16_t)c;
-      c += sf[s];
-    }
+  __shared__ double srf[4096];  // 1 / f (0 for an absent symbol)
+  __shared__ uint32_t wsum[4];
+  for (int s = threadIdx.x; s < nsym; s += 256) {
+    const uint16_t f = freq[s];
+    sf[s] = f;
+    srf[s] = f ? 1.0 / (double)f : 0.0;
   }
   __syncthreads();
+  (void)table_cum<256>(sf, sc, nsym, wsum);
   const int lane = threadIdx.x & 63;
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (g >= G) return;
@@ -73,27 +141,57 @@ __global__ __launch_bounds__(256) void k_rans_encode(const int32_t* __restrict__
   const uint32_t e0 = eofs[g], etot = eofs[g + 1] - e0;
   uint32_t eafter = 0;
   uint32_t x = RLOW;
-  const uint64_t below = lanes_below(lane);
-  for (int k = L - 1; k >= 0; --k) {
-    const int64_t p = (g * L + k) * RLANES + lane;
-    const bool active = p < N;
-    const int v = active ? q[p] : 0;
-    const bool inw = v >= -RWIN && v <= RWIN;
-    const int s = inw ? v - lo : esc;
-    const uint64_t em = __ballot(active && !inw);
-    const uint32_t ne = (uint32_t)__popcll(em);
-    if (active && !inw) esc_out[e0 + etot - eafter - ne + (uint32_t)__popcll(em & below)] = v;
-    eafter += ne;
-    const uint32_t f = active ? sf[s] : 1u, c = active ? sc[s] : 0u;
-    const bool emit = active && (uint64_t)x >= ((uint64_t)f << 18);  // f = 2^14: never
-    const uint64_t wm = __ballot(emit);
-    const int nw = __popcll(wm);
-    if (emit) {
-      tw[tail - nw + __popcll(wm & below)] = (uint16_t)(x & 0xffffu);
-      x >>= 16;
+  const int64_t pbase = g * (int64_t)L * RLANES + lane;  // this lane's code at step 0
+  // steps k < kact hold a code for this lane (all of them but in the last group's tail)
+  const int kact = pbase < N ? (int)min((int64_t)L, (N - pbase + RLANES - 1) / RLANES) : 0;
+  // block b holds steps k = L - 1 - EB b - j, j < EB (the symbols are encoded in reverse)
+  auto load_block = [&](int b, int32_t(&dst)[EB]) {
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      const int k = L - 1 - EB * b - j;
+      dst[j] = (k >= 0 && k < kact) ? q[pbase + (int64_t)k * RLANES] : 0;
     }
-    tail -= nw;
-    if (active) x = ((x / f) << RPROB) + (x % f) + c;
+  };
+  const int nblk = (L + EB - 1) / EB;
+  int32_t nxt[EB];
+  load_block(0, nxt);
+  for (int b = 0; b < nblk; ++b) {
+    int32_t cur[EB];
+#pragma unroll
+    for (int j = 0; j < EB; ++j) cur[j] = nxt[j];
+    if (b + 1 < nblk) load_block(b + 1, nxt);
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      const int k = L - 1 - EB * b - j;
+      if (k < 0) continue;  // (the last block's end; wave-uniform)
+      const bool active = k < kact;
+      const int v = cur[j];
+      const bool inw = v >= -RWIN && v <= RWIN;
+      const int s = !active ? 0 : (inw ? v - lo : esc);
+      const uint64_t em = ballot(active && !inw);
+      if (em) {  // (rare) escaped codes go raw, backwards from the end of the group's escapes
+        const uint32_t ne = (uint32_t)__popcll(em);
+        if (active && !inw) esc_out[e0 + etot - eafter - ne + count_below(em)] = v;
+        eafter += ne;
+      }
+      const uint32_t f = sf[s], c = sc[s];
+      const double rf = srf[s];
+      const bool emit = active && (x >> 18) >= f;  // x >= f 2^18 (never for f = 2^14)
+      const uint64_t wm = ballot(emit);
+      const int nw = __popcll(wm);
+      if (emit) tw[tail - nw + count_below(wm)] = (uint16_t)(x & 0xffffu);
+      tail -= nw;
+      const uint32_t xs = emit ? x >> 16 : x;
+      // xs / f and xs % f: the product with the rounded 1/f truncates to the quotient or one less
+      // (one more would need a quotient near 2^38; here it is below 2^18), so one step corrects it
+      uint32_t qd = (uint32_t)((double)xs * rf);
+      uint32_t r = xs - qd * f;
+      const bool up = r >= f;
+      qd += up ? 1u : 0u;
+      r -= up ? f : 0u;
+      const uint32_t xn = (qd << RPROB) + r + c;
+      x = active ? xn : x;
+    }
   }
   states[g * RLANES + lane] = x;
   if (lane == 0) gwords[g] = (uint32_t)((int64_t)RLANES * L - tail);
@@ -139,102 +237,259 @@ __global__ __launch_bounds__(256) void k_rans_compact(const uint16_t* __restrict
   for (uint32_t i = threadIdx.x; i < n; i += 256) dst[i] = src[i];
 }
 
-template <int MODE>  // 0: int32 codes; 1: float weights; 2: bf16 weights
-__global__ __launch_bounds__(256) void k_rans_decode(const uint16_t* __restrict__ freq, int nsym, int lo,
-                                                     int64_t N, int L, int64_t G,
-                                                     const uint32_t* __restrict__ gofs,
-                                                     const uint32_t* __restrict__ eofs,
-                                                     const uint32_t* __restrict__ states,
-                                                     const int32_t* __restrict__ escapes,
-                                                     uint32_t n_esc,
-                                                     const uint16_t* __restrict__ payload,
-                                                     uint32_t n_words,
-                                                     void* __restrict__ out, int64_t n_in,
-                                                     const double* __restrict__ invd, double cscale,
-                                                     int* __restrict__ flags) {
-  __shared__ uint16_t lut[RM];
-  __shared__ uint16_t sf[4096 + 8], sc[4096 + 8];
-  for (int s = threadIdx.x; s < nsym; s += 256) sf[s] = freq[s];
+constexpr int DW = 8;            // decoder: groups (waves) per workgroup, sharing the slot tables
+constexpr int RSEG = 512;        // payload words per ring segment (8 per lane; the shift by 9 below)
+constexpr int RRING = 2 * RSEG;  // per wave: a ring of two segments in LDS
+constexpr int DB = 16;           // decoder: the column scales of the next DB steps load during DB steps
+constexpr int SL_COLS = 4096;    // decoder: columns whose scales fit in LDS beside the tables
+
+
+// MODE 0: int32 codes; 1: float weights; 2: bf16 weights. SL: the column scales sit in LDS
+// (n_in <= 4096), else they are loaded a block of steps ahead into registers.
+template <int MODE, bool SL>
+__global__ __launch_bounds__(64 * DW) void k_rans_decode(const uint16_t* __restrict__ freq, int nsym,
+                                                         int lo, int64_t N, int L, int64_t G,
+                                                         const uint32_t* __restrict__ gofs,
+                                                         const uint32_t* __restrict__ eofs,
+                                                         const uint32_t* __restrict__ states,
+                                                         const int32_t* __restrict__ escapes,
+                                                         uint32_t n_esc,
+                                                         const uint16_t* __restrict__ payload,
+                                                         uint32_t n_words,
+                                                         void* __restrict__ out, int64_t n_in,
+                                                         const double* __restrict__ invd,
+                                                         double cscale, int* __restrict__ flags) {
+  constexpr int NT = 64 * DW;
+  __shared__ __attribute__((aligned(16))) uint32_t lut[RM];   // f | (slot - cum) << 15
+  __shared__ __attribute__((aligned(16))) uint16_t lsym[RM];  // the slot's symbol
+  // the payload rings; before decoding they hold the frequencies and their sums (4096 each)
+  __shared__ __attribute__((aligned(16))) uint16_t ring[DW * RRING];
+  static_assert(DW * RRING >= 2 * 4096, "the table build borrows the rings");
+  __shared__ uint32_t wsum[DW];
+  __shared__ double ssc[SL ? SL_COLS : 1];  // c / U_jj per column
+  uint16_t* sf = ring;
+  uint16_t* sc = ring + 4096;
+  const int t = threadIdx.x;
+  for (int s = t; s < nsym; s += NT) sf[s] = freq[s];
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t c = 0;
-    for (int s = 0; s < nsym; ++s) {
-      sc[s] = (uint16_t)c;
-      c += sf[s];
+  if (table_cum<NT>(sf, sc, nsym, wsum) != (uint32_t)RM) {  // the same verdict in every thread
+    if (t == 0) atomicOr(flags, FLAG_RANGE);
+    return;
+  }
+  // slot -> symbol: each present symbol marks the first slot of its range, and a prefix maximum
+  // carries the mark over the range (marks grow with the slot, as the sums do)
+  for (int i = t; i < RM / 8; i += NT) reinterpret_cast<uint4*>(lsym)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  for (int s = t; s < nsym; s += NT)
+    if (sf[s] != 0) lsym[sc[s]] = (uint16_t)s;
+  __syncthreads();
+  {
+    constexpr int PER = RM / NT;  // consecutive slots per thread
+    static_assert(PER % 8 == 0, "whole 16-byte pieces");
+    const int lane = t & 63, w = t >> 6;
+    uint16_t m[PER];
+#pragma unroll
+    for (int h = 0; h < PER / 8; ++h) {
+      const uint4 v = reinterpret_cast<const uint4*>(lsym + t * PER)[h];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m[8 * h + 2 * e] = (uint16_t)(u[e] & 0xffffu);
+        m[8 * h + 2 * e + 1] = (uint16_t)(u[e] >> 16);
+      }
+    }
+    uint32_t run = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) run = max(run, (uint32_t)m[i]);
+    uint32_t inc = run;
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(inc, d, 64);
+      if (lane >= d) inc = max(inc, o);
+    }
+    const uint32_t before = __shfl_up(inc, 1, 64);
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    run = lane > 0 ? before : 0u;
+    for (int i = 0; i < w; ++i) run = max(run, wsum[i]);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      run = max(run, (uint32_t)m[i]);
+      m[i] = (uint16_t)run;
+    }
+#pragma unroll
+    for (int h = 0; h < PER / 8; ++h) {
+      uint32_t u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = (uint32_t)m[8 * h + 2 * e] | ((uint32_t)m[8 * h + 2 * e + 1] << 16);
+      reinterpret_cast<uint4*>(lsym + t * PER)[h] = make_uint4(u[0], u[1], u[2], u[3]);
+    }
+#pragma unroll
+    for (int h = 0; h < PER / 4; ++h) {
+      uint32_t u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * h + e, slot = t * PER + i;
+        u[e] = (uint32_t)sf[m[i]] | ((uint32_t)(slot - sc[m[i]]) << 15);
+      }
+      reinterpret_cast<uint4*>(lut + t * PER)[h] = make_uint4(u[0], u[1], u[2], u[3]);
     }
   }
+  if (SL)
+    for (int c = t; c < n_in; c += NT) ssc[c] = cscale * invd[c];
   __syncthreads();
-  for (int slot = threadIdx.x; slot < RM; slot += 256) {  // largest s with cum[s] <= slot, f > 0
-    int a = 0, b = nsym - 1;
-    while (a < b) {
-      const int m = (a + b + 1) >> 1;
-      if (sc[m] <= slot) a = m;
-      else b = m - 1;
-    }
-    while (a > 0 && sf[a] == 0) --a;  // zero-frequency symbols share their successor's cumulative
-    lut[slot] = (uint16_t)a;
-  }
-  __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = t & 63;
+  const int64_t g = (int64_t)blockIdx.x * DW + (t >> 6);
   if (g >= G) return;
   const int esc = nsym - 1;
+  uint16_t* rg = ring + (t >> 6) * RRING;
   uint32_t x = states[g * RLANES + lane];
   uint32_t wp = gofs[g], ep = eofs[g];
-  const uint64_t below = lanes_below(lane);
-  int64_t col = MODE != 0 ? ((g * L) * RLANES + lane) % n_in : 0;
-  for (int k = 0; k < L; ++k) {
-    const int64_t p = (g * L + k) * RLANES + lane;
-    const bool active = p < N;
-    const uint32_t slot = x & (RM - 1);
-    const int s = lut[slot];
-    if (active) x = (uint32_t)sf[s] * (x >> RPROB) + slot - sc[s];
-    const bool isesc = active && s == esc;
-    const uint64_t em = __ballot(isesc);
-    int v = lo + s;
-    bool bad = false;  // reads past the escapes or the payload: a corrupt container
-    if (isesc) {
-      const uint32_t i = ep + (uint32_t)__popcll(em & below);
-      bad |= i >= n_esc;
-      v = i < n_esc ? escapes[i] : 0;
+  // Payload words through a ring of two 512-word segments per wave: segment h holds the words
+  // [A + 512 h, A + 512 (h + 1)) (zero past the payload) in slot h & 1; segments below `filled`
+  // have been written, the next two wait in registers (P0 the even one, P1 the odd one). Eight
+  // steps read at most 512 words, [wp, wp + 512): checked every eighth step, the segment of
+  // wp + 511 has grown by at most one, so writing one segment when it reaches `filled` keeps the
+  // next eight steps' words in the ring, and the segment it replaces (filled - 2) lies behind wp.
+  // The words wait in registers for at least two refills (16 steps) before they are written.
+  const uint32_t A = wp;
+  // (one word per 32-bit register: packing two would wait for the loads at once)
+  auto word = [&](uint64_t i) -> uint32_t { return i < n_words ? (uint32_t)payload[i] : 0u; };
+  uint32_t P0[8], P1[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    rg[64 * h + lane] = (uint16_t)word((uint64_t)A + 64 * h + lane);
+    rg[RSEG + 64 * h + lane] = (uint16_t)word((uint64_t)A + RSEG + 64 * h + lane);
+    P0[h] = word((uint64_t)A + 2 * RSEG + 64 * h + lane);
+    P1[h] = word((uint64_t)A + 3 * RSEG + 64 * h + lane);
+  }
+  uint32_t filled = 2;
+  __builtin_amdgcn_wave_barrier();
+  const int64_t pbase = g * (int64_t)L * RLANES + lane;  // this lane's output at step 0
+  // steps k < kact write an output for this lane (all of them but in the last group's tail)
+  const int kact = pbase < N ? (int)min((int64_t)L, (N - pbase + RLANES - 1) / RLANES) : 0;
+  const int step_col = MODE != 0 ? (int)(RLANES % n_in) : 0;  // the column moves by 64 per step
+  int col = MODE != 0 ? (int)(pbase % n_in) : 0;  // this step's column (SL) or the next one loaded
+  auto next_col = [&]() {
+    col += step_col;
+    col -= col >= n_in ? (int)n_in : 0;
+  };
+  auto load_scales = [&](int kb, double(&dst)[DB]) {
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
+      dst[j] = kb + j < kact ? cscale * invd[col] : 0.0;
+      next_col();
     }
-    ep += (uint32_t)__popcll(em);
-    const bool need = active && x < RLOW;
-    const uint64_t wm = __ballot(need);
-    if (need) {
-      const uint32_t i = wp + (uint32_t)__popcll(wm & below);
-      bad |= i >= n_words;
-      x = (x << 16) | (i < n_words ? payload[i] : 0u);
-    }
-    wp += (uint32_t)__popcll(wm);
-    if (bad) atomicOr(flags, FLAG_RANGE);
-    if (active) {
-      if (MODE == 0) {
-        ((int32_t*)out)[p] = v;
-      } else {
-        const float w = (float)((cscale * invd[col]) * (double)v);
-        if (MODE == 1) {
-          ((float*)out)[p] = w;
-        } else {
-          uint32_t u = __float_as_uint(w);
-          u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-          ((uint16_t*)out)[p] = (uint16_t)u;
+  };
+  constexpr bool PREF = MODE != 0 && !SL;
+  double snxt[DB];
+  if (PREF) load_scales(0, snxt);
+  const uint32_t ep0 = ep;
+  const int nblk = (L + DB - 1) / DB;
+  // FULL: every lane writes at every step (every group but the last)
+  auto run = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    for (int b = 0; b < nblk; ++b) {
+      double scur[DB];
+      if (PREF) {
+#pragma unroll
+        for (int j = 0; j < DB; ++j) scur[j] = snxt[j];
+        if (b + 1 < nblk) load_scales((b + 1) * DB, snxt);
+      }
+#pragma unroll
+      for (int j = 0; j < DB; ++j) {
+        const int k = b * DB + j;
+        if (k >= L) continue;  // (the last block's end; wave-uniform)
+        if ((j & 7) == 0 && ((wp - A + (RSEG - 1)) >> 9) >= filled) {  // wave-uniform
+          const uint64_t nb = (uint64_t)A + (uint64_t)(filled + 2) * RSEG;
+          if (filled & 1u) {
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+              rg[RSEG + 64 * h + lane] = (uint16_t)P1[h];
+              P1[h] = word(nb + 64 * h + lane);
+            }
+          } else {
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+              rg[64 * h + lane] = (uint16_t)P0[h];
+              P0[h] = word(nb + 64 * h + lane);
+            }
+          }
+          ++filled;
+          __builtin_amdgcn_wave_barrier();
+        }
+        const bool active = FULL || k < kact;
+        const uint32_t slot = x & (RM - 1);
+        const uint32_t e = lut[slot];
+        const int s = lsym[slot];
+        double scale = 0.0;
+        if (MODE != 0) {
+          if (SL) {
+            scale = ssc[col];
+            next_col();
+          } else {
+            scale = scur[j];
+          }
+        }
+        const uint32_t xn = (e & 0x7fffu) * (x >> RPROB) + (e >> 15);  // (both reads in flight at once)
+        x = active ? xn : x;
+        const bool isesc = active && s == esc;
+        const uint64_t em = ballot(isesc);
+        int v = lo + s;
+        if (em) {  // (rare) the escaped codes; waited for here so that the store below never waits
+          if (isesc) {
+            const uint32_t i = ep + count_below(em);
+            v = i < n_esc ? escapes[i] : 0;
+          }
+          asm volatile("" : "+v"(v));
+          ep += (uint32_t)__popcll(em);
+        }
+        const bool need = active && x < RLOW;
+        const uint64_t wm = ballot(need);
+        const uint32_t w = rg[(wp + count_below(wm) - A) & (RRING - 1)];
+        x = need ? ((x << 16) | w) : x;
+        wp += (uint32_t)__popcll(wm);
+        if (active) {
+          const int64_t p = pbase + (int64_t)k * RLANES;
+          if (MODE == 0) {
+            ((int32_t*)out)[p] = v;
+          } else {
+            const float wt = (float)(scale * (double)v);
+            if (MODE == 1) {
+              ((float*)out)[p] = wt;
+            } else {
+              uint32_t u = __float_as_uint(wt);
+              u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+              ((uint16_t*)out)[p] = (uint16_t)u;
+            }
+          }
         }
       }
     }
-    if (MODE != 0) {  // the column of the next step's weight
-      col += RLANES;
-      while (col >= n_in) col -= n_in;
-    }
-  }
-  if (x != RLOW) atomicOr(flags, FLAG_RANGE);  // every stream ends in the encoder's start state
+  };
+  if ((g + 1) * (int64_t)L * RLANES <= N) run(std::true_type{});
+  else run(std::false_type{});
+  // A read past the payload or the escapes (a corrupt container) happened exactly when the group
+  // consumed past their ends (the largest index read is the last one consumed); every stream ends
+  // in the encoder's start state.
+  const bool bad = (uint64_t)A + (uint32_t)(wp - A) > (uint64_t)n_words ||
+                   (uint64_t)ep0 + (uint32_t)(ep - ep0) > (uint64_t)n_esc;
+  if (bad || x != RLOW) atomicOr(flags, FLAG_RANGE);
 }
 
 }  // namespace
 
 int launch_rans_esc_count(const int32_t* q, int64_t N, int L, int64_t G, uint32_t* cnt, hipStream_t st) {
-  WSIC_LAUNCH("rans_esc", 4.0 * (double)N, st, k_rans_esc_count, dim3((unsigned)((G + 3) / 4)), dim3(256),
-              0, q, N, L, G, cnt);
+  if (G <= 0) return WSIC_OK;
+  if (G > 0x7fffffff) {
+    set_error("internal: %lld coder groups", (long long)G);
+    return WSIC_E_INVAL;
+  }
+  if ((((uintptr_t)q) & 15) == 0)
+    WSIC_LAUNCH("rans_esc", 4.0 * (double)N, st, k_rans_esc_count<true>, dim3((unsigned)G), dim3(256),
+                0, q, N, L, G, cnt);
+  else
+    WSIC_LAUNCH("rans_esc", 4.0 * (double)N, st, k_rans_esc_count<false>, dim3((unsigned)G),
+                dim3(256), 0, q, N, L, G, cnt);
   return WSIC_OK;
 }
 
@@ -264,18 +519,19 @@ int launch_rans_decode(int mode, const uint16_t* freq, int nsym, int lo, int64_t
                        const int32_t* escapes, uint32_t n_esc, const uint16_t* payload,
                        uint32_t n_words, void* out, int64_t n_in, const double* invd, double c,
                        int* flags, hipStream_t st) {
-  if (nsym > 4096) return WSIC_E_INVAL;
-  const dim3 grid((unsigned)((G + 3) / 4));
+  if (nsym > 4096 || n_in <= 0 || n_in > 0x7fffffff) return WSIC_E_INVAL;
+  const dim3 grid((unsigned)((G + DW - 1) / DW));
   const double work = (double)N * (mode == 0 ? 4.0 : (mode == 1 ? 4.0 : 2.0));
-  if (mode == 0)
-    WSIC_LAUNCH("rans_decode", work, st, k_rans_decode<0>, grid, dim3(256), 0, freq, nsym, lo, N, L, G,
-                gofs, eofs, states, escapes, n_esc, payload, n_words, out, n_in, invd, c, flags);
-  else if (mode == 1)
-    WSIC_LAUNCH("rans_decode", work, st, k_rans_decode<1>, grid, dim3(256), 0, freq, nsym, lo, N, L, G,
-                gofs, eofs, states, escapes, n_esc, payload, n_words, out, n_in, invd, c, flags);
-  else
-    WSIC_LAUNCH("rans_decode", work, st, k_rans_decode<2>, grid, dim3(256), 0, freq, nsym, lo, N, L, G,
-                gofs, eofs, states, escapes, n_esc, payload, n_words, out, n_in, invd, c, flags);
+  const bool sl = n_in <= SL_COLS;
+#define WSIC_RANS_DEC(M, S)                                                                        \
+  WSIC_LAUNCH("rans_decode", work, st, (k_rans_decode<M, S>), grid, dim3(64 * DW), 0, freq, nsym, lo, \
+              N, L, G, gofs, eofs, states, escapes, n_esc, payload, n_words, out, n_in, invd, c, flags)
+  if (mode == 0) WSIC_RANS_DEC(0, false);
+  else if (mode == 1 && sl) WSIC_RANS_DEC(1, true);
+  else if (mode == 1) WSIC_RANS_DEC(1, false);
+  else if (sl) WSIC_RANS_DEC(2, true);
+  else WSIC_RANS_DEC(2, false);
+#undef WSIC_RANS_DEC
   return WSIC_OK;
 }
 

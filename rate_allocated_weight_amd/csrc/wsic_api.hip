@@ -1922,7 +1922,9 @@ static int rans_decode_any(const uint8_t* in, size_t in_bytes, int mode, void* d
   int f = 0;
   WSIC_TRY(read_flags(flags, &f, st));
   if (f & FLAG_RANGE) {
-    set_error("rans_decode: a stream did not end in its start state (corrupt container)");
+    set_error("rans_decode: corrupt container (a frequency table that does not sum to 2^14, a "
+              "read past the escapes or the payload, or a stream that did not end in its start "
+              "state)");
     return WSIC_E_INVAL;
   }
   return flags_status(f, "rans_decode");

@@ -45,6 +45,64 @@ def test_container_matches_reference(device, n, spread, esc, L):
     np.testing.assert_array_equal(back.cpu().numpy(), q)
 
 
+@pytest.mark.parametrize("n,spread,esc,L", [(64 * 1024 * 2 + 4321, 30.0, 17, 1024),
+                                            (64 * 300 * 5 + 11, 3.0, 0, 300),
+                                            (64 * 1000 + 5, 400.0, 5, 1000),
+                                            (64 * 2048, 1.0e4, 0, 2048)])
+def test_long_streams_match_reference(device, n, spread, esc, L):
+    """Streams long enough that the decoder refills its payload ring many times, stream lengths that
+    are not a multiple of the kernels' step blocks, a rate near 10 bits, and a source that is mostly
+    escapes: containers equal the reference's byte for byte and decode back to the codes."""
+    q = _codes(n + 1, n, spread, esc)
+    qt = torch.from_numpy(q).to(DEV)
+    blob, nb = lib.rans_encode(qt, L)
+    ref = rans.encode(q, L)
+    say(f"[rans-long] n={n} L={L} spread={spread}: {8.0 * len(ref) / n:.3f} bits per code")
+    assert nb == len(ref)
+    assert blob[:nb].cpu().numpy().tobytes() == ref
+    back = lib.rans_decode(blob, nb, n)
+    np.testing.assert_array_equal(back.cpu().numpy(), q)
+
+
+@pytest.mark.parametrize("L", [37, 1000])
+def test_decode_to_weights_long_streams(device, L):
+    """Decoding to weights with streams whose length is not a multiple of the step blocks (the
+    column scales are loaded a block ahead) and with many ring refills (4 bits per code, 1000
+    codes per stream) equals the dequantization of wsic_distortion bit for bit."""
+    layer = workloads.make_layer("spiked", 300, 333, 900, seed=0, name="spiked_300x333", dtype="bf16", rank=16)
+    Lc, info = oracle.cholesky_lower(oracle.covariance(layer.x_chunks))
+    U = torch.from_numpy(np.ascontiguousarray(Lc.T)).to(DEV)
+    Wt = w_tensor(layer)
+    wf = lib.waterfill(Wt, U, 4.0)
+    codes = wf["codes"].contiguous()
+    blob, nb = lib.rans_encode(codes, L)
+    assert blob[:nb].cpu().numpy().tobytes() == rans.encode(codes.cpu().numpy().ravel(), L)
+    for dt in (torch.float32, torch.bfloat16):
+        _, w_ref = lib.distortion(Wt, codes, U, wf["c"], resid=wf["resid"], w_hat_dtype=dt)
+        w = lib.rans_decode_dequant(blob, nb, layer.n_out, layer.n_in, U, wf["c"], dtype=dt)
+        assert torch.equal(w.view(torch.int16) if dt == torch.bfloat16 else w.view(torch.int32),
+                           w_ref.view(torch.int16) if dt == torch.bfloat16 else w_ref.view(torch.int32))
+
+
+def test_decode_to_weights_wide_rows(device):
+    """More than 4096 columns: the column scales no longer fit beside the decoder's tables in LDS
+    and are loaded a block of steps ahead instead; the weights still equal the dequantization of
+    wsic_distortion bit for bit, for whole and ragged stream blocks."""
+    n_out, n_in = 24, 4500
+    rng = np.random.default_rng(7)
+    codes = torch.from_numpy(_codes(11, n_out * n_in, 3.0).reshape(n_out, n_in)).to(DEV)
+    U = torch.diag(torch.from_numpy(rng.uniform(0.5, 2.0, n_in))).to(DEV)
+    W = torch.zeros(n_out, n_in, dtype=torch.float32, device=DEV)
+    c = 0.0123
+    for L in (1000, 37):
+        blob, nb = lib.rans_encode(codes, L)
+        for dt in (torch.float32, torch.bfloat16):
+            _, w_ref = lib.distortion(W, codes, U, c, mode="direct", w_hat_dtype=dt)
+            w = lib.rans_decode_dequant(blob, nb, n_out, n_in, U, c, dtype=dt)
+            assert torch.equal(w.view(torch.int16) if dt == torch.bfloat16 else w.view(torch.int32),
+                               w_ref.view(torch.int16) if dt == torch.bfloat16 else w_ref.view(torch.int32))
+
+
 @pytest.mark.parametrize("R", [1.0, 2.0, 4.0])
 def test_sic_codes_coded_size(device, R):
     layer = workloads.make_layer("spiked", 300, 333, 900, seed=0, name="spiked_300x333", dtype="bf16", rank=16)
@@ -85,5 +143,13 @@ def test_damaged_container_is_rejected(device):
         lib.rans_decode(blob, nb - 100, q.size)
     bad = blob.clone()
     bad[nb - 2000:nb - 1000] ^= 0x5A  # payload bytes: streams no longer end in their start state
+    with pytest.raises(lib.WsicError):
+        lib.rans_decode(bad, nb, q.size)
+    bad = blob.clone()
+    bad[64] ^= 0x01  # the first frequency: the table no longer sums to 2^14
+    with pytest.raises(lib.WsicError):
+        lib.rans_decode(bad, nb, q.size)
+    bad = blob.clone()
+    bad[64:64 + 40] = 0xFF  # frequencies far above 2^14
     with pytest.raises(lib.WsicError):
         lib.rans_decode(bad, nb, q.size)
