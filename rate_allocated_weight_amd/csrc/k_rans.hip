@@ -343,15 +343,17 @@ __global__ __launch_bounds__(64 * DW) void k_rans_decode(const uint16_t* __restr
   const int esc = nsym - 1;
   uint16_t* rg = ring + (t >> 6) * RRING;
   uint32_t x = states[g * RLANES + lane];
-  uint32_t wp = gofs[g], ep = eofs[g];
-  // Payload words through a ring of two 512-word segments per wave: segment h holds the words
-  // [A + 512 h, A + 512 (h + 1)) (zero past the payload) in slot h & 1; segments below `filled`
-  // have been written, the next two wait in registers (P0 the even one, P1 the odd one). Eight
-  // steps read at most 512 words, [wp, wp + 512): checked every eighth step, the segment of
-  // wp + 511 has grown by at most one, so writing one segment when it reaches `filled` keeps the
-  // next eight steps' words in the ring, and the segment it replaces (filled - 2) lies behind wp.
-  // The words wait in registers for at least two refills (16 steps) before they are written.
-  const uint32_t A = wp;
+  uint32_t ep = eofs[g];
+  // Payload words through a ring of two 512-word segments per wave. The group's words start at
+  // A, and wr counts those consumed. Segment h holds the words [A + 512 h, A + 512 (h + 1)) (zero
+  // past the payload) in slot h & 1; segments below `filled` have been written, the next two
+  // wait in registers (P0 the even one, P1 the odd one). Eight steps read at most 512 words,
+  // [A + wr, A + wr + 512): checked every eighth step, the segment of wr + 511 has grown by at
+  // most one, so writing one segment when it reaches `filled` keeps the next eight steps' words
+  // in the ring, and the segment it replaces (filled - 2) lies behind wr. The words wait in
+  // registers for at least two refills (16 steps) before they are written.
+  const uint32_t A = gofs[g];
+  uint32_t wr = 0;
   // (one word per 32-bit register: packing two would wait for the loads at once)
   auto word = [&](uint64_t i) -> uint32_t { return i < n_words ? (uint32_t)payload[i] : 0u; };
   uint32_t P0[8], P1[8];
@@ -385,93 +387,102 @@ __global__ __launch_bounds__(64 * DW) void k_rans_decode(const uint16_t* __restr
   if (PREF) load_scales(0, snxt);
   const uint32_t ep0 = ep;
   const int nblk = (L + DB - 1) / DB;
-  // FULL: every lane writes at every step (every group but the last)
-  auto run = [&](auto full_tag) {
+  // FULL: every lane writes at every step (every group but the last); TAIL: the last, partial
+  // block of steps (L not a multiple of DB)
+  auto block = [&](auto full_tag, auto tail_tag, int b) {
     constexpr bool FULL = decltype(full_tag)::value;
-    for (int b = 0; b < nblk; ++b) {
-      double scur[DB];
-      if (PREF) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    double scur[DB];
+    if (PREF) {
 #pragma unroll
-        for (int j = 0; j < DB; ++j) scur[j] = snxt[j];
-        if (b + 1 < nblk) load_scales((b + 1) * DB, snxt);
+      for (int j = 0; j < DB; ++j) scur[j] = snxt[j];
+      if (b + 1 < nblk) load_scales((b + 1) * DB, snxt);
+    }
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
+      const int k = b * DB + j;
+      if (TAIL && k >= L) continue;  // (wave-uniform)
+      if ((j & 7) == 0 && ((wr + (RSEG - 1)) >> 9) >= filled) {  // wave-uniform
+        const uint64_t nb = (uint64_t)A + (uint64_t)(filled + 2) * RSEG;
+        if (filled & 1u) {
+#pragma unroll
+          for (int h = 0; h < 8; ++h) {
+            rg[RSEG + 64 * h + lane] = (uint16_t)P1[h];
+            P1[h] = word(nb + 64 * h + lane);
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 8; ++h) {
+            rg[64 * h + lane] = (uint16_t)P0[h];
+            P0[h] = word(nb + 64 * h + lane);
+          }
+        }
+        ++filled;
+        __builtin_amdgcn_wave_barrier();
       }
-#pragma unroll
-      for (int j = 0; j < DB; ++j) {
-        const int k = b * DB + j;
-        if (k >= L) continue;  // (the last block's end; wave-uniform)
-        if ((j & 7) == 0 && ((wp - A + (RSEG - 1)) >> 9) >= filled) {  // wave-uniform
-          const uint64_t nb = (uint64_t)A + (uint64_t)(filled + 2) * RSEG;
-          if (filled & 1u) {
-#pragma unroll
-            for (int h = 0; h < 8; ++h) {
-              rg[RSEG + 64 * h + lane] = (uint16_t)P1[h];
-              P1[h] = word(nb + 64 * h + lane);
-            }
-          } else {
-#pragma unroll
-            for (int h = 0; h < 8; ++h) {
-              rg[64 * h + lane] = (uint16_t)P0[h];
-              P0[h] = word(nb + 64 * h + lane);
-            }
-          }
-          ++filled;
-          __builtin_amdgcn_wave_barrier();
+      const bool active = FULL || k < kact;
+      const uint32_t slot = x & (RM - 1);
+      const uint32_t e = lut[slot];
+      const int s = lsym[slot];
+      double scale = 0.0;
+      if (MODE != 0) {
+        if (SL) {
+          scale = ssc[col];
+          next_col();
+        } else {
+          scale = scur[j];
         }
-        const bool active = FULL || k < kact;
-        const uint32_t slot = x & (RM - 1);
-        const uint32_t e = lut[slot];
-        const int s = lsym[slot];
-        double scale = 0.0;
-        if (MODE != 0) {
-          if (SL) {
-            scale = ssc[col];
-            next_col();
-          } else {
-            scale = scur[j];
-          }
+      }
+      // the state's chain first (update, renormalization word); the symbol's work after it
+      const uint32_t xn = (e & 0x7fffu) * (x >> RPROB) + (e >> 15);
+      x = active ? xn : x;
+      const bool need = active && x < RLOW;
+      const uint64_t wm = ballot(need);
+      // (wr plus the needing lanes below, in the two mbcnt steps)
+      const uint32_t w = rg[__builtin_amdgcn_mbcnt_hi((uint32_t)(wm >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)wm, wr)) &
+                            (RRING - 1)];
+      x = need ? ((x << 16) | w) : x;
+      wr += (uint32_t)__popcll(wm);
+      const bool isesc = active && s == esc;
+      const uint64_t em = ballot(isesc);
+      int v = lo + s;
+      if (em) {  // (rare) the escaped codes; waited for here so that the store below never waits
+        if (isesc) {
+          const uint32_t i = ep + count_below(em);
+          v = i < n_esc ? escapes[i] : 0;
         }
-        const uint32_t xn = (e & 0x7fffu) * (x >> RPROB) + (e >> 15);  // (both reads in flight at once)
-        x = active ? xn : x;
-        const bool isesc = active && s == esc;
-        const uint64_t em = ballot(isesc);
-        int v = lo + s;
-        if (em) {  // (rare) the escaped codes; waited for here so that the store below never waits
-          if (isesc) {
-            const uint32_t i = ep + count_below(em);
-            v = i < n_esc ? escapes[i] : 0;
-          }
-          asm volatile("" : "+v"(v));
-          ep += (uint32_t)__popcll(em);
-        }
-        const bool need = active && x < RLOW;
-        const uint64_t wm = ballot(need);
-        const uint32_t w = rg[(wp + count_below(wm) - A) & (RRING - 1)];
-        x = need ? ((x << 16) | w) : x;
-        wp += (uint32_t)__popcll(wm);
-        if (active) {
-          const int64_t p = pbase + (int64_t)k * RLANES;
-          if (MODE == 0) {
-            ((int32_t*)out)[p] = v;
+        asm volatile("" : "+v"(v));
+        ep += (uint32_t)__popcll(em);
+      }
+      if (active) {
+        const int64_t p = pbase + (int64_t)k * RLANES;
+        if (MODE == 0) {
+          ((int32_t*)out)[p] = v;
+        } else {
+          const float wt = (float)(scale * (double)v);
+          if (MODE == 1) {
+            ((float*)out)[p] = wt;
           } else {
-            const float wt = (float)(scale * (double)v);
-            if (MODE == 1) {
-              ((float*)out)[p] = wt;
-            } else {
-              uint32_t u = __float_as_uint(wt);
-              u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-              ((uint16_t*)out)[p] = (uint16_t)u;
-            }
+            uint32_t u = __float_as_uint(wt);
+            u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+            ((uint16_t*)out)[p] = (uint16_t)u;
           }
         }
       }
     }
+  };
+  auto run = [&](auto full_tag) {
+    const int nwhole = L / DB;
+    for (int b = 0; b < nwhole; ++b) block(full_tag, std::false_type{}, b);
+    if (nwhole < nblk) block(full_tag, std::true_type{}, nwhole);
   };
   if ((g + 1) * (int64_t)L * RLANES <= N) run(std::true_type{});
   else run(std::false_type{});
   // A read past the payload or the escapes (a corrupt container) happened exactly when the group
   // consumed past their ends (the largest index read is the last one consumed); every stream ends
   // in the encoder's start state.
-  const bool bad = (uint64_t)A + (uint32_t)(wp - A) > (uint64_t)n_words ||
+  const bool bad = (uint64_t)A + wr > (uint64_t)n_words ||
                    (uint64_t)ep0 + (uint32_t)(ep - ep0) > (uint64_t)n_esc;
   if (bad || x != RLOW) atomicOr(flags, FLAG_RANGE);
 }
