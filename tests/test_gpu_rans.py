@@ -49,12 +49,15 @@ def test_container_matches_reference(device, n, spread, esc, L):
                                             (64 * 300 * 5 + 11, 3.0, 0, 300),
                                             (64 * 1000 + 5, 400.0, 5, 1000),
                                             (64 * 2048, 1.0e4, 0, 2048),
-                                            (64 * 8 * 1100 + 3, 2.0, 5, 8)])
+                                            (64 * 8 * 1100 + 3, 2.0, 5, 8),
+                                            (200, 2.0, 1, 1),
+                                            (64 * 65536, 2.0, 3, 65536)])
 def test_long_streams_match_reference(device, n, spread, esc, L):
     """Streams long enough that the decoder refills its payload ring many times, stream lengths that
     are not a multiple of the kernels' step blocks, a rate near 10 bits, a source that is mostly
-    escapes, and 1101 short groups (138 decoder workgroups): containers equal the reference's byte
-    for byte and decode back to the codes."""
+    escapes, 1101 short groups (138 decoder workgroups), and both ends of the stream length (one
+    code per stream; 65536, the largest, in a single group of 4.2 M codes): containers equal the
+    reference's byte for byte and decode back to the codes."""
     q = _codes(n + 1, n, spread, esc)
     qt = torch.from_numpy(q).to(DEV)
     blob, nb = lib.rans_encode(qt, L)
