@@ -244,6 +244,16 @@ constexpr int DB = 16;           // decoder: the column scales of the next DB st
 constexpr int SL_COLS = 4096;    // decoder: columns whose scales fit in LDS beside the tables
 
 
+// The decoder's output for code v as stored bits: the code (MODE 0), or the weight c v / U_jj
+// (scale = c / U_jj) as float (MODE 1) or bf16, rounded to nearest even from the float (MODE 2).
+template <int MODE>
+__device__ __forceinline__ uint32_t output_bits(double scale, int v) {
+  if (MODE == 0) return (uint32_t)v;
+  const uint32_t u = __float_as_uint((float)(scale * (double)v));
+  if (MODE == 1) return u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 // MODE 0: int32 codes; 1: float weights; 2: bf16 weights. SL: the column scales sit in LDS
 // (n_in <= 4096), else they are loaded a block of steps ahead into registers.
 template <int MODE, bool SL>
@@ -442,33 +452,28 @@ __global__ __launch_bounds__(64 * DW) void k_rans_decode(const uint16_t* __restr
       const uint32_t w = rg[__builtin_amdgcn_mbcnt_hi((uint32_t)(wm >> 32),
                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)wm, wr)) &
                             (RRING - 1)];
+      // the output of the table's symbol, formed while the word is read (an escaped lane's is
+      // formed again below)
+      int v = lo + s;
+      uint32_t ov = output_bits<MODE>(scale, v);
       x = need ? ((x << 16) | w) : x;
       wr += (uint32_t)__popcll(wm);
       const bool isesc = active && s == esc;
       const uint64_t em = ballot(isesc);
-      int v = lo + s;
       if (em) {  // (rare) the escaped codes; waited for here so that the store below never waits
         if (isesc) {
           const uint32_t i = ep + count_below(em);
           v = i < n_esc ? escapes[i] : 0;
+          ov = output_bits<MODE>(scale, v);
         }
-        asm volatile("" : "+v"(v));
+        asm volatile("" : "+v"(ov));
         ep += (uint32_t)__popcll(em);
       }
       if (active) {
         const int64_t p = pbase + (int64_t)k * RLANES;
-        if (MODE == 0) {
-          ((int32_t*)out)[p] = v;
-        } else {
-          const float wt = (float)(scale * (double)v);
-          if (MODE == 1) {
-            ((float*)out)[p] = wt;
-          } else {
-            uint32_t u = __float_as_uint(wt);
-            u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-            ((uint16_t*)out)[p] = (uint16_t)u;
-          }
-        }
+        if (MODE == 0) ((int32_t*)out)[p] = (int32_t)ov;
+        else if (MODE == 1) ((uint32_t*)out)[p] = ov;
+        else ((uint16_t*)out)[p] = (uint16_t)ov;
       }
     }
   };
