@@ -1885,8 +1885,11 @@ int wsic_rans_encode(const int32_t* codes, int64_t n, int32_t lane_symbols, uint
   }
 }
 
+// clear_flags false: the caller cleared the flags and queued kernels that may set them (their
+// verdict is read back with the decode's)
 static int rans_decode_any(const uint8_t* in, size_t in_bytes, int mode, void* dst, int64_t n,
-                           int64_t n_in, const double* invd, double c, int* flags, hipStream_t st) {
+                           int64_t n_in, const double* invd, double c, int* flags, hipStream_t st,
+                           bool clear_flags = true) {
   if (in_bytes < 64) {
     set_error("rans_decode: container too short");
     return WSIC_E_INVAL;
@@ -1913,7 +1916,7 @@ static int rans_decode_any(const uint8_t* in, size_t in_bytes, int mode, void* d
     set_error("rans_decode: container truncated (%zu of %zu bytes)", in_bytes, lay.total);
     return WSIC_E_INVAL;
   }
-  WSIC_TRY(launch_fill_zero(flags, FLAGS_BYTES, st));
+  if (clear_flags) WSIC_TRY(launch_fill_zero(flags, FLAGS_BYTES, st));
   WSIC_TRY(launch_rans_decode(mode, (const uint16_t*)(in + lay.freq), nsym, lo, N, L, G,
                               (const uint32_t*)(in + lay.gofs), (const uint32_t*)(in + lay.eofs),
                               (const uint32_t*)(in + lay.states), (const int32_t*)(in + lay.esc),
@@ -1961,13 +1964,12 @@ int wsic_rans_decode_dequant(const uint8_t* in, size_t in_bytes, int64_t n_out, 
     Carve cv(ws);
     int* flags = cv.take<int>(FLAGS_BYTES / sizeof(int));
     double* invd = cv.take<double>((size_t)n_in);
+    // the column scales are formed while the container's header is read back; a bad diagonal
+    // of U is reported with the decode's own verdict (the decode only multiplies by the scales)
     WSIC_TRY(launch_fill_zero(flags, FLAGS_BYTES, st));
     WSIC_TRY(launch_prep(U, ldu, n_in, invd, flags, st));
-    int f = 0;
-    WSIC_TRY(read_flags(flags, &f, st));
-    WSIC_TRY(flags_status(f, "rans_decode_dequant"));
     return rans_decode_any(in, in_bytes, w_hat_dtype == WSIC_BF16 ? 2 : 1, W_hat, n_out * n_in, n_in,
-                           invd, c, flags, st);
+                           invd, c, flags, st, false);
   } catch (...) {
     set_error("rans_decode_dequant: internal exception");
     return WSIC_E_INVAL;

@@ -108,6 +108,25 @@ def test_decode_to_weights_wide_rows(device):
                                w_ref.view(torch.int16) if dt == torch.bfloat16 else w_ref.view(torch.int32))
 
 
+def test_decode_to_weights_rejects_bad_diagonal(device):
+    """A zero or NaN diagonal entry of U is reported (its check travels with the decode's own
+    verdict), and a good U decodes correctly right after."""
+    n_out, n_in = 40, 70
+    q = _codes(5, n_out * n_in, 2.0).reshape(n_out, n_in)
+    codes = torch.from_numpy(q).to(DEV)
+    blob, nb = lib.rans_encode(codes, 16)
+    for bad in (0.0, float("nan")):
+        U = torch.eye(n_in, dtype=torch.float64, device=DEV)
+        U[3, 3] = bad
+        with pytest.raises(lib.WsicError):
+            lib.rans_decode_dequant(blob, nb, n_out, n_in, U, 0.01, dtype=torch.float32)
+    d = np.linspace(0.5, 2.0, n_in)
+    U = torch.diag(torch.from_numpy(d)).to(DEV)
+    w = lib.rans_decode_dequant(blob, nb, n_out, n_in, U, 0.01, dtype=torch.float32)
+    ref = ((0.01 * (1.0 / d))[None, :] * q.astype(np.float64)).astype(np.float32)
+    np.testing.assert_array_equal(w.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("R", [1.0, 2.0, 4.0])
 def test_sic_codes_coded_size(device, R):
     layer = workloads.make_layer("spiked", 300, 333, 900, seed=0, name="spiked_300x333", dtype="bf16", rank=16)
