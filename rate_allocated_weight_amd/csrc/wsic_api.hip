@@ -1853,13 +1853,9 @@ int wsic_rans_encode(const int32_t* codes, int64_t n, int32_t lane_symbols, uint
     WSIC_TRY(launch_fill_zero(out, lay.esc, st));
     uint32_t* eofs = (uint32_t*)(out + lay.eofs);
     WSIC_TRY(launch_scan_u32(cnt, G, eofs, st));
-    uint32_t n_esc = 0;
-    const ReadPiece pe{&n_esc, eofs + G, sizeof(uint32_t)};
-    WSIC_TRY(read_back(&pe, 1, st));
-    if (n_esc != novf) {
-      set_error("rans_encode: internal: %u escapes counted, %u in the histogram", n_esc, novf);
-      return WSIC_E_INVAL;
-    }
+    // the histogram counted the escapes already; the scan's total is checked against it with the
+    // payload's length below (the escapes written stay inside the container's bound either way)
+    const uint32_t n_esc = novf;
     lay = rans_layout(G, nsym, n_esc, 0);
     if (lay.payload > lay.esc + 4 * (size_t)n_esc)
       WSIC_TRY(launch_fill_zero(out + lay.esc + 4 * (size_t)n_esc, lay.payload - lay.esc - 4 * (size_t)n_esc, st));
@@ -1868,9 +1864,14 @@ int wsic_rans_encode(const int32_t* codes, int64_t n, int32_t lane_symbols, uint
                                 (int32_t*)(out + lay.esc), temp, gwords, (uint32_t*)(out + lay.states), st));
     uint32_t* gofs = (uint32_t*)(out + lay.gofs);
     WSIC_TRY(launch_scan_u32(gwords, G, gofs, st));
-    uint32_t nw = 0;
-    const ReadPiece pw{&nw, gofs + G, sizeof(uint32_t)};
-    WSIC_TRY(read_back(&pw, 1, st));
+    uint32_t nw = 0, n_esc_scan = 0;
+    const ReadPiece pw[2] = {{&nw, gofs + G, sizeof(uint32_t)},
+                             {&n_esc_scan, eofs + G, sizeof(uint32_t)}};
+    WSIC_TRY(read_back(pw, 2, st));
+    if (n_esc_scan != n_esc) {
+      set_error("rans_encode: internal: %u escapes counted, %u in the histogram", n_esc_scan, n_esc);
+      return WSIC_E_INVAL;
+    }
     lay = rans_layout(G, nsym, n_esc, nw);
     WSIC_TRY(launch_rans_compact(temp, L, G, gwords, gofs, (uint16_t*)(out + lay.payload), st));
     uint32_t hdr[16] = {RANS_MAGIC, 1u, (uint32_t)(n & 0xffffffffLL), (uint32_t)(n >> 32), (uint32_t)L,
