@@ -177,3 +177,18 @@ def test_damaged_container_is_rejected(device):
     bad[64:64 + 40] = 0xFF  # frequencies far above 2^14
     with pytest.raises(lib.WsicError):
         lib.rans_decode(bad, nb, q.size)
+    # sections located from the header (groups G, symbols nsym): word offsets pointing far past
+    # the payload, and scrambled initial states; every read stays bounded and the decode fails
+    hdr = np.frombuffer(blob[:64].cpu().numpy().tobytes(), dtype="<u4")
+    G, nsym = int(hdr[5]), int(hdr[7])
+    a16 = lambda v: (v + 15) // 16 * 16
+    gofs = a16(64 + 2 * nsym)
+    states = a16(a16(gofs + 4 * (G + 1)) + 4 * (G + 1))
+    bad = blob.clone()
+    bad[gofs + 4:gofs + 4 * G] = 0xF0
+    with pytest.raises(lib.WsicError):
+        lib.rans_decode(bad, nb, q.size)
+    bad = blob.clone()
+    bad[states:states + 4 * 64 * G] ^= 0x3C
+    with pytest.raises(lib.WsicError):
+        lib.rans_decode(bad, nb, q.size)
